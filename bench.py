@@ -1,0 +1,226 @@
+"""Benchmark of the packed-twin decode path on one MI355X.
+
+A step is one pass of the hot path over one batch of synthetic input: the SSQ
+twin GEMV over a 17408 x 5120 packed twin matrix (both twins' outputs from one
+pass over the weights) followed by the greedy verify of the two output
+vectors.  ``value`` is effective weight bandwidth: packed weight bytes per
+step / step time, with inputs resident in HBM.  The weights rotate over three
+copies (568 MB, more than twice the 256 MB Infinity Cache), so every step
+reads its weights from HBM.
+
+Also reported on the same JSON line:
+  * roofline: the SSQ GEMV kernel alone (algorithmic bytes per launch / average
+    launch time measured with HIP events on its stream) against 8 TB/s HBM;
+  * per_kernel: the Q8 multi-stream GEMV over 17408 x 5120 at N = 1, 2, 4
+    streams (effective weight GB/s, GEMV/s, and t(N=4)/t(N=1)), and the verify;
+  * cpu_baseline: the fp64 oracle (scalar C, one host core) running the same
+    SSQ GEMV, timed on a bounded number of passes.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROWS, COLS = 17408, 5120
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective weight GB/s (% of 8 TB/s) + GEMV/s, 17408x5120 SSQ/Q8, N=1,2,4 streams"
+MALL_BYTES = 256 * 2**20
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def copies_for(nbytes: int) -> int:
+    """Copies of a buffer to rotate through so the set is >= 2x the Infinity Cache."""
+    return max(2, -(-2 * MALL_BYTES // nbytes))
+
+
+def timed_loop(torch, fn, n_iter, stream):
+    """Average ms per call of fn(i) for i in range(n_iter), HIP events on `stream`."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(n_iter):
+        fn(i)
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / n_iter
+
+
+def cpu_baseline(d, budget_s: float):
+    """The oracle (scalar fp64 C, one thread) on the same SSQ GEMV, repeated
+    until budget_s seconds have passed (at least once)."""
+    import oracle
+    P = oracle.pack_ssq(d["A"], d["B"], d["sA"], d["sB"])
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.gemv_ssq(P, ROWS, COLS, d["xA"], d["xB"])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per = el / n
+    return {"value": round(P.nbytes / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} full {ROWS}x{COLS} SSQ twin GEMVs (both twins), scalar fp64 C oracle, "
+                      f"{per:.3f} s each, {el:.1f} s total",
+            "gemv_per_s": round(1.0 / per, 4)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only-main", action="store_true", help="time the SSQ step only (profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import packed_twin_int8_amd as pti
+    import synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    log(f"device {torch.cuda.get_device_name(0)}")
+
+    # ---------------- inputs: SSQ twin workload, seed 2
+    d = synth.twin(ROWS, COLS, synth.SEED_SSQ_FFN)
+    P = pti.pack_ssq(d["A"], d["B"], d["sA"], d["sB"])
+    w_bytes = P.nbytes
+    n_copies = copies_for(w_bytes)
+    w0 = torch.from_numpy(P).to(dev)
+    ws = [w0] + [w0.clone() for _ in range(n_copies - 1)]
+    xa = torch.from_numpy(d["xA"]).to(dev)
+    xb = torch.from_numpy(d["xB"]).to(dev)
+    ya = torch.empty(ROWS, dtype=torch.float32, device=dev)
+    yb = torch.empty(ROWS, dtype=torch.float32, device=dev)
+    y2 = torch.stack([ya, yb])  # verify reads [2][ROWS]; GEMV writes into its rows
+    ya, yb = y2[0], y2[1]
+    tok = torch.zeros(2, dtype=torch.int32, device=dev)
+    am = torch.empty(2, dtype=torch.int32, device=dev)
+    acc = torch.empty(1, dtype=torch.int32, device=dev)
+    L = pti.lib()
+    sp = pti._stream(stream)
+
+    def gemv(i):
+        st = L.pti_gemv_ssq(ws[i % n_copies].data_ptr(), xa.data_ptr(), xb.data_ptr(), ya.data_ptr(), yb.data_ptr(),
+                            ROWS, COLS, sp)
+        if st:
+            pti._check("pti_gemv_ssq", st)
+
+    def verify(i):
+        st = L.pti_verify_argmax(y2.data_ptr(), tok.data_ptr(), am.data_ptr(), acc.data_ptr(), ROWS, 2, sp)
+        if st:
+            pti._check("pti_verify_argmax", st)
+
+    def step(i):
+        gemv(i)
+        verify(i)
+
+    log(f"ssq twin {ROWS}x{COLS}: {w_bytes} weight bytes, {n_copies} copies rotated")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = timed_loop(torch, step, args.steps, stream)
+    log(f"step: {ms_step * 1e3:.2f} us")
+
+    gemv_algo_bytes = w_bytes + 2 * COLS * 4 + 2 * ROWS * 4
+    ms_gemv = timed_loop(torch, gemv, args.steps, stream)
+    ms_verify = timed_loop(torch, verify, args.steps, stream)
+    log(f"ssq gemv alone: {ms_gemv * 1e3:.2f} us; verify alone {ms_verify * 1e3:.2f} us")
+
+    result = {
+        "metric": METRIC,
+        "value": round(w_bytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "ssq_twin_gemv_17408x5120+greedy_verify",
+            "rows": ROWS, "cols": COLS, "format": "SSQ mode-16 (68 B blocks), int8 twins, f16 block scales",
+            "streams": 2, "seed": synth.SEED_SSQ_FFN, "weight_copies_rotated": n_copies,
+            "rotated_bytes": n_copies * w_bytes, "device": torch.cuda.get_device_name(0),
+        },
+        "gemv_per_s": round(1.0 / (ms_step * 1e-3), 1),
+        "frac_of_hbm_peak": round(w_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gemv_kernel<SSQ> (pti_gemv_ssq)",
+            "achieved": round(gemv_algo_bytes / (ms_gemv * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gemv_algo_bytes / (ms_gemv * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": gemv_algo_bytes,
+            "avg_launch_us": round(ms_gemv * 1e3, 3),
+        },
+    }
+    per_kernel = {"ssq_twin_gemv": {"us": round(ms_gemv * 1e3, 3),
+                                    "weight_GBps": round(w_bytes / (ms_gemv * 1e-3) / 1e9, 2),
+                                    "gemv_per_s": round(1 / (ms_gemv * 1e-3), 1)},
+                  "verify_n2_v17408": {"us": round(ms_verify * 1e3, 3)}}
+    del ws, w0
+    torch.cuda.empty_cache()
+
+    # ---------------- Q8 multi-stream, N = 1, 2, 4
+    if not args.only_main:
+        q = synth.q8(ROWS, COLS, 4, synth.SEED_Q8_FFN)
+        Pq = pti.pack_q8(q["Q"], q["S"])
+        nq = copies_for(Pq.nbytes)
+        wq0 = torch.from_numpy(Pq).to(dev)
+        wqs = [wq0] + [wq0.clone() for _ in range(nq - 1)]
+        X = torch.from_numpy(q["X"]).to(dev)
+        Y = torch.empty((4, ROWS), dtype=torch.float32, device=dev)
+        t = {}
+        for n in (1, 2, 4):
+            def qgemv(i, n=n):
+                st = L.pti_gemv_q8_multi(wqs[i % nq].data_ptr(), X.data_ptr(), Y.data_ptr(), ROWS, COLS, n, sp)
+                if st:
+                    pti._check("pti_gemv_q8_multi", st)
+            for i in range(args.warmup):
+                qgemv(i)
+            t[n] = timed_loop(torch, qgemv, args.steps, stream)
+            algo = Pq.nbytes + n * (COLS + ROWS) * 4
+            per_kernel[f"q8_gemv_n{n}"] = {
+                "us": round(t[n] * 1e3, 3),
+                "weight_GBps": round(Pq.nbytes / (t[n] * 1e-3) / 1e9, 2),
+                "frac_of_hbm_peak": round(algo / (t[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "gemv_per_s": round(1 / (t[n] * 1e-3), 1),
+                "outputs_per_s": round(n * ROWS / (t[n] * 1e-3), 1),
+            }
+            log(f"q8 n={n}: {t[n] * 1e3:.2f} us, {Pq.nbytes / (t[n] * 1e-3) / 1e9:.1f} GB/s")
+        per_kernel["q8_step_cost_n4_over_n1"] = round(t[4] / t[1], 4)
+        del wqs, wq0
+    result["per_kernel"] = per_kernel
+
+    if not args.no_cpu:
+        log("cpu baseline (oracle)...")
+        result["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

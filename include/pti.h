@@ -1,0 +1,167 @@
+/*
+ * pti.h -- C ABI of libpti.so: the packed-twin (PTI) decode hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (by title and section):
+ *   [Digest]  "Packed Twin Inference：无需草稿模型的推测解码新方案，实现2倍吞吐量提升"
+ *             (zingnex.cn forum digest of the packed-twin-inference project)
+ *   [README]  "打包双子推理（PTI）" (bittide.aicompass.dev; the project README in
+ *             Chinese translation)
+ *
+ * The operations: a matrix-vector product (GEMV) over int8 weights that are
+ * read from memory once per call and shared by several token streams.
+ *   - SSQ ("side-by-side quantization") packs the int8 weights of two models,
+ *     the twins A and B, into one uint16 per position, A in the high byte and
+ *     B in the low byte, in 68-byte blocks [scale_A f16][scale_B f16][32 x uint16]
+ *     [Digest, section "PTI的核心创新：SSQ打包技术" (SSQ packing)].  One load of a
+ *     slot feeds both twins' accumulations
+ *     [README, section "与 SSQ（Side-by-Side Quantization）的关系" (relation to SSQ)].
+ *   - Q8 stores one model as 34-byte blocks [scale f16][32 x int8] (two of them
+ *     have the size of one SSQ block [Digest, SSQ packing]); one read of a block
+ *     is shared by n_streams activation vectors [README, section
+ *     "带宽分析：为什么会有开销" (bandwidth analysis), the multi-stream kernel
+ *     that reads four activation vectors per weight load].
+ *   - Verify takes each stream's greedy token and counts how many streams'
+ *     speculative inputs are confirmed [README, section "接受机制如何工作" (how
+ *     acceptance works); Digest, section "技术实现架构" (implementation
+ *     architecture), the verify step].
+ *
+ * Conventions shared by every call
+ *   - Return value: PTI_OK (0) or a negative PTI_ERR_* code.  Nothing aborts,
+ *     throws or exits.  Arguments are validated before anything is written or
+ *     launched; on a validation error nothing is written.
+ *   - Matrices are row-major, little-endian, with no header or padding: row r
+ *     holds cols/32 consecutive blocks, block b covering columns 32b..32b+31.
+ *     A weight's value is scale * int8 (symmetric, no zero point).
+ *   - Ownership: the caller owns every buffer.  The library allocates no memory,
+ *     keeps no state other than a thread-local copy of the last HIP error, and
+ *     may be called from several threads.
+ *   - Device calls take device pointers and a HIP stream (a hipStream_t passed
+ *     as void*, NULL = the default stream).  They enqueue work and return
+ *     without synchronising; outputs are overwritten, never accumulated into.
+ *     A HIP launch failure returns PTI_ERR_HIP (see pti_last_hip_error).
+ *   - Device calls need: w 4-byte aligned, activations 16-byte aligned, every
+ *     other device pointer 4-byte aligned; outputs must not overlap any input
+ *     or each other.  Inputs may alias each other (e.g. x_a == x_b).
+ *   - Sizes: 1 <= rows <= PTI_MAX_ROWS, 32 <= cols <= PTI_MAX_COLS,
+ *     cols % 32 == 0, 1 <= vocab <= PTI_MAX_VOCAB.
+ *   - Numerics: fp32 accumulation.  For every output, the error against the
+ *     exact result is below 1e-5 * sum_c |scale * q_c * x_c| for finite inputs.
+ *     The result of one stream depends only on that stream's inputs and on
+ *     (rows, cols): it is bitwise the same whatever n_streams or the stream's
+ *     slot, and bitwise the same between an SSQ twin and a Q8 GEMV of the same
+ *     model's weights.  Non-finite scales or activations give unspecified
+ *     (non-finite or finite) outputs for the affected rows.
+ */
+#ifndef PTI_H
+#define PTI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PTI_BLOCK 32            /* weights per scale block, both formats */
+#define PTI_SSQ_BLOCK_BYTES 68  /* [scale_A f16][scale_B f16][32 x uint16] */
+#define PTI_Q8_BLOCK_BYTES 34   /* [scale f16][32 x int8] */
+#define PTI_MAX_STREAMS 4
+#define PTI_MAX_ROWS 2147483647LL
+#define PTI_MAX_COLS (1LL << 24)
+#define PTI_MAX_VOCAB 2147483647LL
+
+enum pti_status {
+    PTI_OK = 0,
+    PTI_ERR_NULL = -1,     /* a required pointer is NULL */
+    PTI_ERR_SHAPE = -2,    /* rows/cols/vocab outside the limits above, or cols % 32 != 0 */
+    PTI_ERR_NSTREAMS = -3, /* n_streams outside [1, PTI_MAX_STREAMS] */
+    PTI_ERR_ALIGN = -4,    /* a device pointer is not aligned as required */
+    PTI_ERR_HIP = -5,      /* the HIP runtime reported an error; see pti_last_hip_error() */
+    PTI_ERR_OVERLAP = -6   /* an output range overlaps an input range or another output */
+};
+
+/* Static text for a status code ("unknown status" for other values). */
+const char *pti_status_str(int status);
+
+/* hipError_t value of the last PTI_ERR_HIP returned on the calling thread
+ * (0 if none). */
+int pti_last_hip_error(void);
+
+/* ABI version of this header: 1. */
+int pti_abi_version(void);
+
+/* ------------------------------------------------------------------------- */
+/* Host-side packing [Digest, SSQ packing; Digest, implementation architecture:
+ * the packing, unpacking and format-conversion tools].  CPU, synchronous; all
+ * buffers are caller-owned host memory.  Bit-preserving for every int8 value
+ * (including -128) and every f16 bit pattern.                              */
+
+/* Bytes of a packed rows x cols matrix: rows*(cols/32)*68 (SSQ) or
+ * rows*(cols/32)*34 (Q8); 0 if the shape is invalid. */
+size_t pti_ssq_bytes(int64_t rows, int64_t cols);
+size_t pti_q8_bytes(int64_t rows, int64_t cols);
+
+/* a, b: int8 [rows][cols] (twin A, twin B); scale_a, scale_b: f16 bit patterns
+ * [rows][cols/32]; out: pti_ssq_bytes(rows, cols) bytes.  Block (r, k) is at
+ * byte (r*cols/32 + k)*68: bytes 0..1 scale_a, 2..3 scale_b, then slot j
+ * (= A_j << 8 | B_j as uint16) at bytes 4+2j (B_j) and 5+2j (A_j). */
+int pti_pack_ssq(const int8_t *a, const int8_t *b, const uint16_t *scale_a, const uint16_t *scale_b,
+                 int64_t rows, int64_t cols, uint8_t *out);
+/* Inverse of pti_pack_ssq. */
+int pti_unpack_ssq(const uint8_t *in, int64_t rows, int64_t cols, int8_t *a, int8_t *b,
+                   uint16_t *scale_a, uint16_t *scale_b);
+
+/* q: int8 [rows][cols]; scale: f16 bits [rows][cols/32]; out: pti_q8_bytes bytes.
+ * Block (r, k) at byte (r*cols/32 + k)*34: bytes 0..1 scale, bytes 2+j q_j. */
+int pti_pack_q8(const int8_t *q, const uint16_t *scale, int64_t rows, int64_t cols, uint8_t *out);
+/* Inverse of pti_pack_q8. */
+int pti_unpack_q8(const uint8_t *in, int64_t rows, int64_t cols, int8_t *q, uint16_t *scale);
+
+/* Split an SSQ matrix into the two twins' Q8 matrices ([scale_a][A x 32] and
+ * [scale_b][B x 32] per block); join is the exact inverse.  q8_a, q8_b:
+ * pti_q8_bytes each; ssq: pti_ssq_bytes.  Inputs and outputs must not overlap. */
+int pti_ssq_split(const uint8_t *ssq, int64_t rows, int64_t cols, uint8_t *q8_a, uint8_t *q8_b);
+int pti_ssq_join(const uint8_t *q8_a, const uint8_t *q8_b, int64_t rows, int64_t cols, uint8_t *ssq);
+
+/* ------------------------------------------------------------------------- */
+/* Device calls                                                              */
+
+/* SSQ twin GEMV [README, relation to SSQ: one slot load, unpack high and low
+ * byte, accumulate scale_A*A*x_A and scale_B*B*x_B]:
+ *   y_a[r] = sum_c scale_A(r, c/32) * A[r][c] * x_a[c]
+ *   y_b[r] = sum_c scale_B(r, c/32) * B[r][c] * x_b[c]
+ * w_ssq: device, pti_ssq_bytes(rows, cols) bytes (4-byte aligned);
+ * x_a, x_b: device fp32 [cols] (16-byte aligned; may be the same buffer);
+ * y_a, y_b: device fp32 [rows], distinct, not overlapping any input. */
+int pti_gemv_ssq(const void *w_ssq, const float *x_a, const float *x_b, float *y_a, float *y_b,
+                 int64_t rows, int64_t cols, void *stream);
+
+/* Q8 multi-stream GEMV [README, bandwidth analysis: one weight read serves the
+ * activation vectors of all streams]:
+ *   y[n][r] = sum_c scale(r, c/32) * q[r][c] * x[n][c]   for n < n_streams
+ * w_q8: device, pti_q8_bytes(rows, cols) bytes (4-byte aligned);
+ * x: device fp32 [n_streams][cols], contiguous (16-byte aligned);
+ * y: device fp32 [n_streams][rows], contiguous, not overlapping w or x;
+ * 1 <= n_streams <= 4. */
+int pti_gemv_q8_multi(const void *w_q8, const float *x, float *y, int64_t rows, int64_t cols,
+                      int n_streams, void *stream);
+
+/* Greedy verify [README, how acceptance works; Digest, implementation
+ * architecture, step 3]: per stream n, argmax_out[n] = the index of the largest
+ * logits[n][*] (the lowest index wins a tie; -0 equals +0; NaN ordering is
+ * unspecified).  Stream 0 runs on the confirmed token; tokens_in[i] (i >= 1) is
+ * the guess stream i ran on, checked against argmax_out[i-1].  accept_out[0] =
+ * 1 + the number of leading checks i = 1, 2, ... that pass (a failed check
+ * voids every later stream); tokens_in[0] is not read.
+ * logits: device fp32 [n_streams][vocab] contiguous; tokens_in: device int32
+ * [n_streams]; argmax_out: device int32 [n_streams]; accept_out: device int32
+ * [1]; outputs must not overlap inputs or each other. */
+int pti_verify_argmax(const float *logits, const int32_t *tokens_in, int32_t *argmax_out,
+                      int32_t *accept_out, int64_t vocab, int n_streams, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PTI_H */

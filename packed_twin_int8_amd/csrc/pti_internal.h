@@ -1,0 +1,36 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pti.h"
+
+namespace pti {
+
+// Records a HIP error code for pti_last_hip_error() on this thread.
+void set_hip_error(int err);
+
+inline bool shape_ok(int64_t rows, int64_t cols)
+{
+    return rows >= 1 && rows <= PTI_MAX_ROWS && cols >= PTI_BLOCK && cols <= PTI_MAX_COLS &&
+           cols % PTI_BLOCK == 0;
+}
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Half-open byte range [p, p + n).
+struct Range {
+    const void *p;
+    size_t n;
+};
+
+inline bool overlap(Range a, Range b)
+{
+    if (a.n == 0 || b.n == 0)
+        return false;
+    uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+}  // namespace pti

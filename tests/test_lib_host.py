@@ -1,0 +1,175 @@
+"""libpti.so on the CPU: exported symbols, the host packer against the oracle's
+packer (bit-exact), and every argument error the C ABI reports before it
+touches the GPU."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import packed_twin_int8_amd as pti
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pti.h")
+
+OK, NULL, SHAPE, NSTREAMS, ALIGN, HIP, OVERLAP = 0, -1, -2, -3, -4, -5, -6
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pti_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_are_exported():
+    syms = declared_symbols()
+    assert len(syms) >= 14
+    assert set(syms) == set(pti.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", pti.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (pti_[a-z0-9_]+)", out))
+    missing = [s for s in syms if s not in exported]
+    assert not missing, missing
+    L = pti.lib()
+    for s in syms:
+        getattr(L, s)
+    assert L.pti_abi_version() == 1
+
+
+def test_status_strings():
+    for st in (OK, NULL, SHAPE, NSTREAMS, ALIGN, HIP, OVERLAP):
+        assert pti.status_str(st) and pti.status_str(st) != "unknown status"
+    assert pti.status_str(7) == "unknown status"
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (3, 96), (5, 512), (16, 1024), (7, 5632)])
+def test_pack_matches_oracle(rows, cols):
+    d = synth.twin(rows, cols, seed=rows * 1000 + cols)
+    d["A"][0, 0] = -128
+    d["B"][-1, -1] = -128
+    d["sA"][0, 0] = 0x0001   # subnormal
+    d["sB"][0, 0] = 0x8000   # -0
+    d["sA"][-1, -1] = 0x7C00  # +inf
+    d["sB"][-1, -1] = 0x7E01  # NaN payload
+    P = pti.pack_ssq(d["A"], d["B"], d["sA"], d["sB"])
+    assert np.array_equal(P, oracle.pack_ssq(d["A"], d["B"], d["sA"], d["sB"]))
+    assert P.nbytes == pti.ssq_bytes(rows, cols) == rows * cols // 32 * 68
+    for got, want in zip(pti.unpack_ssq(P, rows, cols), (d["A"], d["B"], d["sA"], d["sB"])):
+        assert np.array_equal(got, want)
+    Q = pti.pack_q8(d["A"], d["sA"])
+    assert np.array_equal(Q, oracle.pack_q8(d["A"], d["sA"]))
+    assert Q.nbytes == pti.q8_bytes(rows, cols) == rows * cols // 32 * 34
+    q, s = pti.unpack_q8(Q, rows, cols)
+    assert np.array_equal(q, d["A"]) and np.array_equal(s, d["sA"])
+    qa, qb = pti.ssq_split(P, rows, cols)
+    assert np.array_equal(qa, oracle.pack_q8(d["A"], d["sA"]))
+    assert np.array_equal(qb, oracle.pack_q8(d["B"], d["sB"]))
+    assert np.array_equal(pti.ssq_join(qa, qb, rows, cols), P)
+
+
+def test_pack_random_bytes_roundtrip():
+    g = np.random.default_rng(5)
+    rows, cols = 9, 320
+    P = g.integers(0, 256, (rows, cols // 32 * 68), dtype=np.uint8)
+    assert np.array_equal(pti.pack_ssq(*pti.unpack_ssq(P, rows, cols)), P)
+    Q = g.integers(0, 256, (rows, cols // 32 * 34), dtype=np.uint8)
+    assert np.array_equal(pti.pack_q8(*pti.unpack_q8(Q, rows, cols)), Q)
+
+
+def test_pack_large_threaded():
+    # big enough to take the multi-threaded path
+    rows, cols = 1024, 5120
+    d = synth.twin(rows, cols, seed=9)
+    P = pti.pack_ssq(d["A"], d["B"], d["sA"], d["sB"])
+    assert np.array_equal(P, oracle.pack_ssq(d["A"], d["B"], d["sA"], d["sB"]))
+
+
+# ------------------------------------------------------------------ ABI errors
+
+def _fake(addr):
+    # never dereferenced: every call below fails validation first
+    return ctypes.c_void_p(addr)
+
+
+A0 = 0x10000000  # 256-byte aligned fake device addresses, far apart
+A1 = 0x20000000
+A2 = 0x30000000
+A3 = 0x40000000
+A4 = 0x50000000
+
+
+def test_host_packer_errors():
+    L = pti.lib()
+    buf = np.zeros(4096, np.uint8)
+    p = buf.ctypes.data_as(ctypes.c_void_p)
+    assert L.pti_pack_ssq(None, p, p, p, 1, 32, p) == NULL
+    assert L.pti_pack_ssq(p, p, p, p, 1, 33, p) == SHAPE
+    assert L.pti_pack_ssq(p, p, p, p, 0, 32, p) == SHAPE
+    assert L.pti_pack_q8(p, p, 1, 16, p) == SHAPE
+    assert L.pti_unpack_q8(p, -1, 32, p, p) == SHAPE
+    assert L.pti_ssq_bytes(1, 31) == 0 and L.pti_q8_bytes(0, 32) == 0
+    assert L.pti_ssq_bytes(2, 64) == 272 and L.pti_q8_bytes(2, 64) == 136
+    # split/join reject overlapping buffers
+    assert L.pti_ssq_split(p, 1, 32, p, _fake(buf.ctypes.data + 2000)) == OVERLAP
+
+
+def test_gemv_ssq_errors():
+    L = pti.lib()
+    f = L.pti_gemv_ssq
+    assert f(None, _fake(A1), _fake(A1), _fake(A2), _fake(A3), 8, 64, None) == NULL
+    assert f(_fake(A0), _fake(A1), _fake(A1), None, _fake(A3), 8, 64, None) == NULL
+    assert f(_fake(A0), _fake(A1), _fake(A1), _fake(A2), _fake(A3), 0, 64, None) == SHAPE
+    assert f(_fake(A0), _fake(A1), _fake(A1), _fake(A2), _fake(A3), 8, 48, None) == SHAPE
+    assert f(_fake(A0), _fake(A1), _fake(A1), _fake(A2), _fake(A3), 8, (1 << 24) + 32, None) == SHAPE
+    assert f(_fake(A0 + 2), _fake(A1), _fake(A1), _fake(A2), _fake(A3), 8, 64, None) == ALIGN
+    assert f(_fake(A0), _fake(A1 + 4), _fake(A1), _fake(A2), _fake(A3), 8, 64, None) == ALIGN
+    assert f(_fake(A0), _fake(A1), _fake(A1), _fake(A2 + 1), _fake(A3), 8, 64, None) == ALIGN
+    # y_b overlaps y_a; y_a overlaps w; y_b overlaps x_b
+    assert f(_fake(A0), _fake(A1), _fake(A1), _fake(A2), _fake(A2 + 16), 8, 64, None) == OVERLAP
+    assert f(_fake(A0), _fake(A1), _fake(A1), _fake(A0 + 64), _fake(A3), 8, 64, None) == OVERLAP
+    assert f(_fake(A0), _fake(A1), _fake(A4), _fake(A2), _fake(A4 + 8), 8, 64, None) == OVERLAP
+
+
+def test_gemv_q8_errors():
+    L = pti.lib()
+    f = L.pti_gemv_q8_multi
+    assert f(_fake(A0), None, _fake(A2), 8, 64, 1, None) == NULL
+    assert f(_fake(A0), _fake(A1), _fake(A2), 8, 64, 0, None) == NSTREAMS
+    assert f(_fake(A0), _fake(A1), _fake(A2), 8, 64, 5, None) == NSTREAMS
+    assert f(_fake(A0), _fake(A1), _fake(A2), 8, 0, 1, None) == SHAPE
+    assert f(_fake(A0), _fake(A1 + 8), _fake(A2), 8, 64, 1, None) == ALIGN
+    assert f(_fake(A0), _fake(A1), _fake(A2 + 2), 8, 64, 1, None) == ALIGN
+    # y [4][8] floats = 128 B starting 64 B before x
+    assert f(_fake(A0), _fake(A1), _fake(A1 - 64), 8, 64, 4, None) == OVERLAP
+
+
+def test_verify_errors():
+    L = pti.lib()
+    f = L.pti_verify_argmax
+    assert f(None, _fake(A1), _fake(A2), _fake(A3), 100, 2, None) == NULL
+    assert f(_fake(A0), _fake(A1), _fake(A2), _fake(A3), 0, 2, None) == SHAPE
+    assert f(_fake(A0), _fake(A1), _fake(A2), _fake(A3), 100, 0, None) == NSTREAMS
+    assert f(_fake(A0), _fake(A1), _fake(A2), _fake(A3), 100, 5, None) == NSTREAMS
+    assert f(_fake(A0), _fake(A1), _fake(A2 + 2), _fake(A3), 100, 2, None) == ALIGN
+    assert f(_fake(A0), _fake(A1), _fake(A2), _fake(A2 + 4), 100, 2, None) == OVERLAP
+    assert f(_fake(A0), _fake(A1), _fake(A0 + 396), _fake(A3), 100, 2, None) == OVERLAP
+
+
+def test_no_device_reports_hip_error():
+    """With valid arguments and no GPU on this host the launch itself fails:
+    the call must return PTI_ERR_HIP, not crash.  (Skipped where a GPU exists:
+    the fake pointers would then reach a kernel.)"""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    L = pti.lib()
+    st = L.pti_gemv_q8_multi(_fake(A0), _fake(A1), _fake(A2), 8, 64, 1, None)
+    assert st == HIP
+    assert L.pti_last_hip_error() != 0
+    with pytest.raises(pti.PtiError):
+        pti._check("pti_gemv_q8_multi", st)
