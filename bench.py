@@ -77,6 +77,134 @@ def cpu_baseline(d, budget_s: float):
             "gemv_per_s": round(1.0 / per, 4)}
 
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "gemv_ssq_17408x5120_pmc.txt")
+KERNEL_SOURCES = ("packed_twin_int8_amd/csrc/pti_gemv.hip", "packed_twin_int8_amd/build.py")
+PROFILE_CMDS = {
+    "kt": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_kt -o kt -- python3 bench.py --no-cpu",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_fetch -o fetch -- "
+             "python3 bench.py --only-main --no-cpu --steps 10 --warmup 2 --copy-calibration",
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_write -o write -- "
+             "python3 bench.py --only-main --no-cpu --steps 10 --warmup 2 --copy-calibration",
+    "summary": "python3 bench.py --summarize-profiles gpurun_out/prof_kt gpurun_out/prof_fetch "
+               "gpurun_out/prof_write --profiles-out profiles",
+}
+CALIB_BYTES = 64 * 2**20 * 4  # torch.neg over 64 Mi fp32: reads and writes this many bytes
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per SSQ GEMV launch from the committed PMC summary, or None if
+    there is none or the kernel source changed since the counters were taken."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith((" ", "#", "|")):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        return {"bytes": int(kv["traffic_bytes_per_launch"]), "fetch_bytes": int(kv["fetch_bytes_per_launch"]),
+                "write_bytes": int(kv["write_bytes_per_launch"]), "source": os.path.relpath(TRAFFIC_FILE, HERE)}
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    with open(files[0], newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name: str) -> str:
+    """Kernel name without the parameter list (template arguments kept)."""
+    name = name.replace("(anonymous namespace)::", "")
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def summarize_profiles(kt_dir, fetch_dir, write_dir, out_dir):
+    """Turn rocprofv3 CSV output into the text summaries kept under profiles/."""
+    src_hash = kernel_source_hash()
+    kt = _csv_rows(kt_dir, "kernel_stats.csv")
+    lines = ["# rocprofv3 kernel-trace statistics: bench.py default run (SSQ twin GEMV 17408x5120 + verify,",
+             "# then Q8 multi-stream GEMV 17408x5120 at N=1,2,4), one MI355X",
+             "", "command: " + PROFILE_CMDS["kt"], "summary: " + PROFILE_CMDS["summary"],
+             "kernel_source_sha256: " + src_hash, "",
+             "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in kt:
+        lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                     f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.2f} |")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "gemv_ssq_q8_17408x5120_kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def per_kernel(d, counter):
+        acc = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return acc
+
+    def pick(acc, key):
+        ks = [k for k in acc if key(k)]
+        if len(ks) != 1:
+            raise SystemExit(f"expected one kernel, found {ks}")
+        v = acc[ks[0]]
+        return ks[0], sum(v) / len(v), len(v)
+
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        acc = per_kernel(d, counter)
+        gname, g_kib, g_n = pick(acc, lambda k: "gemv_kernel" in k)
+        cname, c_kib, c_n = pick(acc, lambda k: "neg_kernel" in k or "neg" in k.lower())
+        factor = CALIB_BYTES / 1024.0 / c_kib
+        out[counter] = dict(gname=gname, g_kib=g_kib, g_n=g_n, cname=cname, c_kib=c_kib, c_n=c_n, factor=factor,
+                            bytes=int(round(g_kib * 1024 * factor)))
+    algo = ROWS * (COLS // 32) * 68 + 2 * COLS * 4 + 2 * ROWS * 4
+    fb, wb = out["FETCH_SIZE"]["bytes"], out["WRITE_SIZE"]["bytes"]
+    lines = ["# HBM traffic of the SSQ twin GEMV (17408x5120), rocprofv3 PMC counters, one MI355X",
+             "# Each counter is scaled by the ratio of known bytes to the counter's reading for torch.neg",
+             "# over 256 MiB (reads 256 MiB, writes 256 MiB) in the same run.",
+             "", "command_fetch: " + PROFILE_CMDS["fetch"], "command_write: " + PROFILE_CMDS["write"],
+             "summary: " + PROFILE_CMDS["summary"], ""]
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        o = out[counter]
+        lines += [f"| {counter} | kernel | dispatches | avg KiB/dispatch |", "|---|---|---|---|",
+                  f"| | {o['gname']} | {o['g_n']} | {o['g_kib']:.1f} |",
+                  f"| | {o['cname'][:90]} (calibration, {CALIB_BYTES} B) | {o['c_n']} | {o['c_kib']:.1f} |",
+                  f"calibration factor {counter}: {o['factor']:.4f}", ""]
+    lines += [f"algorithmic_bytes_per_launch: {algo}",
+              f"fetch_bytes_per_launch: {fb}", f"write_bytes_per_launch: {wb}",
+              f"traffic_bytes_per_launch: {fb + wb}",
+              f"traffic_over_algorithmic: {(fb + wb) / algo:.4f}",
+              "kernel_source_sha256: " + src_hash]
+    with open(os.path.join(out_dir, os.path.basename(TRAFFIC_FILE)), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -85,7 +213,15 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-main", action="store_true", help="time the SSQ step only (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run 3 elementwise copies of 256 MiB (reference kernel for HBM byte counters)")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ summaries from rocprofv3 CSV output (CPU only) and exit")
+    ap.add_argument("--profiles-out", default=os.path.join(HERE, "profiles"))
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles, args.profiles_out)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
@@ -133,6 +269,15 @@ def main():
         gemv(i)
         verify(i)
 
+    if args.copy_calibration:
+        # torch.neg: an elementwise kernel that reads and writes 256 MiB each
+        src = torch.ones(64 * 2**20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 x torch.neg over {src.numel() * 4} bytes")
+        del src, dst
     log(f"ssq twin {ROWS}x{COLS}: {w_bytes} weight bytes, {n_copies} copies rotated")
     for i in range(args.warmup):
         step(i)
@@ -145,6 +290,7 @@ def main():
     ms_verify = timed_loop(torch, verify, args.steps, stream)
     log(f"ssq gemv alone: {ms_gemv * 1e3:.2f} us; verify alone {ms_verify * 1e3:.2f} us")
 
+    traffic = read_traffic()
     result = {
         "metric": METRIC,
         "value": round(w_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -173,9 +319,10 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gemv_algo_bytes / (ms_gemv * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic["bytes"] if traffic else None,
             "algorithmic_bytes_per_launch": gemv_algo_bytes,
             "avg_launch_us": round(ms_gemv * 1e3, 3),
+            "traffic_source": traffic["source"] if traffic else None,
         },
     }
     per_kernel = {"ssq_twin_gemv": {"us": round(ms_gemv * 1e3, 3),

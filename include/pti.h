@@ -47,10 +47,12 @@
  *     cols % 32 == 0, 1 <= vocab <= PTI_MAX_VOCAB.
  *   - Numerics: fp32 accumulation.  For every output, the error against the
  *     exact result is below 1e-5 * sum_c |scale * q_c * x_c| for finite inputs.
- *     The result of one stream depends only on that stream's inputs and on
- *     (rows, cols): it is bitwise the same whatever n_streams or the stream's
- *     slot, and bitwise the same between an SSQ twin and a Q8 GEMV of the same
- *     model's weights.  Non-finite scales or activations give unspecified
+ *     The result of one stream depends only on that stream's inputs, on
+ *     (rows, cols) and on the format: it is bitwise the same whatever
+ *     n_streams, the stream's slot or the call, so A == B twins fed equal
+ *     activations give bitwise equal outputs.  An SSQ twin and a Q8 GEMV of the
+ *     same model's weights agree within the bound above (their lanes group the
+ *     columns differently).  Non-finite scales or activations give unspecified
  *     (non-finite or finite) outputs for the affected rows.
  */
 #ifndef PTI_H

@@ -7,57 +7,78 @@
 // slot feeds twin A (high byte) and twin B (low byte); one Q8 block feeds up to
 // four activation vectors.  Output y[s][r] = sum_c scale(r, c/32) * q[r][c] * x[s][c].
 //
-// Mapping onto CDNA4 (gfx950, wave64, 160 KB LDS per CU):
-//   * Unit = 64 columns = two 32-column blocks: 68 bytes of Q8 (one dword-aligned
-//     block pair) or 136 bytes of SSQ.  A lane loads whole units with dwordx4 loads.
-//   * 16 lanes (one DPP row) own a band of R rows.  Lane j handles units
-//     j, j+16, j+32, ... of every row of the band, so the activations it needs
-//     are the same for all R rows: each LDS read of x serves R rows.
+// Mapping onto CDNA4 (gfx950: 256 CUs of 4 SIMDs, wave64, 160 KB LDS per CU):
+//   * One workgroup per CU with a multiple of four wave64s.  Rows are dealt
+//     round-robin to the SIMDs, so every SIMD gets the same number of rows (to
+//     within one) whatever the row count -- no second dispatch wave, no SIMD
+//     with twice the work -- and the GPU as a whole sweeps the matrix front to
+//     back.  x is staged once per CU whatever the wave count.
+//   * A wave owns its rows end to end: all 64 lanes share each row.  Each lane
+//     owns a fixed set of columns ("units") in every row, so the activations it
+//     needs are the same for all rows; R rows are computed together so each LDS
+//     read of x serves R rows.
+//       SSQ: 8-column units, four lanes per 68-byte block, lane q of the four
+//            reading slots 8q..8q+7 -- so the four lanes' 16-byte loads cover
+//            the block's 64 slot bytes contiguously (the address unit merges a
+//            contiguous quad into one request; scattered 16-byte pieces cost
+//            about 12% of bandwidth in measurements), plus the block's scale
+//            dword.  16 blocks (1088 bytes) per round of 64 lanes.
+//       Q8:  16-column units, two lanes per 34-byte block: the scale's dword and
+//            the 16 quant bytes read as 4 + 1 dwords from dword-aligned
+//            offsets and realigned with v_alignbyte (Q8 blocks sit at 2-byte
+//            offsets half the time).  32 blocks (1088 bytes) per round.
 //   * x is staged into LDS once per workgroup (per K-chunk when it does not
-//     fit), not re-read from L2 per row block: the README's bandwidth analysis
+//     fit), never re-read from L2 per row block: the README's bandwidth analysis
 //     traces the L2 thrash of its multi-stream kernel to that re-reading.  The
-//     LDS layout puts lane j's 16 bytes next to lane j+1's, so every
-//     ds_read_b128 of a 16-lane group is a contiguous 256-byte span.
-//   * Signed bytes convert to fp32 with one SDWA v_cvt_f32_i32 each; each
-//     32-column block is summed in fp32 (column order), scaled by its f16 scale
-//     with one FMA into the lane's accumulator; the 16 lanes of a band reduce
-//     with a fixed DPP tree (row_shr 1, 2, 4, 8).  No MFMA: this is a
-//     matrix-vector product, one FMA per weight and stream.
-//   * The per-row operation order depends only on (rows, cols): not on the
-//     stream count, the stream's slot, R, or the format, so a stream's output is
-//     bitwise independent of those, and an SSQ twin equals a Q8 GEMV of the same
-//     model bit for bit.
-//   * Two unit buffers per lane: the next round's loads are in flight while the
-//     current round is computed.
+//     LDS layout makes each ds_read_b128 of a wave one contiguous 1 KB span.
+//   * Weights are read with buffer loads through one buffer resource per row:
+//     per-lane offsets are fixed, per-round offsets are scalar, and a read
+//     past the row returns 0 instead of touching memory.
+//   * Weight loads run D steps ahead of the compute (a step = one round of R
+//     rows); every step issues the same loads (out-of-range steps through an
+//     empty resource) and sched_barrier pins the order, so each wait covers
+//     exactly one step.
+//   * Signed bytes convert to fp32 with one SDWA v_cvt_f32_i32 each.  Per unit
+//     and stream the products are summed in fp32 in column order, scaled by
+//     the block's f16 scale with one FMA into the lane's accumulator, and the
+//     64 lanes reduce with a fixed DPP tree.  Finished rows park in one lane
+//     each of an output register and are stored after the loop.  No MFMA: this is a matrix-vector
+//     product, one FMA per weight and stream.
+//   * A row's operation order depends only on (rows, cols) and the format: not
+//     on the stream count, the stream's slot, R or the wave count, so a
+//     stream's output is bitwise independent of those.
 #include <hip/hip_runtime.h>
 
 #include "pti_internal.h"
 
-#ifndef PTI_R_Q8_N1
-#define PTI_R_Q8_N1 4
+#ifndef PTI_RMAX_SSQ
+#define PTI_RMAX_SSQ 1  // rows computed together by a wave (SSQ)
 #endif
-#ifndef PTI_R_Q8_N2
-#define PTI_R_Q8_N2 4
+#ifndef PTI_RMAX_Q8
+#define PTI_RMAX_Q8 2   // rows computed together by a wave (Q8)
 #endif
-#ifndef PTI_R_Q8_N4
-#define PTI_R_Q8_N4 4
+#ifndef PTI_WAVES
+#define PTI_WAVES 16    // waves per workgroup (one workgroup per CU)
 #endif
-#ifndef PTI_R_SSQ
-#define PTI_R_SSQ 2
+#ifndef PTI_PREFETCH
+#define PTI_PREFETCH 3  // steps of weight loads in flight ahead of the compute
 #endif
 #ifndef PTI_LDS_BUDGET
-#define PTI_LDS_BUDGET (80 * 1024)
+#define PTI_LDS_BUDGET (160 * 1024)
 #endif
 
 namespace {
 
-constexpr int kLanes = 16;                    // lanes per row band (one DPP row)
-constexpr int kGroups = 16;                   // bands per workgroup
-constexpr int kThreads = kLanes * kGroups;    // 256
-constexpr int kUnitCols = 64;                 // columns per unit
-constexpr int kRoundCols = kLanes * kUnitCols;  // columns covered by one round of a band
+constexpr int kWaves = PTI_WAVES;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kD = PTI_PREFETCH;
+constexpr uint32_t kRoundBytes = 1088;  // bytes of a row one round of 64 lanes covers (both formats)
+static_assert(kWaves % 4 == 0, "waves per workgroup must fill the four SIMDs evenly");
 
 enum Fmt { kQ8 = 0, kSSQ = 1 };
+
+template <int FMT>
+constexpr int unit_cols() { return FMT == kSSQ ? 8 : 16; }
 
 struct GemvArgs {
     const uint8_t *w;
@@ -66,160 +87,298 @@ struct GemvArgs {
     int64_t rows;
     int64_t row_bytes;
     int32_t cols;
-    int32_t nb;            // blocks per row
-    int32_t nu;            // units per row (the last one is half a unit when nb is odd)
-    int32_t rounds;        // ceil(nu / kLanes)
+    int32_t units;         // units per row
+    int32_t rounds;        // ceil(units / 64)
     int32_t chunk_rounds;  // rounds of x held in LDS at once
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
-// dwords per unit
-template <int FMT>
-constexpr int unit_dwords() { return FMT == kQ8 ? 17 : 34; }
-
-template <int FMT>
+// Raw dwords of one unit of one row.
+//   SSQ: sc = [scale_A | scale_B << 16]; d[0..3] = the unit's 8 slots (slot
+//        2k in the low half of d[k]: B in byte 0, A in byte 1; slot 2k+1 in
+//        the high half).
+//   Q8:  sc = the dword holding the scale; d[0..4] = the dwords holding the 16
+//        quants, starting at a byte offset of 0 or 2 in d[0].
 struct Unit {
-    uint32_t d[unit_dwords<FMT>()];
+    uint32_t sc;
+    uint32_t d[5];
 };
 
-template <int N>
-__device__ __forceinline__ void load_dwords(uint32_t *dst, const uint32_t *src)
+// Per-lane byte offsets of the lane's unit within one round of a row,
+// relative to the dword-aligned start of the row.  Q8 has two classes: rows
+// whose start is dword-aligned (class 0) and rows starting 2 bytes into a
+// dword (class 1, only when a row holds an odd number of blocks).
+struct LaneOffsets {
+    uint32_t ssq_sc, ssq_d;              // SSQ: scale dword, first slot dword
+    uint32_t q_sc[2], q_ssh[2];          // Q8: scale dword, bit shift of the scale in it
+    uint32_t q_d[2], q_sh[2], q_h[2];    // Q8: first quant dword, byte shift, 5th dword
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane)
 {
+    LaneOffsets o;
+    o.ssq_sc = ((uint32_t)lane >> 2) * PTI_SSQ_BLOCK_BYTES;
+    o.ssq_d = o.ssq_sc + 4 + 16 * ((uint32_t)lane & 3);
+    const uint32_t pair = (uint32_t)lane >> 1, h = (uint32_t)lane & 1;  // Q8 block within the round, half
 #pragma unroll
-    for (int i = 0; i + 4 <= N; i += 4) {
-        u32x4 v = *reinterpret_cast<const u32x4_a4 *>(src + i);
-        dst[i] = v.x, dst[i + 1] = v.y, dst[i + 2] = v.z, dst[i + 3] = v.w;
+    for (int c = 0; c < 2; c++) {
+        const uint32_t blk = 2 * c + pair * PTI_Q8_BLOCK_BYTES;  // block start
+        const uint32_t q = blk + 2 + 16 * h;                      // first quant
+        o.q_sc[c] = blk & ~3u;
+        o.q_ssh[c] = (blk & 3u) * 8;
+        o.q_d[c] = q & ~3u;
+        o.q_sh[c] = q & 3u;
+        // quant bytes 15-16 are only used when the run starts 2 bytes into a
+        // dword (at d + 16); otherwise the read goes to the run's last dword
+        // (d + 12), so it never leaves the row.  Rows with an odd block count
+        // read just the halfword, at d + 16 or d + 14.
+        o.q_h[c] = o.q_d[c] + 12 + 2 * o.q_sh[c];
     }
-#pragma unroll
-    for (int i = N & ~3; i < N; i++)
-        dst[i] = src[i];
+    return o;
 }
 
-// Loads unit u of a row into canonical dword form (the unit's bytes starting at
-// a dword boundary).  ALIGNED: the unit starts on a dword boundary (always true
-// for SSQ, and for Q8 when the row's block count is even, which also means Q8
-// has no half units).  Otherwise (Q8 with an odd block count: rows alternate
-// 2-byte offsets) it is read as 16-bit words.  A half unit (only its first
-// block exists) reads only that block; the dwords of the missing block are
-// left unset and never used.
-template <int FMT, bool ALIGNED>
-__device__ __forceinline__ void load_unit(Unit<FMT> &w, const uint8_t *row, int u, bool half)
+__device__ __forceinline__ float sbyte(uint32_t d, int k) { return (float)(int8_t)(d >> (8 * k)); }
+
+__device__ __forceinline__ float f16_lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (unsigned short)v); }
+__device__ __forceinline__ float f16_hi(uint32_t v)
 {
-    constexpr int DW = unit_dwords<FMT>();
-    if constexpr (ALIGNED) {
-        const uint32_t *p = reinterpret_cast<const uint32_t *>(row + (size_t)u * (DW * 4));
-        if constexpr (FMT == kQ8) {
-            load_dwords<DW>(w.d, p);
-        } else {
-            load_dwords<DW / 2>(w.d, p);
-            if (!half)
-                load_dwords<DW / 2>(w.d + DW / 2, p + DW / 2);
-        }
-    } else {
-        const uint16_t *p = reinterpret_cast<const uint16_t *>(row + (size_t)u * (DW * 4));
-        const int nh = half ? 17 : 2 * DW;  // halfwords present
-#pragma unroll
-        for (int i = 0; i < DW; i++) {
-            uint32_t lo = (2 * i < nh) ? p[2 * i] : 0u;
-            uint32_t hi = (2 * i + 1 < nh) ? p[2 * i + 1] : 0u;
-            w.d[i] = lo | (hi << 16);
-        }
-    }
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(v >> 16));
 }
 
-__device__ __forceinline__ float f16_to_f32(uint32_t bits16)
-{
-    return (float)__builtin_bit_cast(_Float16, (unsigned short)bits16);
-}
-
-__device__ __forceinline__ float sbyte(uint32_t d, int k)
-{
-    return (float)(int8_t)(d >> (8 * k));
-}
-
-// Signed int8 weight of column (4c + m) of block bb of a unit; for SSQ, twin
-// t (0 = A, high byte of the slot; 1 = B, low byte).
-template <int FMT>
-__device__ __forceinline__ float weight(const Unit<FMT> &w, int bb, int c, int m, int t)
-{
-    if constexpr (FMT == kQ8) {
-        if (bb == 0)  // bytes 2 + 4c + m of the unit
-            return m < 2 ? sbyte(w.d[c], 2 + m) : sbyte(w.d[c + 1], m - 2);
-        return sbyte(w.d[9 + c], m);  // bytes 36 + 4c + m
-    } else {
-        // slot (4c + m) of block bb: dword 17 bb + 1 + 2c + m/2, halfword m % 2
-        const uint32_t d = w.d[17 * bb + 1 + 2 * c + (m >> 1)];
-        return sbyte(d, 2 * (m & 1) + (t == 0 ? 1 : 0));
-    }
-}
-
-template <int FMT>
-__device__ __forceinline__ uint32_t scale_bits(const Unit<FMT> &w, int bb, int t)
-{
-    if constexpr (FMT == kQ8)
-        return bb == 0 ? (w.d[0] & 0xffffu) : (w.d[8] >> 16);
-    else
-        return t == 0 ? (w.d[17 * bb] & 0xffffu) : (w.d[17 * bb] >> 16);
-}
-
-// LDS layout of one chunk of x (float4 elements):
-//   xs[((round * 16 + cg) * NSP + p) * 16 + lane]
-// cg = column group (4 columns) within the lane's unit (0..15), p = piece.
-// Piece p of (lane, cg) holds elements 4p..4p+3 of the column-major flattening
+// LDS layout of one chunk of x (float4 elements), UC = unit columns:
+//   xs[((round * (UC/4) + cg) * NSP + p) * 64 + lane]
+// cg = column group (4 columns) of the lane's unit, p = piece.  Piece p of
+// (lane, cg) holds elements 4p..4p+3 of the column-major flattening
 // e = m * NSP + s (m = column within the group, s = stream); NSP = streams
-// rounded up to 1, 2 or 4 (a fourth stream of zeros pads three streams).
-template <int NSP, int NS>
-__device__ __forceinline__ void stage_x(const GemvArgs &a, float4 *xs, int round0, int nr, int tid)
+// rounded up to 1, 2 or 4 (three streams are padded with a zero fourth).
+// Staging items are (round, column group, lane), spread over the threads.
+template <int UC, int NSP, int NS, int BATCH>
+__device__ __forceinline__ void stage_load(const GemvArgs &a, int item0, float4 (&v)[BATCH][NSP], int tid,
+                                           int nitems)
 {
-    const int jj = tid & (kLanes - 1), cg = tid / kLanes;  // 16 x 16 = 256 items per round
-    for (int il = 0; il < nr; il++) {
-        const int col = ((round0 + il) * kLanes + jj) * kUnitCols + cg * 4;
-        float v[4][4];
+    constexpr int CG = UC / 4;
+#pragma unroll
+    for (int i = 0; i < BATCH; i++) {
+        const int it = item0 + i * kThreads + tid;
+        const int l = it & 63, cg = (it >> 6) % CG, rd = (it >> 6) / CG;
+        const int col = (rd * 64 + l) * UC + cg * 4;
 #pragma unroll
         for (int s = 0; s < NSP; s++) {
-            float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (s < NS && col < a.cols)
-                t = *reinterpret_cast<const float4 *>(a.x[s] + col);
-            v[s][0] = t.x, v[s][1] = t.y, v[s][2] = t.z, v[s][3] = t.w;
-        }
-        float4 *base = xs + ((il * 16 + cg) * NSP) * kLanes + jj;
-#pragma unroll
-        for (int p = 0; p < NSP; p++) {
-            float e[4];
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const int flat = 4 * p + q;
-                e[q] = v[flat % NSP][flat / NSP];
-            }
-            base[p * kLanes] = make_float4(e[0], e[1], e[2], e[3]);
+            v[i][s] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (it < nitems && s < NS && col < a.cols)
+                v[i][s] = *reinterpret_cast<const float4 *>(a.x[s] + col);
         }
     }
 }
 
-// Accumulates one unit of R rows into acc.  xr points at the lane's x for this
-// round: xr[(cg * NSP + p) * 16].
-template <int FMT, int NSP, int NS, int R>
-__device__ __forceinline__ void compute_unit(const Unit<FMT> (&w)[R], const float4 *xr, bool half,
-                                             float (&acc)[R][NS])
+template <int UC, int NSP, int BATCH>
+__device__ __forceinline__ void stage_store(float4 *xs, int item0, const float4 (&v)[BATCH][NSP], int tid,
+                                            int nitems)
 {
+    constexpr int CG = UC / 4;
 #pragma unroll
-    for (int bb = 0; bb < 2; bb++) {
-        if (bb == 1 && half)
+    for (int i = 0; i < BATCH; i++) {
+        const int it = item0 + i * kThreads + tid;
+        if (it >= nitems)
             break;
+        const int l = it & 63, cg = (it >> 6) % CG, rd = (it >> 6) / CG;
+        float e[4][4];  // [stream][column]
+#pragma unroll
+        for (int s = 0; s < NSP; s++)
+            e[s][0] = v[i][s].x, e[s][1] = v[i][s].y, e[s][2] = v[i][s].z, e[s][3] = v[i][s].w;
+        float4 *base = xs + ((rd * CG + cg) * NSP) * 64 + l;
+#pragma unroll
+        for (int p = 0; p < NSP; p++) {
+            float o[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int f = 4 * p + q;
+                o[q] = e[f % NSP][f / NSP];
+            }
+            base[p * 64] = make_float4(o[0], o[1], o[2], o[3]);
+        }
+    }
+}
+
+// Stage rounds [r0, r0 + nr) of x into LDS rounds 0..nr-1 (nr at most the
+// LDS budget's chunk, which BATCH items per thread cover).
+template <int UC, int NSP, int NS, int BATCH>
+__device__ __forceinline__ void stage_all(const GemvArgs &a0, float4 *xs, int r0, int nr, int tid)
+{
+    GemvArgs a = a0;  // x pointers shifted to the chunk's first column
+    const int c0 = r0 * 64 * UC;
+#pragma unroll
+    for (int s = 0; s < NS; s++)
+        a.x[s] += c0;
+    a.cols -= c0;
+    const int nitems = nr * 64 * (UC / 4);  // <= BATCH * kThreads
+    float4 v[BATCH][NSP];
+    stage_load<UC, NSP, NS, BATCH>(a, 0, v, tid, nitems);
+    stage_store<UC, NSP, BATCH>(xs, 0, v, tid, nitems);
+}
+
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf,
+                                                                 BOUND_ZERO));
+}
+
+// Sum over the 64 lanes; the total lands in lane 63.  Fixed tree: row_shr 1, 2,
+// 4, 8 within each 16-lane row, then row_bcast15 and row_bcast31 across rows.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = v + dpp<0x111, 0xf, true>(v);
+    v = v + dpp<0x112, 0xf, true>(v);
+    v = v + dpp<0x114, 0xf, true>(v);
+    v = v + dpp<0x118, 0xf, true>(v);
+    v = v + dpp<0x142, 0xa, false>(v);
+    v = v + dpp<0x143, 0xc, false>(v);
+    return v;
+}
+
+template <int FMT, int NSP, int NS, int R, bool ROWS4>
+struct Wave {
+    static constexpr int UC = unit_cols<FMT>();
+    static constexpr int CG = UC / 4;
+
+    const GemvArgs &a;
+    const float4 *xs;
+    int lane;
+    // Rows of this wave (wave-uniform): row(t) = first + t * stride, t < nrow.
+    int64_t first, stride;
+    int nrow, npass;
+    const uint8_t *wave_base;  // row first
+    int64_t row_step;          // bytes from one row of the wave to the next
+    LaneOffsets lo;
+    float acc[R][NS];
+    float outv[NS];  // finished rows of the current group, row j of the group in lane j
+    int gp0;         // first pass of the current group
+    Unit bufs[kD + 1][R];
+
+    // Cursors over the steps (pass, round) of the current segment: passes
+    // [p0, p1), rounds [i0, i1).  The issue cursor runs kD steps ahead of the
+    // compute cursor; each keeps what it needs of its pass in scalar
+    // registers, rebuilt when it enters a new pass, so a step costs a few
+    // scalar instructions (the scalar unit is shared by the CU's waves).
+    int p1, i0, i1, nsteps;
+    int ip, ir;                        // issue cursor
+    __amdgpu_buffer_rsrc_t irs[R];     // its pass's rows (empty past the end)
+    int icls[R];                       // Q8 class of those rows
+    int cp, cr;                        // compute cursor
+    int cnrows;                        // rows in the compute cursor's pass
+    int ccls[R];
+
+    __device__ __forceinline__ Wave(const GemvArgs &a_, const float4 *xs_, int lane_, int64_t first_,
+                                    int64_t stride_, int nrow_)
+        : a(a_), xs(xs_), lane(lane_), first(first_), stride(stride_), nrow(nrow_)
+    {
+        npass = (nrow + R - 1) / R;
+        wave_base = a.w + first * a.row_bytes;
+        row_step = stride * a.row_bytes;
+        lo = lane_offsets(lane_);
+#pragma unroll
+        for (int r = 0; r < R; r++)
+#pragma unroll
+            for (int s = 0; s < NS; s++)
+                acc[r][s] = 0.f;
+    }
+
+    __device__ __forceinline__ int rows_in(int pass) const { return min(R, nrow - pass * R); }
+
+    // Buffer resources over the rows of pass p (dword-aligned bases).  Rows
+    // past the pass's last, or a pass past the segment, get empty resources:
+    // their loads return 0 without touching memory, but are still issued, so
+    // the count of loads in flight is the same on every path and each wait
+    // covers exactly one step.
+    __device__ __forceinline__ void set_issue_pass(int p)
+    {
+        const int nr_in = p < p1 ? rows_in(p) : 0;
+        const uint8_t *base = wave_base + (int64_t)p * R * row_step;
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const uintptr_t q = reinterpret_cast<uintptr_t>(base + r * row_step);
+            const uint32_t e0 = (uint32_t)(q & 3);
+            icls[r] = ROWS4 ? 0 : (int)(e0 >> 1);
+            const uint32_t n = r < nr_in ? e0 + (uint32_t)a.row_bytes : 0u;
+            irs[r] = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(q & ~uintptr_t(3)), (short)0, (int)n,
+                                                       0x00020000);
+        }
+    }
+
+    __device__ __forceinline__ void set_compute_pass(int p)
+    {
+        cnrows = rows_in(p);
+        if constexpr (!ROWS4) {
+            const uint8_t *base = wave_base + (int64_t)p * R * row_step;
+#pragma unroll
+            for (int r = 0; r < R; r++)
+                ccls[r] = (int)((reinterpret_cast<uintptr_t>(base + r * row_step) >> 1) & 1);
+        }
+    }
+
+    // Issue the loads of the issue cursor's step into buf, then advance it.
+    __device__ __forceinline__ void issue(Unit (&buf)[R])
+    {
+        const int soff = ir * (int)kRoundBytes;
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            if constexpr (FMT == kSSQ) {
+                buf[r].sc = __builtin_amdgcn_raw_buffer_load_b32(irs[r], (int)lo.ssq_sc, soff, 0);
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(irs[r], (int)lo.ssq_d, soff, 0);
+                buf[r].d[0] = v.x, buf[r].d[1] = v.y, buf[r].d[2] = v.z, buf[r].d[3] = v.w;
+            } else {
+                const int c = icls[r];
+                buf[r].sc = __builtin_amdgcn_raw_buffer_load_b32(irs[r], (int)lo.q_sc[c], soff, 0);
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(irs[r], (int)lo.q_d[c], soff, 0);
+                buf[r].d[0] = v.x, buf[r].d[1] = v.y, buf[r].d[2] = v.z, buf[r].d[3] = v.w;
+                // rows of an even number of blocks: the dword holding quant
+                // bytes 15-16 lies inside the row; otherwise read the halfword
+                buf[r].d[4] = ROWS4 ? __builtin_amdgcn_raw_buffer_load_b32(irs[r], (int)lo.q_h[c], soff, 0)
+                                    : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                          irs[r], (int)lo.q_h[c] + 2 - (int)lo.q_sh[c], soff, 0);
+            }
+        }
+        if (++ir == i1) {
+            ir = i0;
+            set_issue_pass(++ip);
+        }
+    }
+
+    // Accumulate the compute cursor's step from buf (x of round cr at LDS round
+    // cr - i0); at the end of a pass reduce its rows.  Lanes past
+    // the last unit of a row, and rows past the last of a partial pass, read
+    // zero weights through the buffer bounds (and such lanes zero activations
+    // from LDS), so they add nothing and need no branch; only the stores are
+    // guarded.
+    __device__ __forceinline__ void compute(const Unit (&buf)[R])
+    {
+        const int nrows = cnrows;
+        const float4 *xr = xs + ((cr - i0) * CG * NSP) * 64 + lane;
+        uint32_t q[R][4];
+        if constexpr (FMT == kQ8) {
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                // realign the 16 quants: byte offset 0 or 2 within d[0]
+                const uint32_t sh = ROWS4 ? lo.q_sh[0] : lo.q_sh[ccls[r]];
+#pragma unroll
+                for (int k = 0; k < 4; k++)
+                    q[r][k] = __builtin_amdgcn_alignbyte(buf[r].d[k + 1], buf[r].d[k], sh);
+            }
+        }
         float bs[R][NS];
 #pragma unroll
-        for (int c = 0; c < 8; c++) {
+        for (int c = 0; c < CG; c++) {
             float xv[4][NSP];
 #pragma unroll
             for (int p = 0; p < NSP; p++) {
-                const float4 t = xr[((bb * 8 + c) * NSP + p) * kLanes];
+                const float4 t = xr[(c * NSP + p) * 64];
                 const float e[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    const int flat = 4 * p + q;
-                    xv[flat / NSP][flat % NSP] = e[q];
+                for (int qq = 0; qq < 4; qq++) {
+                    const int f = 4 * p + qq;
+                    xv[f / NSP][f % NSP] = e[qq];
                 }
             }
 #pragma unroll
@@ -227,128 +386,222 @@ __device__ __forceinline__ void compute_unit(const Unit<FMT> (&w)[R], const floa
 #pragma unroll
                 for (int m = 0; m < 4; m++) {
                     if constexpr (FMT == kQ8) {
-                        const float q = weight<FMT>(w[r], bb, c, m, 0);
+                        const float wq = sbyte(q[r][c], m);
 #pragma unroll
                         for (int s = 0; s < NS; s++)
-                            bs[r][s] = (c == 0 && m == 0) ? q * xv[m][s] : __builtin_fmaf(q, xv[m][s], bs[r][s]);
+                            bs[r][s] = (c == 0 && m == 0) ? wq * xv[m][s] : __builtin_fmaf(wq, xv[m][s], bs[r][s]);
                     } else {
+                        // slot 4c + m of the unit: dword 2c + m/2, halfword m % 2;
+                        // twin A = high byte, twin B = low byte
+                        const uint32_t dw = buf[r].d[2 * c + (m >> 1)];
 #pragma unroll
                         for (int s = 0; s < NS; s++) {
-                            const float q = weight<FMT>(w[r], bb, c, m, s);
-                            bs[r][s] = (c == 0 && m == 0) ? q * xv[m][s] : __builtin_fmaf(q, xv[m][s], bs[r][s]);
+                            const float wq = sbyte(dw, 2 * (m & 1) + (s == 0 ? 1 : 0));
+                            bs[r][s] = (c == 0 && m == 0) ? wq * xv[m][s] : __builtin_fmaf(wq, xv[m][s], bs[r][s]);
                         }
                     }
                 }
             }
         }
 #pragma unroll
-        for (int r = 0; r < R; r++)
+        for (int r = 0; r < R; r++) {
+            if constexpr (FMT == kQ8) {
+                const float d = f16_lo(buf[r].sc >> (ROWS4 ? lo.q_ssh[0] : lo.q_ssh[ccls[r]]));
+#pragma unroll
+                for (int s = 0; s < NS; s++)
+                    acc[r][s] = __builtin_fmaf(d, bs[r][s], acc[r][s]);
+            } else {
+                acc[r][0] = __builtin_fmaf(f16_lo(buf[r].sc), bs[r][0], acc[r][0]);
+                acc[r][1] = __builtin_fmaf(f16_hi(buf[r].sc), bs[r][1], acc[r][1]);
+            }
+        }
+        if (cr == a.rounds - 1) {  // the pass's rows are complete
+            // The sums move to lane (row in group) of outv; they are stored
+            // after the loop, so the loop holds no vector stores (stores share
+            // the counter that the weight-load waits use).
+            const int j0 = (cp - gp0) * R;
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+#pragma unroll
+                for (int s = 0; s < NS; s++) {
+                    const float v = wave_sum(acc[r][s]);
+                    const float t = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+                    outv[s] = lane == j0 + r ? t : outv[s];
+                    acc[r][s] = 0.f;
+                }
+            }
+        }
+        if (++cr == i1) {
+            cr = i0;
+            if (++cp < p1)
+                set_compute_pass(cp);
+        }
+    }
+
+    // Run steps (pass, round) for passes [p0, p1) and rounds [i0, i1).
+    // begin() issues the loads of the first kD steps; loop() computes step s
+    // from buffer s % (kD + 1) after issuing the loads of step s + kD into the
+    // buffer step s - 1 used.  Unrolled kD + 1 times so every buffer index is
+    // a compile-time constant.
+    __device__ __forceinline__ void begin(int p0_, int p1_, int i0_, int i1_)
+    {
+        p1 = p1_, i0 = i0_, i1 = i1_;
+        nsteps = max(0, (p1_ - p0_) * (i1_ - i0_));
+        ip = cp = p0_;
+        ir = cr = i0_;
+        set_issue_pass(ip);
+        if (cp < p1)
+            set_compute_pass(cp);
+#pragma unroll
+        for (int k = 0; k < kD; k++)
+            issue(bufs[k]);
+    }
+
+    // The exit leaves both loops directly: a path from an early exit back to
+    // the loop head would make the compiler's count of loads in flight at the
+    // head pessimistic, and every step would then wait for all of them.
+    __device__ __forceinline__ void loop()
+    {
+        for (int s = 0;; s += kD + 1) {
+#pragma unroll
+            for (int k = 0; k <= kD; k++) {
+                if (s + k >= nsteps)
+                    goto done;
+                issue(bufs[(k + kD) % (kD + 1)]);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(bufs[k]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    done:;
+    }
+
+    // Passes per output group: a group's rows fit one lane each of outv.
+    static constexpr int kGroupPasses = 64 / R;
+
+    __device__ __forceinline__ void begin_group(int g0)
+    {
+        gp0 = g0;
+#pragma unroll
+        for (int s = 0; s < NS; s++)
+            outv[s] = 0.f;
+    }
+
+    // Store the finished rows of the group of passes [gp0, g1).
+    __device__ __forceinline__ void store_group(int g1)
+    {
+        const int nj = min(g1 * R, nrow) - gp0 * R;
+        if (lane < nj) {
+            const int64_t row = first + (int64_t)(gp0 * R + lane) * stride;
 #pragma unroll
             for (int s = 0; s < NS; s++)
-                acc[r][s] = __builtin_fmaf(f16_to_f32(scale_bits<FMT>(w[r], bb, FMT == kQ8 ? 0 : s)), bs[r][s],
-                                           acc[r][s]);
+                a.y[s][row] = outv[s];
+        }
     }
-}
+};
 
-__device__ __forceinline__ float dpp_shr(float v, int ctrl_shift)
-{
-    int iv = __builtin_bit_cast(int, v), r;
-    switch (ctrl_shift) {
-    case 1: r = __builtin_amdgcn_update_dpp(0, iv, 0x111, 0xf, 0xf, true); break;
-    case 2: r = __builtin_amdgcn_update_dpp(0, iv, 0x112, 0xf, 0xf, true); break;
-    case 4: r = __builtin_amdgcn_update_dpp(0, iv, 0x114, 0xf, 0xf, true); break;
-    default: r = __builtin_amdgcn_update_dpp(0, iv, 0x118, 0xf, 0xf, true); break;
-    }
-    return __builtin_bit_cast(float, r);
-}
-
-// Sum over the 16 lanes of a DPP row; the total lands in the row's lane 15.
-__device__ __forceinline__ float row_sum16(float v)
-{
-    v = v + dpp_shr(v, 1);
-    v = v + dpp_shr(v, 2);
-    v = v + dpp_shr(v, 4);
-    v = v + dpp_shr(v, 8);
-    return v;
-}
-
-template <int FMT, int NSP, int NS, int R, bool ALIGNED>
+template <int FMT, int NSP, int NS, int R, bool ROWS4>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a)
 {
     extern __shared__ float4 xs[];
-    const int tid = threadIdx.x, j = tid & (kLanes - 1), g = tid / kLanes;
-    const int64_t row0 = ((int64_t)blockIdx.x * kGroups + g) * R;
+    constexpr int UC = unit_cols<FMT>();
+    // Staging items per thread: enough for the largest chunk of x the LDS
+    // budget holds, so a chunk is staged in one straight-line batch (no loop
+    // between the first weight loads and the main loop, which keeps the
+    // compiler's count of loads in flight exact).
+    constexpr int kMaxChunkItems = (PTI_LDS_BUDGET / (64 * UC * NSP * 4)) * 64 * (UC / 4);
+    constexpr int BATCH = (kMaxChunkItems + kThreads - 1) / kThreads;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    // Rows are dealt round-robin to the SIMDs of the grid: SIMD sg (of nsimd)
+    // gets rows sg, sg + nsimd, sg + 2 nsimd, ..., so every SIMD gets the same
+    // count to within one and, at any moment, the whole GPU reads one window
+    // of consecutive rows.  Waves w, w + 4, w + 8, ... of a workgroup share a
+    // SIMD and take turns through its rows.
+    constexpr int kPerSimd = kWaves / 4;
+    const int64_t nsimd = (int64_t)gridDim.x * 4;
+    const int64_t sg = (int64_t)blockIdx.x * 4 + (wv & 3);
+    const int j = wv >> 2;
+    const int64_t n_simd_rows = sg < a.rows ? (a.rows - sg + nsimd - 1) / nsimd : 0;
+    const int nrow = (int)(n_simd_rows > j ? (n_simd_rows - j + kPerSimd - 1) / kPerSimd : 0);
+    Wave<FMT, NSP, NS, R, ROWS4> w(a, xs, lane, sg + (int64_t)j * nsimd, (int64_t)kPerSimd * nsimd, nrow);
 
-    const uint8_t *rowp[R];
-    bool rvalid[R];
-#pragma unroll
-    for (int r = 0; r < R; r++) {
-        rvalid[r] = row0 + r < a.rows;
-        rowp[r] = a.w + (rvalid[r] ? row0 + r : 0) * a.row_bytes;
-    }
-
-    float acc[R][NS];
-#pragma unroll
-    for (int r = 0; r < R; r++)
-#pragma unroll
-        for (int s = 0; s < NS; s++)
-            acc[r][s] = 0.f;
-
-    Unit<FMT> wa[R], wb[R];
-    // Lanes past the last unit and rows past the last row load a valid unit
-    // (the row's last one, row 0) and skip its compute / store.
-    auto load = [&](Unit<FMT>(&buf)[R], int round) {
-        const int u = min(round * kLanes + j, a.nu - 1);
-        const bool half = 2 * u + 1 >= a.nb;
-#pragma unroll
-        for (int r = 0; r < R; r++)
-            load_unit<FMT, ALIGNED>(buf[r], rowp[r], u, half);
-    };
-    auto compute = [&](const Unit<FMT>(&buf)[R], int round, int il) {
-        const int u = round * kLanes + j;
-        if (u < a.nu)
-            compute_unit<FMT, NSP, NS, R>(buf, xs + (il * 16 * NSP) * kLanes + j, 2 * u + 1 >= a.nb, acc);
-    };
-
-    for (int round0 = 0; round0 < a.rounds; round0 += a.chunk_rounds) {
-        const int nr = min(a.chunk_rounds, a.rounds - round0);
-        load(wa, round0);  // in flight while x is staged
-        if (round0)
-            __syncthreads();  // every lane is done with the previous chunk
-        stage_x<NSP, NS>(a, xs, round0, nr, tid);
+    if (a.chunk_rounds >= a.rounds) {
+        // All of x fits: stage it once, then run every pass.  The x loads go
+        // out first, then the first weight loads, so the LDS stores wait only
+        // for x while the weights are already in flight.
+        float4 v[BATCH][NSP];
+        const int nitems = a.rounds * 64 * (UC / 4);
+        stage_load<UC, NSP, NS, BATCH>(a, 0, v, tid, nitems);
+        __builtin_amdgcn_sched_barrier(0);
+        w.begin(0, min(w.npass, w.kGroupPasses), 0, a.rounds);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_store<UC, NSP, BATCH>(xs, 0, v, tid, nitems);
         __syncthreads();
-        for (int il = 0; il < nr; il += 2) {
-            if (il + 1 < nr)
-                load(wb, round0 + il + 1);
-            compute(wa, round0 + il, il);
-            if (il + 1 >= nr)
-                break;
-            if (il + 2 < nr)
-                load(wa, round0 + il + 2);
-            compute(wb, round0 + il + 1, il + 1);
+        w.begin_group(0);
+        w.loop();
+        w.store_group(min(w.npass, w.kGroupPasses));
+        // waves with more rows than one output group holds
+        for (int g0 = w.kGroupPasses; g0 < w.npass; g0 += w.kGroupPasses) {
+            const int g1 = min(w.npass, g0 + w.kGroupPasses);
+            w.begin_group(g0);
+            w.begin(g0, g1, 0, a.rounds);
+            w.loop();
+            w.store_group(g1);
         }
+    } else {
+        // x in K-chunks: every wave of the workgroup walks the same
+        // (pass, chunk) sequence so that the barriers match
+        const int64_t max_rows = (a.rows + nsimd * kPerSimd - 1) / (nsimd * kPerSimd);
+        const int max_pass = (int)((max_rows + R - 1) / R);
+        for (int p = 0; p < max_pass; p++)
+            for (int i0 = 0; i0 < a.rounds; i0 += a.chunk_rounds) {
+                const int i1 = min(a.rounds, i0 + a.chunk_rounds);
+                __syncthreads();
+                stage_all<UC, NSP, NS, BATCH>(a, xs, i0, i1 - i0, tid);
+                __syncthreads();
+                if (p < w.npass) {
+                    if (i0 == 0)
+                        w.begin_group(p);
+                    w.begin(p, p + 1, i0, i1);
+                    w.loop();
+                    if (i1 == a.rounds)
+                        w.store_group(p + 1);
+                }
+            }
     }
-
-#pragma unroll
-    for (int r = 0; r < R; r++)
-#pragma unroll
-        for (int s = 0; s < NS; s++) {
-            const float v = row_sum16(acc[r][s]);
-            if (j == kLanes - 1 && rvalid[r])
-                a.y[s][row0 + r] = v;
-        }
 }
 
-template <int FMT, int NSP, int NS, int R, bool ALIGNED>
+int device_cus()
+{
+    static thread_local int dev_cached = -1, cus = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    if (dev != dev_cached) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        dev_cached = dev;
+    }
+    return cus;
+}
+
+template <int FMT, int NSP, int NS, bool ROWS4>
 int launch(const GemvArgs &a0, hipStream_t stream)
 {
+    constexpr int UC = unit_cols<FMT>();
+    constexpr int R = FMT == kSSQ ? PTI_RMAX_SSQ : PTI_RMAX_Q8;
     GemvArgs a = a0;
-    const int per_round = kRoundCols * NSP * 4;  // LDS bytes per round of x
+    const int per_round = 64 * UC * NSP * 4;  // LDS bytes per round of x
     a.chunk_rounds = max(1, min(a.rounds, PTI_LDS_BUDGET / per_round));
     const size_t lds = (size_t)a.chunk_rounds * per_round;
-    const int64_t bands = (a.rows + R - 1) / R;
-    const dim3 grid((unsigned)((bands + kGroups - 1) / kGroups));
-    auto kern = gemv_kernel<FMT, NSP, NS, R, ALIGNED>;
+    const int cus = device_cus();
+    if (cus <= 0) {
+        pti::set_hip_error(hipGetLastError());
+        return PTI_ERR_HIP;
+    }
+    const int64_t grid = std::min<int64_t>(cus, (a.rows + kWaves - 1) / kWaves);
+    auto kern = gemv_kernel<FMT, NSP, NS, R, ROWS4>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -359,7 +612,7 @@ int launch(const GemvArgs &a0, hipStream_t stream)
         }
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         pti::set_hip_error(e);
@@ -368,16 +621,16 @@ int launch(const GemvArgs &a0, hipStream_t stream)
     return PTI_OK;
 }
 
-GemvArgs make_args(const void *w, int64_t rows, int64_t cols, int fmt_bytes)
+template <int FMT>
+GemvArgs make_args(const void *w, int64_t rows, int64_t cols)
 {
     GemvArgs a{};
     a.w = static_cast<const uint8_t *>(w);
     a.rows = rows;
     a.cols = (int32_t)cols;
-    a.nb = (int32_t)(cols / PTI_BLOCK);
-    a.row_bytes = (int64_t)a.nb * fmt_bytes;
-    a.nu = (a.nb + 1) / 2;
-    a.rounds = (a.nu + kLanes - 1) / kLanes;
+    a.row_bytes = (cols / PTI_BLOCK) * (FMT == kSSQ ? PTI_SSQ_BLOCK_BYTES : PTI_Q8_BLOCK_BYTES);
+    a.units = (int32_t)(cols / unit_cols<FMT>());
+    a.rounds = (a.units + 63) / 64;
     return a;
 }
 
@@ -401,10 +654,10 @@ int pti_gemv_ssq(const void *w_ssq, const float *x_a, const float *x_b, float *y
         pti::overlap(ya, {x_a, xn}) || pti::overlap(ya, {x_b, xn}) || pti::overlap(yb, {x_a, xn}) ||
         pti::overlap(yb, {x_b, xn}))
         return PTI_ERR_OVERLAP;
-    GemvArgs a = make_args(w_ssq, rows, cols, PTI_SSQ_BLOCK_BYTES);
+    GemvArgs a = make_args<kSSQ>(w_ssq, rows, cols);
     a.x[0] = x_a, a.x[1] = x_b;
     a.y[0] = y_a, a.y[1] = y_b;
-    return launch<kSSQ, 2, 2, PTI_R_SSQ, true>(a, static_cast<hipStream_t>(stream));
+    return launch<kSSQ, 2, 2, true>(a, static_cast<hipStream_t>(stream));
 }
 
 int pti_gemv_q8_multi(const void *w_q8, const float *x, float *y, int64_t rows, int64_t cols, int n_streams,
@@ -422,22 +675,26 @@ int pti_gemv_q8_multi(const void *w_q8, const float *x, float *y, int64_t rows, 
                  yn = size_t(n_streams) * rows * 4;
     if (pti::overlap({y, yn}, {w_q8, wn}) || pti::overlap({y, yn}, {x, xn}))
         return PTI_ERR_OVERLAP;
-    GemvArgs a = make_args(w_q8, rows, cols, PTI_Q8_BLOCK_BYTES);
+    GemvArgs a = make_args<kQ8>(w_q8, rows, cols);
     for (int s = 0; s < n_streams; s++) {
         a.x[s] = x + (size_t)s * cols;
         a.y[s] = y + (size_t)s * rows;
     }
-    const bool aligned_rows = (a.nb % 2) == 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    // rows start on dword boundaries when a row holds an even number of blocks
+    if ((cols / PTI_BLOCK) % 2 == 0) {
+        switch (n_streams) {
+        case 1: return launch<kQ8, 1, 1, true>(a, st);
+        case 2: return launch<kQ8, 2, 2, true>(a, st);
+        case 3: return launch<kQ8, 4, 3, true>(a, st);
+        default: return launch<kQ8, 4, 4, true>(a, st);
+        }
+    }
     switch (n_streams) {
-    case 1:
-        return aligned_rows ? launch<kQ8, 1, 1, PTI_R_Q8_N1, true>(a, st) : launch<kQ8, 1, 1, PTI_R_Q8_N1, false>(a, st);
-    case 2:
-        return aligned_rows ? launch<kQ8, 2, 2, PTI_R_Q8_N2, true>(a, st) : launch<kQ8, 2, 2, PTI_R_Q8_N2, false>(a, st);
-    case 3:
-        return aligned_rows ? launch<kQ8, 4, 3, PTI_R_Q8_N4, true>(a, st) : launch<kQ8, 4, 3, PTI_R_Q8_N4, false>(a, st);
-    default:
-        return aligned_rows ? launch<kQ8, 4, 4, PTI_R_Q8_N4, true>(a, st) : launch<kQ8, 4, 4, PTI_R_Q8_N4, false>(a, st);
+    case 1: return launch<kQ8, 1, 1, false>(a, st);
+    case 2: return launch<kQ8, 2, 2, false>(a, st);
+    case 3: return launch<kQ8, 4, 3, false>(a, st);
+    default: return launch<kQ8, 4, 4, false>(a, st);
     }
 }
 
