@@ -72,6 +72,7 @@ extern "C" {
 #define PTI_MAX_ROWS 2147483647LL
 #define PTI_MAX_COLS (1LL << 24)
 #define PTI_MAX_VOCAB 2147483647LL
+#define PTI_MAX_ELEMS (1LL << 40)  /* element count limit of the elementwise and norm calls */
 
 enum pti_status {
     PTI_OK = 0,
@@ -161,6 +162,122 @@ int pti_gemv_q8_multi(const void *w_q8, const float *x, float *y, int64_t rows, 
  * [1]; outputs must not overlap inputs or each other. */
 int pti_verify_argmax(const float *logits, const int32_t *tokens_in, int32_t *argmax_out,
                       int32_t *accept_out, int64_t vocab, int n_streams, void *stream);
+
+/* Sampled verify [README, how acceptance works: at temperature > 0 a guess is
+ * confirmed when it equals the token the stream before it samples, which
+ * happens with the collision probability sum_x p(x)^2; Digest, implementation
+ * architecture: the softmax and verify kernels]: per stream n, weights
+ * w_j = exp((logits[n][j] - max_j logits[n][j]) / temperature) in fp64, and
+ * tokens_out[n] = the first index j of nonzero weight at which a running sum
+ * of the weights exceeds uniforms[n] * sum_j w_j (if rounding leaves none, the
+ * last index of nonzero weight before the target).  The running sum is taken
+ * in a fixed, index-monotone order (per 1/1024 of the vocabulary in index
+ * order, then across those parts in order), so the draw equals an in-order
+ * sequential inverse-CDF draw except where u * sum lies within a few fp64 ulps
+ * of a cumulative sum.  accept_out[0] as in pti_verify_argmax, with the drawn
+ * tokens in place of the argmaxes.
+ * logits: device fp32 [n_streams][vocab] (finite; otherwise tokens_out is
+ * unspecified and may be -1); tokens_in: device int32 [n_streams];
+ * uniforms: device fp64 [n_streams] in [0, 1) (8-byte aligned); temperature:
+ * finite, > 0; tokens_out: device int32 [n_streams]; accept_out: device int32
+ * [1].  Outputs must not overlap inputs or each other. */
+int pti_sample_verify(const float *logits, const int32_t *tokens_in, const double *uniforms, double temperature,
+                      int32_t *tokens_out, int32_t *accept_out, int64_t vocab, int n_streams, void *stream);
+
+/* ------------------------------------------------------------------------- */
+/* Decoder-stack glue [Digest, implementation architecture: the forward pass in
+ * which one weight load serves every stream].  Device calls, conventions as
+ * above; they compute in fp64 internally and round once to fp32, so each
+ * output is within 1 fp32 ulp of the exact value of its formula on the given
+ * fp32 inputs (bit-exact for pti_embed_* and pti_add).                      */
+
+/* x[n][c] = scale(tokens[n], c/32) * q[tokens[n]][c]: row tokens[n] of a Q8
+ * matrix [vocab][hidden], dequantised.  tokens: device int32 [n_streams];
+ * x: device fp32 [n_streams][hidden].  A token outside [0, vocab) yields a row
+ * of NaN. */
+int pti_embed_q8(const void *w_q8, const int32_t *tokens, float *x, int64_t vocab, int64_t hidden, int n_streams,
+                 void *stream);
+/* Two-stream form over an SSQ matrix [vocab][hidden]: x[0] = twin A's row
+ * tokens[0], x[1] = twin B's row tokens[1].  tokens: device int32 [2];
+ * x: device fp32 [2][hidden]. */
+int pti_embed_ssq(const void *w_ssq, const int32_t *tokens, float *x, int64_t vocab, int64_t hidden, void *stream);
+
+/* y[n][c] = x[n][c] / sqrt(mean_c x[n][c]^2 + eps) (no gain), for
+ * n < n_streams; x, y: device fp32 [n_streams][dim]; y may equal x (in place)
+ * but not overlap it otherwise; eps finite, >= 0; 1 <= dim <= PTI_MAX_ELEMS. */
+int pti_rmsnorm(const float *x, float *y, int64_t dim, int n_streams, float eps, void *stream);
+
+/* y[i] = g[i] / (1 + exp(-g[i])) * u[i] (SiLU gate times up projection), i < n.
+ * y may equal g or u (in place) but not overlap them otherwise. */
+int pti_silu_mul(const float *g, const float *u, float *y, int64_t n, void *stream);
+
+/* y[i] = a[i] + b[i] in fp32 (the residual add), i < n.  y may equal a or b. */
+int pti_add(const float *a, const float *b, float *y, int64_t n, void *stream);
+
+/* ------------------------------------------------------------------------- */
+/* Toy decoder stack and the staggered multi-stream decode loop.
+ *
+ * The pages run one model as N staggered streams that share every weight load
+ * [README, how acceptance works; Digest, implementation architecture].  The
+ * stand-in model is an MLP-residual stack:
+ *   h_0 = embed row of the token;
+ *   h_{l+1} = h_l + down_l(silu(gate_l r_l) * up_l r_l), r_l = rmsnorm(h_l);
+ *   logits = head rmsnorm(h_L).
+ * All matrices share one format.  PTI_FMT_Q8: each pass serves n_streams in
+ * 1..4 through the multi-stream GEMV.  PTI_FMT_SSQ: a twin pair packed side by
+ * side; a pass serves exactly 2 streams, stream 0 on twin A (the verifier) and
+ * stream 1 on twin B (the drafter).                                          */
+
+#define PTI_FMT_Q8 0
+#define PTI_FMT_SSQ 1
+#define PTI_TOY_MAX_LAYERS 64
+
+typedef struct pti_toy_model {
+    int32_t format;   /* PTI_FMT_Q8 or PTI_FMT_SSQ */
+    int32_t n_layers; /* 1 .. PTI_TOY_MAX_LAYERS */
+    int64_t hidden;   /* multiple of 32 */
+    int64_t ffn;      /* multiple of 32 */
+    int64_t vocab;
+    float eps;        /* RMSNorm epsilon, finite, >= 0 */
+    const void *embed;       /* device, [vocab][hidden] */
+    const void *head;        /* device, [vocab][hidden] */
+    const void *const *gate; /* host array of n_layers device pointers, [ffn][hidden] each */
+    const void *const *up;   /* same */
+    const void *const *down; /* host array of n_layers device pointers, [hidden][ffn] each */
+} pti_toy_model;
+
+/* Device workspace bytes needed by pti_toy_forward / pti_toy_decode for this
+ * model and stream count; 0 if the model or n_streams is invalid. */
+size_t pti_toy_workspace_bytes(const pti_toy_model *m, int n_streams);
+
+/* One pass: logits[n][*] for tokens[n], n < n_streams (2 for SSQ).
+ * tokens: device int32 [n_streams]; logits: device fp32 [n_streams][vocab];
+ * work: device, >= pti_toy_workspace_bytes bytes, 256-byte aligned, not
+ * overlapping tokens or logits.  Enqueued on `stream`, no synchronisation. */
+int pti_toy_forward(const pti_toy_model *m, const int32_t *tokens, float *logits, void *work, size_t work_bytes,
+                    int n_streams, void *stream);
+
+/* The staggered decode loop, n_steps steps after first_token.
+ *   - Ramp-up (step 0): stream i >= 1 gets its first input from single-stream
+ *     passes, x_i = draw(x_{i-1}), pass slots N .. 2N-2.
+ *   - Step k = 1 .. n_steps: one N-stream pass (slots 0 .. N-1) draws o_0 ..
+ *     o_{N-1}; accepts[k-1] = 1 + leading run of x_i == o_{i-1};
+ *     committed[k-1] = o_0; stream i's next input is o_i.
+ *   - When accepts[k-1] = a < N, streams a .. N-1 ran on stale guesses: their
+ *     next inputs are drawn again by single-stream passes starting from
+ *     o_{a-1} (slots N .. 2N-1-a).
+ * A draw is the argmax of the logits (temperature == 0) or the sampled-verify
+ * draw at that temperature with uniform uniforms[k * 2N + slot].  A
+ * single-stream pass of stream i >= 1 runs twin B in the SSQ format.
+ * uniforms: host fp64 [(n_steps + 1) * 2 * N], may be NULL when temperature
+ * is 0.  committed, accepts: host int32 [n_steps].  passes: host int32
+ * [(N - 1) + n_steps * (2N - 1)][5] or NULL; each executed draw appends
+ * (step, slot, stream, input token, output token) and *n_passes (host, may be
+ * NULL) receives their count.  Synchronises `stream` after every pass (the
+ * next inputs depend on the accept count). */
+int pti_toy_decode(const pti_toy_model *m, int32_t first_token, int n_streams, int n_steps, double temperature,
+                   const double *uniforms, void *work, size_t work_bytes, int32_t *committed, int32_t *accepts,
+                   int32_t *passes, int64_t *n_passes, void *stream);
 
 #ifdef __cplusplus
 }

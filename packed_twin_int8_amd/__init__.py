@@ -24,8 +24,12 @@ from .build import LIB as LIB_PATH
 
 __all__ = [
     "PtiError", "lib", "ssq_bytes", "q8_bytes", "pack_ssq", "unpack_ssq", "pack_q8", "unpack_q8",
-    "ssq_split", "ssq_join", "gemv_ssq", "gemv_q8_multi", "verify_argmax", "status_str",
+    "ssq_split", "ssq_join", "gemv_ssq", "gemv_q8_multi", "verify_argmax", "status_str", "sample_verify",
+    "embed_q8", "embed_ssq", "rmsnorm", "silu_mul", "add", "ToyStack", "FMT_Q8", "FMT_SSQ",
 ]
+
+FMT_Q8, FMT_SSQ = 0, 1
+TOY_MAX_LAYERS = 64
 
 PTI_OK = 0
 STATUS = {0: "PTI_OK", -1: "PTI_ERR_NULL", -2: "PTI_ERR_SHAPE", -3: "PTI_ERR_NSTREAMS", -4: "PTI_ERR_ALIGN",
@@ -35,8 +39,17 @@ STATUS = {0: "PTI_OK", -1: "PTI_ERR_NULL", -2: "PTI_ERR_SHAPE", -3: "PTI_ERR_NST
 EXPORTS = (
     "pti_status_str", "pti_last_hip_error", "pti_abi_version", "pti_ssq_bytes", "pti_q8_bytes", "pti_pack_ssq",
     "pti_unpack_ssq", "pti_pack_q8", "pti_unpack_q8", "pti_ssq_split", "pti_ssq_join", "pti_gemv_ssq",
-    "pti_gemv_q8_multi", "pti_verify_argmax",
+    "pti_gemv_q8_multi", "pti_verify_argmax", "pti_sample_verify", "pti_embed_q8", "pti_embed_ssq", "pti_rmsnorm",
+    "pti_silu_mul", "pti_add", "pti_toy_workspace_bytes", "pti_toy_forward", "pti_toy_decode",
 )
+
+
+class ToyModelC(ctypes.Structure):
+    """struct pti_toy_model."""
+    _fields_ = [("format", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int64),
+                ("ffn", ctypes.c_int64), ("vocab", ctypes.c_int64), ("eps", ctypes.c_float),
+                ("embed", ctypes.c_void_p), ("head", ctypes.c_void_p), ("gate", ctypes.POINTER(ctypes.c_void_p)),
+                ("up", ctypes.POINTER(ctypes.c_void_p)), ("down", ctypes.POINTER(ctypes.c_void_p))]
 
 
 class PtiError(RuntimeError):
@@ -80,6 +93,17 @@ def lib() -> ctypes.CDLL:
         L.pti_gemv_ssq.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _P]
         L.pti_gemv_q8_multi.argtypes = [_P, _P, _P, _I64, _I64, _INT, _P]
         L.pti_verify_argmax.argtypes = [_P, _P, _P, _P, _I64, _INT, _P]
+        L.pti_sample_verify.argtypes = [_P, _P, _P, ctypes.c_double, _P, _P, _I64, _INT, _P]
+        L.pti_embed_q8.argtypes = [_P, _P, _P, _I64, _I64, _INT, _P]
+        L.pti_embed_ssq.argtypes = [_P, _P, _P, _I64, _I64, _P]
+        L.pti_rmsnorm.argtypes = [_P, _P, _I64, _INT, ctypes.c_float, _P]
+        L.pti_silu_mul.argtypes = [_P, _P, _P, _I64, _P]
+        L.pti_add.argtypes = [_P, _P, _P, _I64, _P]
+        L.pti_toy_workspace_bytes.argtypes = [ctypes.POINTER(ToyModelC), _INT]
+        L.pti_toy_workspace_bytes.restype = ctypes.c_size_t
+        L.pti_toy_forward.argtypes = [ctypes.POINTER(ToyModelC), _P, _P, _P, ctypes.c_size_t, _INT, _P]
+        L.pti_toy_decode.argtypes = [ctypes.POINTER(ToyModelC), ctypes.c_int32, _INT, _INT, ctypes.c_double, _P, _P,
+                                     ctypes.c_size_t, _P, _P, _P, ctypes.POINTER(ctypes.c_int64), _P]
         for name in EXPORTS:  # every declared symbol must resolve
             getattr(L, name)
         _lib = L
@@ -257,3 +281,162 @@ def verify_argmax(logits, tokens_in, argmax_out=None, accept_out=None, stream=No
                                                         argmax_out.data_ptr(), accept_out.data_ptr(), vocab, n,
                                                         _stream(stream)))
     return argmax_out, accept_out
+
+
+def sample_verify(logits, tokens_in, uniforms, temperature: float, tokens_out=None, accept_out=None, stream=None):
+    """Sampled verify at temperature > 0: one inverse-CDF draw per stream with
+    uniforms[n], then the accept count.  logits: float32 [N, vocab];
+    tokens_in: int32 [N]; uniforms: float64 [N] (device)."""
+    torch = _torch()
+    _dev(logits, "logits", torch.float32), _dev(tokens_in, "tokens_in", torch.int32)
+    _dev(uniforms, "uniforms", torch.float64)
+    if logits.dim() == 1:
+        logits = logits.unsqueeze(0)
+    n, vocab = logits.shape
+    if tokens_in.numel() != n or uniforms.numel() != n:
+        raise ValueError("sample_verify: tokens_in and uniforms need one entry per stream")
+    dev = logits.device
+    tokens_out = torch.empty(n, dtype=torch.int32, device=dev) if tokens_out is None else _dev(
+        tokens_out, "tokens_out", torch.int32)
+    accept_out = torch.empty(1, dtype=torch.int32, device=dev) if accept_out is None else _dev(
+        accept_out, "accept_out", torch.int32)
+    _check("pti_sample_verify", lib().pti_sample_verify(logits.data_ptr(), tokens_in.data_ptr(), uniforms.data_ptr(),
+                                                        float(temperature), tokens_out.data_ptr(),
+                                                        accept_out.data_ptr(), vocab, n, _stream(stream)))
+    return tokens_out, accept_out
+
+
+# ---------------------------------------------------------------- decoder-stack glue
+
+def embed_q8(w, tokens, vocab: int, hidden: int, x=None, stream=None):
+    """Rows tokens[n] of a Q8 matrix [vocab, hidden], dequantised -> float32 [N, hidden]."""
+    torch = _torch()
+    _dev(w, "w", torch.uint8), _dev(tokens, "tokens", torch.int32)
+    n = tokens.numel()
+    if w.numel() != q8_bytes(vocab, hidden):
+        raise ValueError("embed_q8: weight size mismatch")
+    x = torch.empty((n, hidden), dtype=torch.float32, device=w.device) if x is None else _dev(x, "x", torch.float32)
+    _check("pti_embed_q8", lib().pti_embed_q8(w.data_ptr(), tokens.data_ptr(), x.data_ptr(), vocab, hidden, n,
+                                              _stream(stream)))
+    return x
+
+
+def embed_ssq(w, tokens, vocab: int, hidden: int, x=None, stream=None):
+    """Twin A's row tokens[0] and twin B's row tokens[1] of an SSQ matrix -> float32 [2, hidden]."""
+    torch = _torch()
+    _dev(w, "w", torch.uint8), _dev(tokens, "tokens", torch.int32)
+    if tokens.numel() != 2 or w.numel() != ssq_bytes(vocab, hidden):
+        raise ValueError("embed_ssq: shape mismatch")
+    x = torch.empty((2, hidden), dtype=torch.float32, device=w.device) if x is None else _dev(x, "x", torch.float32)
+    _check("pti_embed_ssq", lib().pti_embed_ssq(w.data_ptr(), tokens.data_ptr(), x.data_ptr(), vocab, hidden,
+                                                _stream(stream)))
+    return x
+
+
+def rmsnorm(x, eps: float, y=None, stream=None):
+    """y[n] = x[n] / sqrt(mean(x[n]^2) + eps) per row of x [N, dim]."""
+    torch = _torch()
+    _dev(x, "x", torch.float32)
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    n, dim = x.shape
+    y = torch.empty_like(x) if y is None else _dev(y, "y", torch.float32)
+    _check("pti_rmsnorm", lib().pti_rmsnorm(x.data_ptr(), y.data_ptr(), dim, n, float(eps), _stream(stream)))
+    return y
+
+
+def silu_mul(g, u, y=None, stream=None):
+    """y = silu(g) * u elementwise."""
+    torch = _torch()
+    _dev(g, "g", torch.float32), _dev(u, "u", torch.float32)
+    if g.shape != u.shape:
+        raise ValueError("silu_mul: shape mismatch")
+    y = torch.empty_like(g) if y is None else _dev(y, "y", torch.float32)
+    _check("pti_silu_mul", lib().pti_silu_mul(g.data_ptr(), u.data_ptr(), y.data_ptr(), g.numel(), _stream(stream)))
+    return y
+
+
+def add(a, b, y=None, stream=None):
+    """y = a + b elementwise (fp32)."""
+    torch = _torch()
+    _dev(a, "a", torch.float32), _dev(b, "b", torch.float32)
+    if a.shape != b.shape:
+        raise ValueError("add: shape mismatch")
+    y = torch.empty_like(a) if y is None else _dev(y, "y", torch.float32)
+    _check("pti_add", lib().pti_add(a.data_ptr(), b.data_ptr(), y.data_ptr(), a.numel(), _stream(stream)))
+    return y
+
+
+class ToyStack:
+    """Device weights of the decoder stack plus the struct that names them.
+
+    ``mats``: dict with "emb", "head" (uint8 tensors [vocab, ...]) and
+    "gate", "up", "down" (lists of uint8 tensors), all packed in ``fmt``
+    (FMT_Q8 or FMT_SSQ) and resident on the GPU."""
+
+    def __init__(self, mats: dict, hidden: int, ffn: int, vocab: int, fmt: int = FMT_Q8, eps: float = 1e-6):
+        torch = _torch()
+        self.mats = mats  # keeps the tensors alive
+        L = len(mats["gate"])
+        if not (1 <= L <= TOY_MAX_LAYERS) or len(mats["up"]) != L or len(mats["down"]) != L:
+            raise ValueError("ToyStack: layer lists must have equal length in [1, 64]")
+        nbytes = ssq_bytes if fmt == FMT_SSQ else q8_bytes
+        want = {"emb": nbytes(vocab, hidden), "head": nbytes(vocab, hidden)}
+        for k, v in want.items():
+            _dev(mats[k], k, torch.uint8)
+            if mats[k].numel() != v:
+                raise ValueError(f"ToyStack: {k} size mismatch")
+        for k, (r, c) in (("gate", (ffn, hidden)), ("up", (ffn, hidden)), ("down", (hidden, ffn))):
+            for t in mats[k]:
+                _dev(t, k, torch.uint8)
+                if t.numel() != nbytes(r, c):
+                    raise ValueError(f"ToyStack: {k} size mismatch")
+        Arr = ctypes.c_void_p * L
+        self._gate = Arr(*[t.data_ptr() for t in mats["gate"]])
+        self._up = Arr(*[t.data_ptr() for t in mats["up"]])
+        self._down = Arr(*[t.data_ptr() for t in mats["down"]])
+        vp = ctypes.POINTER(ctypes.c_void_p)
+        self.c = ToyModelC(fmt, L, hidden, ffn, vocab, eps, mats["emb"].data_ptr(), mats["head"].data_ptr(),
+                           ctypes.cast(self._gate, vp), ctypes.cast(self._up, vp), ctypes.cast(self._down, vp))
+        self.fmt, self.hidden, self.ffn, self.vocab, self.device = fmt, hidden, ffn, vocab, mats["emb"].device
+
+    def workspace(self, n_streams: int):
+        nb = lib().pti_toy_workspace_bytes(ctypes.byref(self.c), n_streams)
+        if nb == 0:
+            raise PtiError("pti_toy_workspace_bytes", -3 if self.fmt == FMT_SSQ else -2)
+        torch = _torch()
+        return torch.empty(nb, dtype=torch.uint8, device=self.device)  # torch allocations are 256-byte aligned
+
+    def forward(self, tokens, logits=None, work=None, stream=None):
+        """logits [N, vocab] for device int32 tokens [N]."""
+        torch = _torch()
+        _dev(tokens, "tokens", torch.int32)
+        n = tokens.numel()
+        work = self.workspace(n) if work is None else work
+        logits = torch.empty((n, self.vocab), dtype=torch.float32, device=self.device) if logits is None else _dev(
+            logits, "logits", torch.float32)
+        _check("pti_toy_forward", lib().pti_toy_forward(ctypes.byref(self.c), tokens.data_ptr(), logits.data_ptr(),
+                                                        work.data_ptr(), work.numel(), n, _stream(stream)))
+        return logits
+
+    def decode(self, first_token: int, n_streams: int, n_steps: int, temperature: float = 0.0, uniforms=None,
+               work=None, stream=None):
+        """The staggered decode loop.  uniforms: float64 array [(n_steps+1) * 2N]
+        (host) when temperature > 0.  Returns (committed, accepts, passes) as
+        numpy arrays; passes rows are (step, slot, stream, input, output)."""
+        work = self.workspace(n_streams) if work is None else work
+        N = n_streams
+        committed = np.zeros(max(n_steps, 1), np.int32)
+        accepts = np.zeros(max(n_steps, 1), np.int32)
+        passes = np.zeros(((N - 1) + n_steps * (2 * N - 1), 5), np.int32)
+        npass = ctypes.c_int64(0)
+        u = None
+        if temperature > 0:
+            u = _np(uniforms, np.float64)
+            if u.size != (n_steps + 1) * 2 * N:
+                raise ValueError("decode: uniforms must hold (n_steps + 1) * 2 * n_streams values")
+        _check("pti_toy_decode", lib().pti_toy_decode(
+            ctypes.byref(self.c), int(first_token), N, n_steps, float(temperature), None if u is None else _hp(u),
+            work.data_ptr(), work.numel(), _hp(committed), _hp(accepts), _hp(passes) if passes.size else None,
+            ctypes.byref(npass), _stream(stream)))
+        return committed[:n_steps], accepts[:n_steps], passes[:npass.value]

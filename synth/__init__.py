@@ -103,14 +103,19 @@ LAYER_SHAPES = (
 TOY = dict(hidden=2048, ffn=5632, layers=4, vocab=32000)
 
 
-def toy_weights(seed: int = SEED_TOY, lm_scale_div: float = 1.0):
+def toy_weights(seed: int = SEED_TOY, lm_scale_div: float = 1.0, hidden: int | None = None, ffn: int | None = None,
+                layers: int | None = None, vocab: int | None = None):
     """Raw weights of the toy stack, drawn in a fixed order: embedding Q8
     [vocab, hidden]; per layer gate [ffn, hidden], up [ffn, hidden],
     down [hidden, ffn]; LM head [vocab, hidden].  Each matrix draws its int8
     values then its f16 scales.  ``lm_scale_div`` divides the LM-head scales
-    (before f16 rounding) to flatten the output distribution."""
+    (before f16 rounding) to flatten the output distribution.  The sizes
+    default to TOY; smaller ones give the same distributions at test scale."""
     g = rng(seed)
-    h, f, L, V = TOY["hidden"], TOY["ffn"], TOY["layers"], TOY["vocab"]
+    h = TOY["hidden"] if hidden is None else hidden
+    f = TOY["ffn"] if ffn is None else ffn
+    L = TOY["layers"] if layers is None else layers
+    V = TOY["vocab"] if vocab is None else vocab
 
     def mat(r, c, div=1.0):
         q = int8_uniform(g, (r, c))

@@ -1,0 +1,519 @@
+"""GPU parity of the decoder-stack glue kernels, the sampled verify, the
+stack's forward pass and the staggered decode loop, through the C ABI.
+
+How parity is established (the composed stack has no useful worst-case error
+bound: propagating |W| |error| through four MLP layers gives bounds near 1e11):
+  * every kernel is compared with the oracle's operation applied to the GPU's
+    own inputs, each with its own bound -- GEMVs 1e-5 * sum|terms|, RMSNorm and
+    SiLU*up within one fp32 ulp, embedding and add bit-exact;
+  * the library's forward pass equals that op-by-op composition bitwise;
+  * every token the decode loop draws equals the oracle's decision (argmax, or
+    the inverse-CDF draw with the same uniform) taken on the GPU's logits for
+    that pass, in the same precision (fp32 compare / fp64 sums);
+  * the loop's control (ramp-up, commits, accept counts, re-draws after a
+    reject) is replayed through the oracle's loop;
+  * sampled acceptance matches the collision probability sum p^2 from the
+    oracle's own fp64 logits (binomial z-tests).
+The oracle's fp64 logits are also compared with the GPU's as a sanity check
+(relative to the logits' spread), not as a parity bar.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import toy
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-6
+TEMP = 0.7
+BAND = 1e-11  # fp64 cumulative sums in another order land within this of each other (relative to the total)
+ULP = 2.0 ** -23
+TINY = 2.0 ** -149
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _pti():
+    import packed_twin_int8_amd as pti
+    return pti
+
+
+def dev(a, dtype=None):
+    torch = _torch()
+    a = np.ascontiguousarray(a if dtype is None else np.asarray(a, dtype=dtype))
+    return torch.from_numpy(a).to("cuda")
+
+
+def host(t):
+    _torch().cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def within_ulp(got, want):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    return np.all(np.abs(got - want) <= ULP * np.abs(want) + TINY)
+
+
+def dims(raw):
+    vocab, hidden = raw["emb"]["Q"].shape
+    return hidden, raw["layers"][0]["gate"]["Q"].shape[0], vocab
+
+
+class Stack:
+    """GPU stack (library packer, device weights) plus the oracle's packed
+    copies of the same matrices (oracle packer) for the op-level checks."""
+
+    def __init__(self, raw, fmt, raw_b=None):
+        pti = _pti()
+        self.raw, self.raw_b, self.fmt = raw, (raw if raw_b is None else raw_b), fmt
+        O = oracle.default()
+        self.H, self.F, self.V = dims(raw)
+
+        def both(key_a, key_b):
+            if fmt == pti.FMT_Q8:
+                return pti.pack_q8(key_a["Q"], key_a["S"]), O.pack_q8(key_a["Q"], key_a["S"])
+            return (pti.pack_ssq(key_a["Q"], key_b["Q"], key_a["S"], key_b["S"]),
+                    O.pack_ssq(key_a["Q"], key_b["Q"], key_a["S"], key_b["S"]))
+
+        mats, self.orc = {"gate": [], "up": [], "down": []}, {"gate": [], "up": [], "down": []}
+        for k in ("emb", "head"):
+            g, o = both(raw[k], self.raw_b[k])
+            mats[k], self.orc[k] = dev(g), o
+        for la, lb in zip(raw["layers"], self.raw_b["layers"]):
+            for k in ("gate", "up", "down"):
+                g, o = both(la[k], lb[k])
+                mats[k].append(dev(g))
+                self.orc[k].append(o)
+        self.gpu = pti.ToyStack(mats, self.H, self.F, self.V, fmt, EPS)
+        self.mats = mats
+        self.n = 2 if fmt == pti.FMT_SSQ else 4
+
+    # ------------------------------------------------------------ op wrappers
+    def gemv(self, w, x):
+        pti = _pti()
+        if self.fmt == pti.FMT_SSQ:
+            ya, yb = pti.gemv_ssq(w, x[0].contiguous(), x[1].contiguous())
+            return _torch().stack([ya, yb])
+        return pti.gemv_q8_multi(w, x)
+
+    def oracle_gemv(self, P, rows, cols, X):
+        O = oracle.default()
+        if self.fmt == _pti().FMT_SSQ:
+            ya, yb, ta, tb = O.gemv_ssq(P, rows, cols, X[0], X[1])
+            return np.stack([ya, yb]), np.stack([ta, tb])
+        return O.gemv_q8(P, rows, cols, X)
+
+    def check_gemv(self, P, rows, cols, x_gpu, y_gpu, what):
+        y, t = self.oracle_gemv(P, rows, cols, host(x_gpu))
+        got = host(y_gpu).astype(np.float64)
+        bad = np.abs(got - y) > 1e-5 * t
+        assert not bad.any(), f"{what}: {bad.sum()} outputs outside 1e-5*sum|terms|"
+
+    def embed_rows(self, tokens):
+        """Exact embedding rows (twin A for stream 0, twin B for stream 1 under SSQ)."""
+        out = []
+        for s, t in enumerate(tokens):
+            src = self.raw_b if (self.fmt == _pti().FMT_SSQ and s == 1) else self.raw
+            out.append(toy.dequant(src["emb"]["Q"][t:t + 1], src["emb"]["S"][t:t + 1])[0])
+        return np.array(out)
+
+    def composed_forward(self, tokens):
+        """The forward pass op by op through the C ABI, each op checked against
+        the oracle's operation on the GPU's inputs; returns the logits tensor."""
+        pti, torch = _pti(), _torch()
+        tok = dev(tokens, np.int32)
+        H, F, V = self.H, self.F, self.V
+        if self.fmt == pti.FMT_SSQ:
+            h = pti.embed_ssq(self.mats["emb"], tok, V, H)
+        else:
+            h = pti.embed_q8(self.mats["emb"], tok, V, H)
+        assert np.array_equal(host(h), self.embed_rows(tokens).astype(np.float32)), "embedding rows"
+        for l in range(len(self.raw["layers"])):
+            r = pti.rmsnorm(h, EPS)
+            assert within_ulp(host(r), toy.rmsnorm(host(h).astype(np.float64), EPS)), f"rmsnorm layer {l}"
+            g = self.gemv(self.mats["gate"][l], r)
+            u = self.gemv(self.mats["up"][l], r)
+            self.check_gemv(self.orc["gate"][l], F, H, r, g, f"gate {l}")
+            self.check_gemv(self.orc["up"][l], F, H, r, u, f"up {l}")
+            m = pti.silu_mul(g, u)
+            gh, uh = host(g).astype(np.float64), host(u).astype(np.float64)
+            assert within_ulp(host(m), toy.silu(gh) * uh), f"silu*up layer {l}"
+            d = self.gemv(self.mats["down"][l], m)
+            self.check_gemv(self.orc["down"][l], H, F, m, d, f"down {l}")
+            h2 = pti.add(h, d)
+            assert np.array_equal(host(h2), host(h) + host(d)), f"residual add layer {l}"
+            h = h2
+        r = pti.rmsnorm(h, EPS)
+        assert within_ulp(host(r), toy.rmsnorm(host(h).astype(np.float64), EPS)), "final rmsnorm"
+        lg = self.gemv(self.mats["head"], r)
+        self.check_gemv(self.orc["head"], V, H, r, lg, "head")
+        torch.cuda.synchronize()
+        return lg
+
+    def logits_for(self, tokens, twin_b=False):
+        """GPU logits of single tokens (through the library's forward), one row per
+        token; twin_b selects twin B's rows under SSQ."""
+        rows = []
+        toks = list(tokens)
+        if self.fmt == _pti().FMT_SSQ:
+            for t in toks:
+                lg = host(self.gpu.forward(dev([t, t], np.int32)))
+                rows.append(lg[1 if twin_b else 0])
+        else:
+            for i in range(0, len(toks), 4):
+                chunk = toks[i:i + 4]
+                rows.extend(host(self.gpu.forward(dev(chunk, np.int32))))
+        return np.array(rows, dtype=np.float32)
+
+
+@pytest.fixture(scope="module")
+def full_raw():
+    return synth.toy_weights(synth.SEED_TOY)
+
+
+@pytest.fixture(scope="module")
+def full_oracle(full_raw):
+    return toy.ToyModel(full_raw, EPS)
+
+
+@pytest.fixture(scope="module")
+def full_q8(full_raw):
+    return Stack(full_raw, _pti().FMT_Q8)
+
+
+@pytest.fixture(scope="module")
+def full_ssq(full_raw):
+    return Stack(full_raw, _pti().FMT_SSQ)  # the model packed against itself
+
+
+@pytest.fixture(scope="module")
+def small_raw():
+    # ragged sizes: 3 blocks of hidden, 5 of ffn, a vocabulary that is not a multiple of 4
+    return synth.toy_weights(synth.SEED_TOY + 10, hidden=96, ffn=160, layers=3, vocab=1001)
+
+
+# ------------------------------------------------------------------ glue ops
+
+def test_embed_q8_rows_exact_and_nan_for_bad_tokens(small_raw):
+    pti = _pti()
+    H, F, V = dims(small_raw)
+    w = dev(pti.pack_q8(small_raw["emb"]["Q"], small_raw["emb"]["S"]))
+    for toks in ([0], [V - 1, 0], [5, 5, 999], [17, 1000, 3, 0]):
+        x = host(pti.embed_q8(w, dev(toks, np.int32), V, H))
+        want = toy.dequant(small_raw["emb"]["Q"][toks], small_raw["emb"]["S"][toks]).astype(np.float32)
+        assert np.array_equal(x, want)
+    x = host(pti.embed_q8(w, dev([-1, V, 2], np.int32), V, H))
+    assert np.isnan(x[0]).all() and np.isnan(x[1]).all() and not np.isnan(x[2]).any()
+
+
+def test_embed_ssq_takes_twin_a_then_twin_b(small_raw):
+    pti = _pti()
+    H, F, V = dims(small_raw)
+    other = synth.toy_weights(99, hidden=96, ffn=160, layers=1, vocab=1001)
+    A, B = small_raw["emb"], other["emb"]
+    w = dev(pti.pack_ssq(A["Q"], B["Q"], A["S"], B["S"]))
+    for t0, t1 in ((0, 0), (3, 1000), (1000, 7)):
+        x = host(pti.embed_ssq(w, dev([t0, t1], np.int32), V, H))
+        assert np.array_equal(x[0], toy.dequant(A["Q"][t0:t0 + 1], A["S"][t0:t0 + 1])[0].astype(np.float32))
+        assert np.array_equal(x[1], toy.dequant(B["Q"][t1:t1 + 1], B["S"][t1:t1 + 1])[0].astype(np.float32))
+
+
+@pytest.mark.parametrize("n,dim", [(1, 1), (2, 7), (4, 2048), (3, 5632), (1, 17408), (4, 33)])
+def test_rmsnorm_within_one_ulp(n, dim):
+    pti = _pti()
+    g = np.random.default_rng(100 + dim)
+    for scale, eps in ((1.0, EPS), (3e3, 0.0), (1e-4, EPS)):
+        x = (g.standard_normal((n, dim)) * scale).astype(np.float32)
+        y = host(pti.rmsnorm(dev(x), eps))
+        assert within_ulp(y, toy.rmsnorm(x.astype(np.float64), eps))
+    xt = dev(x)
+    pti.rmsnorm(xt, EPS, y=xt)  # in place
+    assert within_ulp(host(xt), toy.rmsnorm(x.astype(np.float64), EPS))
+
+
+@pytest.mark.parametrize("n", [1, 1000, 4 * 5632 + 3])
+def test_silu_mul_within_one_ulp(n):
+    pti = _pti()
+    g = np.random.default_rng(200 + n)
+    gv = (g.standard_normal(n) * 30).astype(np.float32)
+    gv[: min(n, 6)] = np.array([0.0, -0.0, 100.0, -100.0, 1e-30, -700.0], np.float32)[: min(n, 6)]
+    uv = (g.standard_normal(n) * 20).astype(np.float32)
+    y = host(pti.silu_mul(dev(gv), dev(uv)))
+    assert within_ulp(y, toy.silu(gv.astype(np.float64)) * uv.astype(np.float64))
+    gt, ut = dev(gv), dev(uv)
+    pti.silu_mul(gt, ut, y=gt)  # in place over g
+    assert np.array_equal(host(gt), y)
+
+
+def test_add_bit_exact():
+    pti = _pti()
+    g = np.random.default_rng(300)
+    a = (g.standard_normal(10001) * 1e4).astype(np.float32)
+    b = (g.standard_normal(10001) * 1e-3).astype(np.float32)
+    assert np.array_equal(host(pti.add(dev(a), dev(b))), a + b)
+    at = dev(a)
+    pti.add(at, dev(b), y=at)
+    assert np.array_equal(host(at), a + b)
+
+
+# ------------------------------------------------------------------ sampled verify
+
+def _oracle_draws(logits, u, temp):
+    out, amb = [], []
+    for row, uu in zip(logits, u):
+        j, a = toy.sample_inverse_cdf(toy.softmax_t(row.astype(np.float64), temp), float(uu), BAND)
+        out.append(j)
+        amb.append(a)
+    return out, amb
+
+
+def draw_is_valid(weights, u, j):
+    """Index j is a correct draw for u when a rounding of the cumulative sums
+    within BAND can put u * Z inside j's interval: w_j > 0 and
+    S_{j-1} - BAND Z <= u Z <= S_j + BAND Z (in-order sums).  Used where the
+    oracle flags its own draw as on a boundary; zero-weight indices between
+    positive ones make the alternative more than one index away."""
+    w = np.asarray(weights, np.float64)
+    cum = np.cumsum(w)
+    Z = cum[-1]
+    if not (0 <= j < w.size) or w[j] <= 0:
+        return False
+    lo, hi = cum[j] - w[j], cum[j]
+    return lo - BAND * Z <= u * Z <= hi + BAND * Z
+
+
+@pytest.mark.parametrize("vocab", [1, 5, 1000, 32000, 32001])
+@pytest.mark.parametrize("temp", [0.05, 0.7, 5.0])
+def test_sample_verify_matches_oracle_draw(vocab, temp):
+    pti = _pti()
+    g = np.random.default_rng(vocab * 7 + int(temp * 100))
+    for n in (1, 2, 3, 4):
+        for rep in range(6):
+            lg = (g.standard_normal((n, vocab)) * (3.0 if rep % 2 else 20.0)).astype(np.float32)
+            u = g.random(n)
+            if rep == 0:
+                u[0] = 0.0
+            if rep == 1:
+                u[-1] = 1.0 - 2.0 ** -53
+            want, amb = _oracle_draws(lg, u, temp)
+            # guesses that confirm the oracle's draws; every third case the last guess is wrong
+            tin = np.array([7] + want[:-1], np.int32)
+            if rep % 3 == 0 and n >= 2:
+                tin[-1] = (tin[-1] + 1) % vocab
+            tok, acc = pti.sample_verify(dev(lg), dev(tin), dev(u, np.float64), temp)
+            got = host(tok).tolist()
+            for j in range(n):
+                if amb[j]:
+                    w = toy.softmax_t(lg[j].astype(np.float64), temp)
+                    assert draw_is_valid(w, float(u[j]), got[j]), (j, got[j], want[j])
+                else:
+                    assert got[j] == want[j], (n, rep, j, got[j], want[j])
+            assert int(host(acc)[0]) == toy.accept_count(tin.tolist(), got)
+
+
+def test_sample_verify_never_draws_zero_weight():
+    """At a small temperature most weights underflow to 0; only indices whose
+    weight is positive may be drawn, whatever u."""
+    pti = _pti()
+    V = 4096
+    lg = np.full((1, V), -1e4, np.float32)
+    hot = [5, 1030, 1031, 4095]
+    lg[0, hot] = [1.0, 1.0, 0.5, 1.0]
+    for u in (0.0, 0.2, 0.5, 0.7, 0.99, 1.0 - 2.0 ** -53):
+        tok, _ = pti.sample_verify(dev(lg), dev([0], np.int32), dev([u], np.float64), 0.01)
+        got = int(host(tok)[0])
+        want, amb = _oracle_draws(lg, [u], 0.01)
+        w = toy.softmax_t(lg[0].astype(np.float64), 0.01)
+        assert got in hot and (got == want[0] or (amb[0] and draw_is_valid(w, u, got))), (u, got, want)
+
+
+# ------------------------------------------------------------------ forward pass
+
+def _forward_checks(stack, tokens):
+    lg_ops = host(stack.composed_forward(tokens))
+    lg_lib = host(stack.gpu.forward(dev(tokens, np.int32)))
+    assert np.array_equal(lg_lib, lg_ops), "library forward differs from the op-by-op composition"
+    return lg_lib
+
+
+def test_forward_small_q8_ops_and_composition(small_raw):
+    pti = _pti()
+    st = Stack(small_raw, pti.FMT_Q8)
+    for toks in ([0], [1000, 3], [5, 5, 999], [17, 1000, 3, 0]):
+        _forward_checks(st, toks)
+
+
+def test_forward_small_ssq_twins_ops_and_composition(small_raw):
+    pti = _pti()
+    other = synth.toy_weights(98, hidden=96, ffn=160, layers=3, vocab=1001)
+    st = Stack(small_raw, pti.FMT_SSQ, raw_b=other)
+    for toks in ([0, 0], [1000, 3], [42, 42]):
+        _forward_checks(st, toks)
+
+
+def test_forward_full_q8_ops_composition_and_sanity(full_q8, full_oracle):
+    toks = [1, 31999, 12345, 7]
+    lg = _forward_checks(full_q8, toks)
+    want = full_oracle.logits(toks)
+    rel = np.abs(lg - want).max() / want.std()
+    print(f"full-chain logits vs fp64 oracle: max |diff| / std = {rel:.3e}")
+    assert rel < 1e-3  # sanity (observed ~1e-6), not a parity bar
+
+
+def test_forward_full_ssq_self_twin(full_ssq, full_oracle):
+    lg = _forward_checks(full_ssq, [1, 2])
+    want = full_oracle.logits([1, 2])
+    assert np.abs(lg - want).max() / want.std() < 1e-3  # sanity
+
+
+# ------------------------------------------------------------------ decode loop
+
+def replay(passes, first, N, steps):
+    """Run the oracle's loop with the GPU's draws; it must ask for exactly the
+    passes the GPU ran, in order, on the same inputs."""
+    lut = {(int(k), int(s)): (int(i), int(a), int(b)) for k, s, i, a, b in passes}
+
+    def draw(k, s, i, t):
+        st, inp, out = lut[(k, s)]
+        assert st == i and inp == t, (k, s, i, t, st, inp)
+        return out
+
+    committed, accepts, p2 = toy.systolic_decode(draw, first, N, steps)
+    assert [tuple(map(int, p)) for p in passes] == p2
+    return committed, accepts
+
+
+def check_draws(stack, passes, temp=0.0, uniforms=None, N=None):
+    """Every draw equals the oracle's decision on the GPU's logits for that input."""
+    by_twin = {False: {}, True: {}}
+    for k, s, i, inp, out in passes:
+        by_twin[bool(stack.fmt == _pti().FMT_SSQ and i >= 1)].setdefault(int(inp), []).append((int(k), int(s), int(out)))
+    n_amb = 0
+    for twin_b, d in by_twin.items():
+        toks = sorted(d)
+        if not toks:
+            continue
+        L = stack.logits_for(toks, twin_b=twin_b)
+        for row, t in zip(L, toks):
+            for k, s, out in d[t]:
+                if temp == 0.0:
+                    assert out == toy.argmax_first(row), (k, s, t, out)
+                else:
+                    w = toy.softmax_t(row.astype(np.float64), temp)
+                    uu = float(uniforms[k * 2 * N + s])
+                    j, amb = toy.sample_inverse_cdf(w, uu, BAND)
+                    n_amb += amb
+                    assert out == j or (amb and draw_is_valid(w, uu, out)), (k, s, t, out, j)
+    return n_amb
+
+
+def test_decode_greedy_q8_four_streams(full_q8, full_oracle):
+    steps = 64
+    c4, a4, p4 = full_q8.gpu.decode(1, 4, steps)
+    assert a4.tolist() == [4] * steps  # greedy self-speculation confirms every guess
+    c1, a1, _ = full_q8.gpu.decode(1, 1, steps)
+    assert c1.tolist() == c4.tolist() and a1.tolist() == [1] * steps  # the single-stream greedy chain
+    rc, ra = replay(p4, 1, 4, steps)
+    assert rc == c4.tolist() and ra == a4.tolist()
+    check_draws(full_q8, p4)
+    # the chain against the fp64 oracle's own greedy decisions, transition by transition
+    prev = [1] + c4.tolist()[:-1]
+    want = full_oracle.logits(prev)
+    agree = sum(int(np.argmax(w)) == t for w, t in zip(want, c4.tolist()))
+    srt = np.sort(want, axis=1)
+    near_tie = int(np.sum(srt[:, -1] - srt[:, -2] < 1e-3 * want.std()))
+    print(f"greedy chain: {agree}/{steps} transitions equal the fp64 oracle's argmax, {near_tie} near-ties")
+    assert agree + near_tie >= steps
+
+
+def test_decode_greedy_ssq_self_twin(full_ssq):
+    st = full_ssq
+    steps = 32
+    c, a, p = st.gpu.decode(1, 2, steps)
+    assert a.tolist() == [2] * steps
+    rc, ra = replay(p, 1, 2, steps)
+    assert rc == c.tolist()
+    check_draws(st, p)
+
+
+def test_decode_greedy_ssq_distinct_twins_rejects_and_redraws(small_raw):
+    """Twin B's head is twin A's plus noise: B's guesses are sometimes wrong, the
+    loop re-draws, and the committed chain is still twin A's greedy chain."""
+    pti = _pti()
+    g = np.random.default_rng(400)
+    other = {k: v for k, v in small_raw.items()}
+    q = small_raw["head"]["Q"].astype(np.int16) + g.integers(-40, 41, size=small_raw["head"]["Q"].shape)
+    other["head"] = dict(Q=np.clip(q, -127, 127).astype(np.int8), S=small_raw["head"]["S"])
+    st = Stack(small_raw, pti.FMT_SSQ, raw_b=other)
+    steps = 200
+    c, a, p = st.gpu.decode(3, 2, steps)
+    assert 1 in a.tolist() and 2 in a.tolist(), np.bincount(a)
+    rc, ra = replay(p, 3, 2, steps)
+    assert rc == c.tolist() and ra == a.tolist()
+    check_draws(st, p)
+
+
+def test_decode_greedy_small_q8_all_stream_counts(small_raw):
+    pti = _pti()
+    st = Stack(small_raw, pti.FMT_Q8)
+    ref = None
+    for N in (1, 2, 3, 4):
+        c, a, p = st.gpu.decode(0, N, 40)
+        assert a.tolist() == [N] * 40
+        ref = c.tolist() if ref is None else ref
+        assert c.tolist() == ref
+        replay(p, 0, N, 40)
+        check_draws(st, p)
+
+
+def test_decode_sampled_q8_four_streams_statistics():
+    """T = 0.7 on the stack with a flatter head (scales / 4, mean sum p^2 ~ 0.5)."""
+    pti = _pti()
+    raw = synth.toy_weights(synth.SEED_TOY, lm_scale_div=4.0)
+    st = Stack(raw, pti.FMT_Q8)
+    N, steps = 4, 160
+    u = np.random.default_rng(synth.SEED_TOY).random((steps + 1) * 2 * N)
+    c, a, p = st.gpu.decode(1, N, steps, temperature=TEMP, uniforms=u)
+    rc, ra = replay(p, 1, N, steps)
+    assert rc == c.tolist() and ra == a.tolist()
+    n_amb = check_draws(st, p, TEMP, u, N)
+    print(f"sampled run: accept histogram {np.bincount(a, minlength=N + 1)[1:]}, {n_amb} boundary draws")
+    # checks evaluated at each step: i = 1 .. min(a, N-1); check i passes iff i < a
+    inputs = {}
+    for k, s, i, inp, out in p:
+        if k >= 1 and s < N:
+            inputs[(int(k), int(s))] = int(inp)
+    ctx, guess, ind = [], [], []
+    for k in range(1, steps + 1):
+        ak = int(a[k - 1])
+        for i in range(1, min(ak, N - 1) + 1):
+            ctx.append(inputs[(k, i - 1)])
+            guess.append(inputs[(k, i)])
+            ind.append(1.0 if i < ak else 0.0)
+    model = toy.ToyModel(raw, EPS)
+    uniq = sorted(set(ctx))
+    P = {}
+    lg = model.logits(uniq)
+    for t, row in zip(uniq, lg):
+        w = toy.softmax_t(row, TEMP)
+        P[t] = w / w.sum()
+    ind = np.array(ind)
+    coll = np.array([float((P[c] ** 2).sum()) for c in ctx])
+    cond = np.array([float(P[c][gs]) for c, gs in zip(ctx, guess)])
+    z_coll = (ind.sum() - coll.sum()) / math.sqrt((coll * (1 - coll)).sum())
+    z_cond = (ind.sum() - cond.sum()) / math.sqrt(max((cond * (1 - cond)).sum(), 1e-12))
+    print(f"{len(ind)} checks: passed {ind.sum():.0f}, expected sum p^2 {coll.sum():.1f} (z {z_coll:.2f}), "
+          f"expected p(guess) {cond.sum():.1f} (z {z_cond:.2f})")
+    assert abs(z_coll) <= 4 and abs(z_cond) <= 4
+    assert 0.2 < coll.mean() < 0.95  # the statistics are informative

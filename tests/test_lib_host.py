@@ -173,3 +173,100 @@ def test_no_device_reports_hip_error():
     assert L.pti_last_hip_error() != 0
     with pytest.raises(pti.PtiError):
         pti._check("pti_gemv_q8_multi", st)
+
+
+def test_sample_verify_errors():
+    L = pti.lib()
+    f = L.pti_sample_verify
+    ok = (_fake(A0), _fake(A1), _fake(A2), 0.7, _fake(A3), _fake(A4), 100, 2, None)
+
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return f(*a)
+
+    assert call(a2=None) == NULL
+    assert call(a3=0.0) == SHAPE and call(a3=-1.0) == SHAPE and call(a3=float("inf")) == SHAPE
+    assert call(a3=float("nan")) == SHAPE
+    assert call(a6=0) == SHAPE
+    assert call(a7=0) == NSTREAMS and call(a7=5) == NSTREAMS
+    assert call(a2=_fake(A2 + 4)) == ALIGN
+    assert call(a4=_fake(A2 + 8)) == OVERLAP  # tokens_out inside uniforms [A2, A2+16)
+    assert call(a5=_fake(A3 + 4)) == OVERLAP  # accept_out inside tokens_out
+
+
+def test_glue_errors():
+    L = pti.lib()
+    assert L.pti_embed_q8(None, _fake(A1), _fake(A2), 100, 64, 1, None) == NULL
+    assert L.pti_embed_q8(_fake(A0), _fake(A1), _fake(A2), 100, 48, 1, None) == SHAPE
+    assert L.pti_embed_q8(_fake(A0), _fake(A1), _fake(A2), 0, 64, 1, None) == SHAPE
+    assert L.pti_embed_q8(_fake(A0), _fake(A1), _fake(A2), 100, 64, 5, None) == NSTREAMS
+    assert L.pti_embed_q8(_fake(A0), _fake(A1 + 1), _fake(A2), 100, 64, 1, None) == ALIGN
+    assert L.pti_embed_q8(_fake(A0), _fake(A1), _fake(A0 + 68), 100, 64, 1, None) == OVERLAP
+    assert L.pti_embed_ssq(_fake(A0), _fake(A1), _fake(A1 + 4), 100, 64, None) == OVERLAP
+    assert L.pti_embed_ssq(_fake(A0), None, _fake(A2), 100, 64, None) == NULL
+    assert L.pti_rmsnorm(_fake(A0), _fake(A1), 0, 1, 1e-6, None) == SHAPE
+    assert L.pti_rmsnorm(_fake(A0), _fake(A1), 64, 1, -1.0, None) == SHAPE
+    assert L.pti_rmsnorm(_fake(A0), _fake(A1), 64, 1, float("nan"), None) == SHAPE
+    assert L.pti_rmsnorm(_fake(A0), _fake(A1), 64, 0, 1e-6, None) == NSTREAMS
+    assert L.pti_rmsnorm(_fake(A0), _fake(A0 + 4), 64, 1, 1e-6, None) == OVERLAP  # shifted in-place
+    assert L.pti_silu_mul(_fake(A0), _fake(A1), _fake(A0 + 4), 64, None) == OVERLAP
+    assert L.pti_silu_mul(_fake(A0), _fake(A1), _fake(A2), 0, None) == SHAPE
+    assert L.pti_silu_mul(_fake(A0), _fake(A1 + 2), _fake(A2), 64, None) == ALIGN
+    assert L.pti_add(_fake(A0), _fake(A1), _fake(A1 + 8), 64, None) == OVERLAP
+    assert L.pti_add(None, _fake(A1), _fake(A2), 64, None) == NULL
+
+
+def _toy(fmt=pti.FMT_Q8, layers=2, hidden=64, ffn=96, vocab=100, eps=1e-6, ptr=A0):
+    Arr = ctypes.c_void_p * max(layers, 1)
+    g = Arr(*([ptr] * max(layers, 1)))
+    vp = ctypes.POINTER(ctypes.c_void_p)
+    m = pti.ToyModelC(fmt, layers, hidden, ffn, vocab, eps, ptr, ptr, ctypes.cast(g, vp), ctypes.cast(g, vp),
+                      ctypes.cast(g, vp))
+    m._keep = g
+    return m
+
+
+def test_toy_errors():
+    L = pti.lib()
+    ws = L.pti_toy_workspace_bytes
+    m = _toy()
+    n = ws(ctypes.byref(m), 4)
+    # h, r, d: 4*64*4 = 1024 each; g, u: 4*96*4 = 1536 each; logits 1600 (-> 1792); four small regions
+    assert n == 3 * 1024 + 2 * 1536 + 1792 + 4 * 256
+    assert ws(ctypes.byref(m), 0) == 0 and ws(ctypes.byref(m), 5) == 0
+    assert ws(ctypes.byref(_toy(fmt=pti.FMT_SSQ)), 4) == 0 and ws(ctypes.byref(_toy(fmt=pti.FMT_SSQ)), 2) > 0
+    for bad in (_toy(fmt=2), _toy(layers=0), _toy(layers=65), _toy(hidden=48), _toy(ffn=0), _toy(vocab=0),
+                _toy(eps=-1.0), _toy(eps=float("inf"))):
+        assert ws(ctypes.byref(bad), 1) == 0
+    assert ws(ctypes.byref(_toy(ptr=A0 + 2)), 1) == 0  # misaligned weights
+    fwd = L.pti_toy_forward
+    assert fwd(None, _fake(A1), _fake(A2), _fake(A3), n, 4, None) == NULL
+    assert fwd(ctypes.byref(_toy(ptr=A0 + 2)), _fake(A1), _fake(A2), _fake(A3), n, 4, None) == ALIGN
+    assert fwd(ctypes.byref(m), _fake(A1), _fake(A2), _fake(A3), n - 1, 4, None) == SHAPE
+    assert fwd(ctypes.byref(m), _fake(A1), _fake(A2), _fake(A3 + 16), n, 4, None) == ALIGN
+    assert fwd(ctypes.byref(m), _fake(A1), _fake(A3 + 512), _fake(A3), n, 4, None) == OVERLAP
+    assert fwd(ctypes.byref(m), _fake(A1), _fake(A2), _fake(A3), n, 5, None) == NSTREAMS
+    dec = L.pti_toy_decode
+    buf = np.zeros(64, np.int32)
+    hp = buf.ctypes.data_as(ctypes.c_void_p)
+    u = np.zeros(64, np.float64).ctypes.data_as(ctypes.c_void_p)
+    npass = ctypes.c_int64(-1)
+    args = [ctypes.byref(m), 3, 4, 5, 0.0, None, _fake(A3), n, hp, hp, None, ctypes.byref(npass), None]
+
+    def d(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return dec(*a)
+
+    assert d(a1=-1) == SHAPE and d(a1=100) == SHAPE
+    assert d(a3=-1) == SHAPE
+    assert d(a4=-0.5) == SHAPE and d(a4=float("nan")) == SHAPE
+    assert d(a4=0.7) == NULL  # sampling needs uniforms
+    assert d(a8=None) == NULL
+    assert d(a7=n - 1) == SHAPE
+    assert d(a6=_fake(A3 + 8)) == ALIGN
+    assert d(a2=3, a0=ctypes.byref(_toy(fmt=pti.FMT_SSQ))) == NSTREAMS
+    assert npass.value == -1  # nothing ran
