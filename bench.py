@@ -177,7 +177,7 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, out_dir):
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         acc = per_kernel(d, counter)
-        gname, g_kib, g_n = pick(acc, lambda k: "gemv_kernel" in k)
+        gname, g_kib, g_n = pick(acc, lambda k: "gemv" in k)  # the PMC runs launch only the SSQ GEMV
         cname, c_kib, c_n = pick(acc, lambda k: "neg_kernel" in k or "neg" in k.lower())
         factor = CALIB_BYTES / 1024.0 / c_kib
         out[counter] = dict(gname=gname, g_kib=g_kib, g_n=g_n, cname=cname, c_kib=c_kib, c_n=c_n, factor=factor,

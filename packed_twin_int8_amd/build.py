@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["pti_host.cpp", "pti_gemv.hip", "pti_verify.hip", "pti_glue.hip", "pti_toy.cpp"]
 ARCH = os.environ.get("PTI_OFFLOAD_ARCH", "gfx950")
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall"]
+COMMON = ["-O3", "-std=c++20", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-munsafe-fp-atomics"]
 

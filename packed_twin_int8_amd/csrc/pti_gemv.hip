@@ -49,6 +49,8 @@
 //     stream's output is bitwise independent of those.
 #include <hip/hip_runtime.h>
 
+#include <utility>
+
 #include "pti_internal.h"
 
 #ifndef PTI_RMAX_SSQ
@@ -457,23 +459,50 @@ struct Wave {
             issue(bufs[k]);
     }
 
-    // The exit leaves both loops directly: a path from an early exit back to
-    // the loop head would make the compiler's count of loads in flight at the
-    // head pessimistic, and every step would then wait for all of them.
+    // One step: issue the loads kD steps ahead, then compute this one.
+    template <int K>
+    __device__ __forceinline__ void step()
+    {
+        issue(bufs[(K + kD) % (kD + 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(bufs[K]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // PAD: run the step count rounded up to a multiple of kD + 1, so the loop
+    // has one exit, at its end.  An exit inside the unrolled body gives the
+    // compiler a path back to the loop head on which fewer loads are in
+    // flight, and it then makes the head's step wait for nearly all of them
+    // (draining the prefetch once per iteration).  The extra steps load
+    // through empty buffer resources (zero weights and scales), so they add
+    // exact zeros to the accumulators, and any row they complete lies past the
+    // segment's passes, in a lane that is never stored.
+    // !PAD: stop after exactly nsteps steps (short segments between barriers,
+    // where padding would cost more than the waits).
+    template <bool PAD>
     __device__ __forceinline__ void loop()
     {
-        for (int s = 0;; s += kD + 1) {
-#pragma unroll
-            for (int k = 0; k <= kD; k++) {
-                if (s + k >= nsteps)
-                    goto done;
-                issue(bufs[(k + kD) % (kD + 1)]);
-                __builtin_amdgcn_sched_barrier(0);
-                compute(bufs[k]);
-                __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PAD) {
+            const int iters = (nsteps + kD) / (kD + 1);
+            for (int it = 0; it < iters; it++) {
+                [&]<int... K>(std::integer_sequence<int, K...>) {
+                    (step<K>(), ...);
+                }(std::make_integer_sequence<int, kD + 1>{});
             }
+        } else {
+            for (int s = 0;; s += kD + 1) {
+#pragma unroll
+                for (int k = 0; k <= kD; k++) {
+                    if (s + k >= nsteps)
+                        goto done;
+                    issue(bufs[(k + kD) % (kD + 1)]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute(bufs[k]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        done:;
         }
-    done:;
     }
 
     // Passes per output group: a group's rows fit one lane each of outv.
@@ -539,14 +568,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a)
         stage_store<UC, NSP, BATCH>(xs, 0, v, tid, nitems);
         __syncthreads();
         w.begin_group(0);
-        w.loop();
+        w.template loop<true>();
         w.store_group(min(w.npass, w.kGroupPasses));
         // waves with more rows than one output group holds
         for (int g0 = w.kGroupPasses; g0 < w.npass; g0 += w.kGroupPasses) {
             const int g1 = min(w.npass, g0 + w.kGroupPasses);
             w.begin_group(g0);
             w.begin(g0, g1, 0, a.rounds);
-            w.loop();
+            w.template loop<true>();
             w.store_group(g1);
         }
     } else {
@@ -564,7 +593,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a)
                     if (i0 == 0)
                         w.begin_group(p);
                     w.begin(p, p + 1, i0, i1);
-                    w.loop();
+                    w.template loop<false>();
                     if (i1 == a.rounds)
                         w.store_group(p + 1);
                 }
@@ -634,6 +663,254 @@ GemvArgs make_args(const void *w, int64_t rows, int64_t cols)
     return a;
 }
 
+// ---------------------------------------------------------------------------
+// Row-split kernel: the workgroup's waves share each row.
+//
+// HBM delivers the most when, at any moment, the requests in flight cover one
+// compact, contiguous window of memory that slides forward (as a grid-stride
+// read does), and when that window is small.  With every wave owning whole
+// rows, the window is several thousand rows wide with one round in flight per
+// row.  Here workgroup g owns rows g, g + G, g + 2G, ... (G workgroups, one
+// per CU) and covers P of them per step: the Q waves of a row each load one of
+// its Q rounds.  At any moment the GPU reads a band of about G * P * (D + 1)
+// consecutive rows, each one whole.
+//
+// A wave always handles the same round of its rows, so the 64 x unit-columns
+// of x it needs are the same for every row: it loads them once into
+// registers (no LDS staging, no LDS reads in the loop).  Per step it reduces
+// its round's partial dot product over its 64 lanes (the same fixed DPP tree)
+// and parks it in LDS; every S steps the workgroup sums the Q partials of
+// each finished row in round order and stores the row.  Each output's order of
+// operations depends only on (rows, cols) and the format, so a stream's
+// result is bitwise independent of the stream count and of its slot.
+//
+// Used when a row has at most 16 rounds and, for Q8, an even number of blocks
+// (every row then starts on a dword boundary).
+constexpr int kSplitMaxWaves = 16;
+#ifndef PTI_SPLIT_PREFETCH
+#define PTI_SPLIT_PREFETCH 1
+#endif
+constexpr int kSD = PTI_SPLIT_PREFETCH;  // steps of loads in flight ahead of the compute
+#ifndef PTI_SPLIT_T_SSQ
+#define PTI_SPLIT_T_SSQ 5  // rounds per wave per step (SSQ)
+#endif
+#ifndef PTI_SPLIT_T_Q8_1
+#define PTI_SPLIT_T_Q8_1 1  // rounds per wave per step (Q8, one stream)
+#endif
+#ifndef PTI_SPLIT_Q8_MAXN
+#define PTI_SPLIT_Q8_MAXN 0  // Q8 uses the row-split kernel for n_streams up to this (all or none, so results do not depend on n_streams)
+#endif
+
+struct SplitArgs {
+    GemvArgs g;
+    int32_t P, Q;   // rows per step, waves (= rounds) per row
+    int32_t S;      // steps per flush of finished rows
+};
+
+// Waves per workgroup at T rounds per wave: up to 16, or 8 when the x slice
+// of T rounds needs more than the 128 registers a 16-wave workgroup allows.
+#ifndef PTI_SPLIT_WAVES_BIG_T
+#define PTI_SPLIT_WAVES_BIG_T 8
+#endif
+constexpr int split_max_waves(int T) { return T >= 3 ? PTI_SPLIT_WAVES_BIG_T : kSplitMaxWaves; }
+
+template <int FMT, int NS, int T>
+__global__ __launch_bounds__(64 * split_max_waves(T)) void gemv_split_kernel(SplitArgs sa)
+{
+    constexpr int UC = unit_cols<FMT>();
+    const GemvArgs &a = sa.g;
+    const int P = sa.P, Q = sa.Q, S = sa.S;
+    extern __shared__ float part[];  // [2][S * P][Q][NS]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int p = wv / Q, q = wv - (wv / Q) * Q;
+    const int64_t G = gridDim.x, g = blockIdx.x;
+    const int64_t wg_rows = g < a.rows ? (a.rows - g + G - 1) / G : 0;
+    const int steps = (int)((wg_rows + P - 1) / P);
+
+    // x of this lane's units in rounds q T .. q T + T - 1 (zero past the row's
+    // last unit), all streams
+    float xv[T][UC][NS];
+#pragma unroll
+    for (int tt = 0; tt < T; tt++) {
+        const int unit = (q * T + tt) * 64 + lane;
+#pragma unroll
+        for (int s = 0; s < NS; s++)
+#pragma unroll
+            for (int k = 0; k < UC / 4; k++) {
+                float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (unit < a.units)
+                    t = *reinterpret_cast<const float4 *>(a.x[s] + unit * UC + 4 * k);
+                xv[tt][4 * k][s] = t.x, xv[tt][4 * k + 1][s] = t.y, xv[tt][4 * k + 2][s] = t.z,
+                              xv[tt][4 * k + 3][s] = t.w;
+            }
+    }
+
+    const LaneOffsets lo = lane_offsets(lane);
+    const int soff = q * T * (int)kRoundBytes;
+    const int64_t row_step = (int64_t)P * G * a.row_bytes;  // bytes from a wave's row to its next
+    const uint8_t *row0 = a.w + (g + (int64_t)p * G) * a.row_bytes;
+
+    // Loads of step t into buf (an empty resource past the workgroup's rows).
+    auto issue = [&](int t, Unit (&ut)[T]) {
+        const int64_t m = (int64_t)t * P + p;  // row slot within the workgroup
+        const int n = m < wg_rows ? (int)a.row_bytes : 0;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(m < wg_rows ? row0 + t * row_step : a.w), (short)0, n, 0x00020000);
+#pragma unroll
+        for (int tt = 0; tt < T; tt++) {
+            Unit &u = ut[tt];
+            const int so = soff + tt * (int)kRoundBytes;
+            if constexpr (FMT == kSSQ) {
+                u.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.ssq_sc, so, 0);
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lo.ssq_d, so, 0);
+                u.d[0] = v.x, u.d[1] = v.y, u.d[2] = v.z, u.d[3] = v.w;
+            } else {
+                u.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.q_sc[0], so, 0);
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lo.q_d[0], so, 0);
+                u.d[0] = v.x, u.d[1] = v.y, u.d[2] = v.z, u.d[3] = v.w;
+                u.d[4] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.q_h[0], so, 0);
+            }
+        }
+    };
+
+    // The round's partial dot product of step t, reduced over the lanes and
+    // parked in LDS, in half `half` of the double buffer at step `local` of
+    // the window (steps past the workgroup's last write nothing).
+    auto compute = [&](int t, int half, int local, const Unit (&ut)[T]) {
+        float acc[NS];
+#pragma unroll
+        for (int tt = 0; tt < T; tt++) {
+        const Unit &u = ut[tt];
+        float bs[NS];
+        if constexpr (FMT == kQ8) {
+            uint32_t qd[4];
+#pragma unroll
+            for (int k = 0; k < 4; k++)
+                qd[k] = __builtin_amdgcn_alignbyte(u.d[k + 1], u.d[k], lo.q_sh[0]);
+#pragma unroll
+            for (int c = 0; c < UC; c++) {
+                const float wq = sbyte(qd[c >> 2], c & 3);
+#pragma unroll
+                for (int s = 0; s < NS; s++)
+                    bs[s] = c == 0 ? wq * xv[tt][c][s] : __builtin_fmaf(wq, xv[tt][c][s], bs[s]);
+            }
+            const float d = f16_lo(u.sc >> lo.q_ssh[0]);
+#pragma unroll
+            for (int s = 0; s < NS; s++)
+                acc[s] = tt == 0 ? d * bs[s] : __builtin_fmaf(d, bs[s], acc[s]);
+        } else {
+            // slot c: dword c/2, halfword c%2; twin A = high byte, twin B = low byte
+#pragma unroll
+            for (int c = 0; c < UC; c++) {
+                const uint32_t dw = u.d[c >> 1];
+#pragma unroll
+                for (int s = 0; s < NS; s++) {
+                    const float wq = sbyte(dw, 2 * (c & 1) + (s == 0 ? 1 : 0));
+                    bs[s] = c == 0 ? wq * xv[tt][c][s] : __builtin_fmaf(wq, xv[tt][c][s], bs[s]);
+                }
+            }
+            const float da = f16_lo(u.sc), db = f16_hi(u.sc);
+            acc[0] = tt == 0 ? da * bs[0] : __builtin_fmaf(da, bs[0], acc[0]);
+            acc[1] = tt == 0 ? db * bs[1] : __builtin_fmaf(db, bs[1], acc[1]);
+        }
+        }
+        const int slot = (half * S + local) * P + p;  // row slot in the double buffer
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+            const float v = wave_sum(acc[s]);
+            if (lane == 63 && t < steps)
+                part[(slot * Q + q) * NS + s] = v;
+        }
+    };
+
+    // Sum the partials of the rows of steps [t0, t1) (in half `half`) in round
+    // order and store them.
+    auto flush = [&](int t0, int t1, int half) {
+        __syncthreads();
+        const int n = (t1 - t0) * P;
+        // streams outermost with a compile-time index: a lane-varying index
+        // into the argument array would load the output pointer from memory,
+        // and that wait would also drain the weight loads in flight
+#pragma unroll
+        for (int s = 0; s < NS; s++)
+            for (int r = tid; r < n; r += 64 * P * Q) {  // r: row slot relative to step t0
+                const int64_t m = (int64_t)t0 * P + r;
+                if (m >= wg_rows)
+                    continue;
+                const int slot = half * S * P + r;
+                float acc = part[(slot * Q) * NS + s];
+                for (int j = 1; j < Q; j++)
+                    acc += part[((slot * Q) + j) * NS + s];
+                a.y[s][g + m * G] = acc;
+            }
+    };
+
+    Unit bufs[kSD + 1][T];
+#pragma unroll
+    for (int k = 0; k < kSD; k++)
+        issue(k, bufs[k]);
+    // Windows of S steps (S a multiple of kSD + 1, so step t always uses
+    // buffer t mod (kSD + 1)); the last window is rounded up to a multiple of
+    // kSD + 1 so the loop has a single exit: its extra steps fall past the
+    // workgroup's rows, load through empty resources and write nothing.
+    int half = 0;
+    for (int t0 = 0; t0 < steps; t0 += S, half ^= 1) {
+        const int t1 = t0 + S < steps ? t0 + S : steps;
+        const int iters = (t1 - t0 + kSD) / (kSD + 1);
+        for (int it = 0; it < iters; it++) {
+            const int local = it * (kSD + 1);
+            const int tb = t0 + local;
+            [&]<int... K>(std::integer_sequence<int, K...>) {
+                ((issue(tb + K + kSD, bufs[(K + kSD) % (kSD + 1)]), __builtin_amdgcn_sched_barrier(0),
+                  compute(tb + K, half, local + K, bufs[K]), __builtin_amdgcn_sched_barrier(0)),
+                 ...);
+            }(std::make_integer_sequence<int, kSD + 1>{});
+        }
+        flush(t0, t1, half);
+    }
+}
+
+// Split geometry for a row of `rounds` rounds, or false if the row-split
+// kernel does not apply.
+bool split_shape(int rounds, int ns, int T, SplitArgs &sa)
+{
+    const int Q = (rounds + T - 1) / T, W = split_max_waves(T);
+    if (rounds < 1 || Q > W)
+        return false;
+    sa.Q = Q;
+    sa.P = W / Q;
+    // flush every S steps, S a multiple of kSD + 1: the double buffer holds
+    // 2 S P Q NS floats, at most 32 KB
+    int S = 64 - 64 % (kSD + 1);
+    while (S > kSD + 1 && 2 * S * sa.P * sa.Q * ns * 4 > 32 * 1024)
+        S -= kSD + 1;
+    sa.S = S;
+    return true;
+}
+
+template <int FMT, int NS, int T>
+int launch_split(const GemvArgs &a, const SplitArgs &sa0, hipStream_t stream)
+{
+    SplitArgs sa = sa0;
+    sa.g = a;
+    const int cus = device_cus();
+    if (cus <= 0) {
+        pti::set_hip_error(hipGetLastError());
+        return PTI_ERR_HIP;
+    }
+    const int64_t grid = std::min<int64_t>(cus, a.rows);
+    const size_t lds = (size_t)2 * sa.S * sa.P * sa.Q * NS * sizeof(float);
+    hipLaunchKernelGGL((gemv_split_kernel<FMT, NS, T>), dim3((unsigned)grid), dim3((unsigned)(64 * sa.P * sa.Q)), lds,
+                       stream, sa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        pti::set_hip_error(e);
+        return PTI_ERR_HIP;
+    }
+    return PTI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -657,6 +934,9 @@ int pti_gemv_ssq(const void *w_ssq, const float *x_a, const float *x_b, float *y
     GemvArgs a = make_args<kSSQ>(w_ssq, rows, cols);
     a.x[0] = x_a, a.x[1] = x_b;
     a.y[0] = y_a, a.y[1] = y_b;
+    SplitArgs sa;
+    if (split_shape(a.rounds, 2, PTI_SPLIT_T_SSQ, sa))
+        return launch_split<kSSQ, 2, PTI_SPLIT_T_SSQ>(a, sa, static_cast<hipStream_t>(stream));
     return launch<kSSQ, 2, 2, true>(a, static_cast<hipStream_t>(stream));
 }
 
@@ -682,6 +962,18 @@ int pti_gemv_q8_multi(const void *w_q8, const float *x, float *y, int64_t rows, 
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     // rows start on dword boundaries when a row holds an even number of blocks
+    SplitArgs sa;
+    if ((cols / PTI_BLOCK) % 2 == 0 && n_streams <= PTI_SPLIT_Q8_MAXN) {
+        const int T = n_streams == 1 ? PTI_SPLIT_T_Q8_1 : 1;
+        if (split_shape(a.rounds, n_streams, T, sa)) {
+            switch (n_streams) {
+            case 1: return launch_split<kQ8, 1, PTI_SPLIT_T_Q8_1>(a, sa, st);
+            case 2: return launch_split<kQ8, 2, 1>(a, sa, st);
+            case 3: return launch_split<kQ8, 3, 1>(a, sa, st);
+            default: return launch_split<kQ8, 4, 1>(a, sa, st);
+            }
+        }
+    }
     if ((cols / PTI_BLOCK) % 2 == 0) {
         switch (n_streams) {
         case 1: return launch<kQ8, 1, 1, true>(a, st);
