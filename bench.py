@@ -314,7 +314,7 @@ def main():
         "frac_of_hbm_peak": round(w_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemv_kernel<SSQ> (pti_gemv_ssq)",
+            "kernel": "gemv_split_kernel<SSQ> (pti_gemv_ssq)",
             "achieved": round(gemv_algo_bytes / (ms_gemv * 1e-3) / 1e9, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

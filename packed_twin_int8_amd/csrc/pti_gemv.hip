@@ -691,6 +691,10 @@ constexpr int kSplitMaxWaves = 16;
 #define PTI_SPLIT_PREFETCH 1
 #endif
 constexpr int kSD = PTI_SPLIT_PREFETCH;  // steps of loads in flight ahead of the compute
+#ifndef PTI_SPLIT_ROUND_PIPE
+#define PTI_SPLIT_ROUND_PIPE 1
+#endif
+constexpr bool kSplitRoundPipe = PTI_SPLIT_ROUND_PIPE && kSD == 1;  // issue the next step round by round
 #ifndef PTI_SPLIT_T_SSQ
 #define PTI_SPLIT_T_SSQ 5  // rounds per wave per step (SSQ)
 #endif
@@ -709,8 +713,11 @@ struct SplitArgs {
 
 // Waves per workgroup at T rounds per wave: up to 16, or 8 when the x slice
 // of T rounds needs more than the 128 registers a 16-wave workgroup allows.
+#ifndef PTI_SPLIT_WG_PER_CU
+#define PTI_SPLIT_WG_PER_CU 1
+#endif
 #ifndef PTI_SPLIT_WAVES_BIG_T
-#define PTI_SPLIT_WAVES_BIG_T 8
+#define PTI_SPLIT_WAVES_BIG_T 4
 #endif
 constexpr int split_max_waves(int T) { return T >= 3 ? PTI_SPLIT_WAVES_BIG_T : kSplitMaxWaves; }
 
@@ -751,33 +758,39 @@ __global__ __launch_bounds__(64 * split_max_waves(T)) void gemv_split_kernel(Spl
     const int64_t row_step = (int64_t)P * G * a.row_bytes;  // bytes from a wave's row to its next
     const uint8_t *row0 = a.w + (g + (int64_t)p * G) * a.row_bytes;
 
-    // Loads of step t into buf (an empty resource past the workgroup's rows).
-    auto issue = [&](int t, Unit (&ut)[T]) {
+    // Buffer resource over the row of step t (empty past the workgroup's rows).
+    auto rsrc_for = [&](int t) {
         const int64_t m = (int64_t)t * P + p;  // row slot within the workgroup
         const int n = m < wg_rows ? (int)a.row_bytes : 0;
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t *>(m < wg_rows ? row0 + t * row_step : a.w), (short)0, n, 0x00020000);
-#pragma unroll
-        for (int tt = 0; tt < T; tt++) {
-            Unit &u = ut[tt];
-            const int so = soff + tt * (int)kRoundBytes;
-            if constexpr (FMT == kSSQ) {
-                u.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.ssq_sc, so, 0);
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lo.ssq_d, so, 0);
-                u.d[0] = v.x, u.d[1] = v.y, u.d[2] = v.z, u.d[3] = v.w;
-            } else {
-                u.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.q_sc[0], so, 0);
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lo.q_d[0], so, 0);
-                u.d[0] = v.x, u.d[1] = v.y, u.d[2] = v.z, u.d[3] = v.w;
-                u.d[4] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.q_h[0], so, 0);
-            }
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(m < wg_rows ? row0 + t * row_step : a.w),
+                                                 (short)0, n, 0x00020000);
+    };
+    // Loads of round tt of this wave's slice.
+    auto load_round = [&](__amdgpu_buffer_rsrc_t rs, int tt, Unit &u) {
+        const int so = soff + tt * (int)kRoundBytes;
+        if constexpr (FMT == kSSQ) {
+            u.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.ssq_sc, so, 0);
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lo.ssq_d, so, 0);
+            u.d[0] = v.x, u.d[1] = v.y, u.d[2] = v.z, u.d[3] = v.w;
+        } else {
+            u.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.q_sc[0], so, 0);
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lo.q_d[0], so, 0);
+            u.d[0] = v.x, u.d[1] = v.y, u.d[2] = v.z, u.d[3] = v.w;
+            u.d[4] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.q_h[0], so, 0);
         }
+    };
+    // Loads of step t into ut.
+    auto issue = [&](int t, Unit (&ut)[T]) {
+        const __amdgpu_buffer_rsrc_t rs = rsrc_for(t);
+#pragma unroll
+        for (int tt = 0; tt < T; tt++)
+            load_round(rs, tt, ut[tt]);
     };
 
     // The round's partial dot product of step t, reduced over the lanes and
     // parked in LDS, in half `half` of the double buffer at step `local` of
     // the window (steps past the workgroup's last write nothing).
-    auto compute = [&](int t, int half, int local, const Unit (&ut)[T]) {
+    auto compute = [&](int t, int half, int local, const Unit (&ut)[T], auto &&after_round) {
         float acc[NS];
 #pragma unroll
         for (int tt = 0; tt < T; tt++) {
@@ -814,6 +827,9 @@ __global__ __launch_bounds__(64 * split_max_waves(T)) void gemv_split_kernel(Spl
             acc[0] = tt == 0 ? da * bs[0] : __builtin_fmaf(da, bs[0], acc[0]);
             acc[1] = tt == 0 ? db * bs[1] : __builtin_fmaf(db, bs[1], acc[1]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        after_round(tt);
+        __builtin_amdgcn_sched_barrier(0);
         }
         const int slot = (half * S + local) * P + p;  // row slot in the double buffer
 #pragma unroll
@@ -844,12 +860,19 @@ __global__ __launch_bounds__(64 * split_max_waves(T)) void gemv_split_kernel(Spl
                     acc += part[((slot * Q) + j) * NS + s];
                 a.y[s][g + m * G] = acc;
             }
+        // Stores count on the same counter as the weight loads.  Without this
+        // wait the compiler cannot tell how many operations follow the
+        // prefetched loads when the loop is re-entered, and it would make the
+        // first step of every iteration wait for all of them; with it, the
+        // count is known (one drain per flush).
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
     };
 
     Unit bufs[kSD + 1][T];
 #pragma unroll
     for (int k = 0; k < kSD; k++)
         issue(k, bufs[k]);
+    const auto nothing = [](int) {};
     // Windows of S steps (S a multiple of kSD + 1, so step t always uses
     // buffer t mod (kSD + 1)); the last window is rounded up to a multiple of
     // kSD + 1 so the loop has a single exit: its extra steps fall past the
@@ -861,11 +884,26 @@ __global__ __launch_bounds__(64 * split_max_waves(T)) void gemv_split_kernel(Spl
         for (int it = 0; it < iters; it++) {
             const int local = it * (kSD + 1);
             const int tb = t0 + local;
-            [&]<int... K>(std::integer_sequence<int, K...>) {
-                ((issue(tb + K + kSD, bufs[(K + kSD) % (kSD + 1)]), __builtin_amdgcn_sched_barrier(0),
-                  compute(tb + K, half, local + K, bufs[K]), __builtin_amdgcn_sched_barrier(0)),
-                 ...);
-            }(std::make_integer_sequence<int, kSD + 1>{});
+            if constexpr (kSplitRoundPipe) {
+                // one step ahead, round by round: after computing round tt of
+                // step t, load round tt of step t + 1 into the buffer it freed,
+                // so T rounds per wave are in flight at all times
+                [&]<int... K>(std::integer_sequence<int, K...>) {
+                    ((
+                         [&] {
+                             const __amdgpu_buffer_rsrc_t rs = rsrc_for(tb + K + 1);
+                             compute(tb + K, half, local + K, bufs[K],
+                                     [&](int tt) { load_round(rs, tt, bufs[(K + 1) % 2][tt]); });
+                         }()),
+                     ...);
+                }(std::make_integer_sequence<int, 2>{});
+            } else {
+                [&]<int... K>(std::integer_sequence<int, K...>) {
+                    ((issue(tb + K + kSD, bufs[(K + kSD) % (kSD + 1)]), __builtin_amdgcn_sched_barrier(0),
+                      compute(tb + K, half, local + K, bufs[K], nothing), __builtin_amdgcn_sched_barrier(0)),
+                     ...);
+                }(std::make_integer_sequence<int, kSD + 1>{});
+            }
         }
         flush(t0, t1, half);
     }
@@ -899,7 +937,7 @@ int launch_split(const GemvArgs &a, const SplitArgs &sa0, hipStream_t stream)
         pti::set_hip_error(hipGetLastError());
         return PTI_ERR_HIP;
     }
-    const int64_t grid = std::min<int64_t>(cus, a.rows);
+    const int64_t grid = std::min<int64_t>((int64_t)cus * PTI_SPLIT_WG_PER_CU, a.rows);
     const size_t lds = (size_t)2 * sa.S * sa.P * sa.Q * NS * sizeof(float);
     hipLaunchKernelGGL((gemv_split_kernel<FMT, NS, T>), dim3((unsigned)grid), dim3((unsigned)(64 * sa.P * sa.Q)), lds,
                        stream, sa);
