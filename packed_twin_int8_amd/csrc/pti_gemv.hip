@@ -1,5 +1,10 @@
 // Packed-weight decode GEMVs for gfx950: the SSQ twin GEMV and the Q8
-// multi-stream GEMV, one kernel family.
+// multi-stream GEMV.
+//
+// Two kernels.  The per-wave-row kernel below (gemv_kernel) serves Q8 at every
+// stream count and SSQ rows of more than 40 rounds; the row-split kernel
+// further down (gemv_ssq_split_kernel) serves the other SSQ shapes.  Each
+// format's choice depends on the shape alone, never on n_streams.
 //
 // What is computed [README = "打包双子推理（PTI）", section "与 SSQ（Side-by-Side
 // Quantization）的关系" (relation to SSQ); section "带宽分析：为什么会有开销"
@@ -7,7 +12,8 @@
 // slot feeds twin A (high byte) and twin B (low byte); one Q8 block feeds up to
 // four activation vectors.  Output y[s][r] = sum_c scale(r, c/32) * q[r][c] * x[s][c].
 //
-// Mapping onto CDNA4 (gfx950: 256 CUs of 4 SIMDs, wave64, 160 KB LDS per CU):
+// Per-wave-row kernel, mapped onto CDNA4 (gfx950: 256 CUs of 4 SIMDs, wave64,
+// 160 KB LDS per CU):
 //   * One workgroup per CU with a multiple of four wave64s.  Rows are dealt
 //     round-robin to the SIMDs, so every SIMD gets the same number of rows (to
 //     within one) whatever the row count -- no second dispatch wave, no SIMD
@@ -49,6 +55,7 @@
 //     stream's output is bitwise independent of those.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <utility>
 
 #include "pti_internal.h"
@@ -139,6 +146,10 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane)
     }
     return o;
 }
+
+// Entry c (0 or 1) of a two-entry offset table, by select: indexing the
+// table with a runtime value would move it to scratch memory.
+__device__ __forceinline__ uint32_t pick(const uint32_t (&t)[2], int c) { return c ? t[1] : t[0]; }
 
 __device__ __forceinline__ float sbyte(uint32_t d, int k) { return (float)(int8_t)(d >> (8 * k)); }
 
@@ -332,14 +343,14 @@ struct Wave {
                 buf[r].d[0] = v.x, buf[r].d[1] = v.y, buf[r].d[2] = v.z, buf[r].d[3] = v.w;
             } else {
                 const int c = icls[r];
-                buf[r].sc = __builtin_amdgcn_raw_buffer_load_b32(irs[r], (int)lo.q_sc[c], soff, 0);
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(irs[r], (int)lo.q_d[c], soff, 0);
+                buf[r].sc = __builtin_amdgcn_raw_buffer_load_b32(irs[r], (int)pick(lo.q_sc, c), soff, 0);
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(irs[r], (int)pick(lo.q_d, c), soff, 0);
                 buf[r].d[0] = v.x, buf[r].d[1] = v.y, buf[r].d[2] = v.z, buf[r].d[3] = v.w;
                 // rows of an even number of blocks: the dword holding quant
                 // bytes 15-16 lies inside the row; otherwise read the halfword
-                buf[r].d[4] = ROWS4 ? __builtin_amdgcn_raw_buffer_load_b32(irs[r], (int)lo.q_h[c], soff, 0)
+                buf[r].d[4] = ROWS4 ? __builtin_amdgcn_raw_buffer_load_b32(irs[r], (int)pick(lo.q_h, c), soff, 0)
                                     : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
-                                          irs[r], (int)lo.q_h[c] + 2 - (int)lo.q_sh[c], soff, 0);
+                                          irs[r], (int)pick(lo.q_h, c) + 2 - (int)pick(lo.q_sh, c), soff, 0);
             }
         }
         if (++ir == i1) {
@@ -363,7 +374,7 @@ struct Wave {
 #pragma unroll
             for (int r = 0; r < R; r++) {
                 // realign the 16 quants: byte offset 0 or 2 within d[0]
-                const uint32_t sh = ROWS4 ? lo.q_sh[0] : lo.q_sh[ccls[r]];
+                const uint32_t sh = ROWS4 ? lo.q_sh[0] : pick(lo.q_sh, ccls[r]);
 #pragma unroll
                 for (int k = 0; k < 4; k++)
                     q[r][k] = __builtin_amdgcn_alignbyte(buf[r].d[k + 1], buf[r].d[k], sh);
@@ -408,7 +419,7 @@ struct Wave {
 #pragma unroll
         for (int r = 0; r < R; r++) {
             if constexpr (FMT == kQ8) {
-                const float d = f16_lo(buf[r].sc >> (ROWS4 ? lo.q_ssh[0] : lo.q_ssh[ccls[r]]));
+                const float d = f16_lo(buf[r].sc >> (ROWS4 ? lo.q_ssh[0] : pick(lo.q_ssh, ccls[r])));
 #pragma unroll
                 for (int s = 0; s < NS; s++)
                     acc[r][s] = __builtin_fmaf(d, bs[r][s], acc[r][s]);
@@ -664,70 +675,48 @@ GemvArgs make_args(const void *w, int64_t rows, int64_t cols)
 }
 
 // ---------------------------------------------------------------------------
-// Row-split kernel: the workgroup's waves share each row.
+// Row-split SSQ kernel: the waves of a workgroup share each row.
 //
-// HBM delivers the most when, at any moment, the requests in flight cover one
-// compact, contiguous window of memory that slides forward (as a grid-stride
-// read does), and when that window is small.  With every wave owning whole
-// rows, the window is several thousand rows wide with one round in flight per
-// row.  Here workgroup g owns rows g, g + G, g + 2G, ... (G workgroups, one
-// per CU) and covers P of them per step: the Q waves of a row each load one of
-// its Q rounds.  At any moment the GPU reads a band of about G * P * (D + 1)
-// consecutive rows, each one whole.
+// HBM delivers the most when the requests in flight form one compact window
+// of memory that slides forward (as a grid-stride read does), and when that
+// window is small.  With every wave owning whole rows, the window spans
+// thousands of rows with one round in flight per row.  Here workgroup g (of
+// G, one per CU) owns rows g, g + G, g + 2G, ... and covers P of them per
+// step; the Q waves of a row each load T consecutive rounds of it.  At any
+// moment the GPU reads a narrow band of consecutive rows, each one whole.
 //
-// A wave always handles the same round of its rows, so the 64 x unit-columns
-// of x it needs are the same for every row: it loads them once into
-// registers (no LDS staging, no LDS reads in the loop).  Per step it reduces
-// its round's partial dot product over its 64 lanes (the same fixed DPP tree)
-// and parks it in LDS; every S steps the workgroup sums the Q partials of
-// each finished row in round order and stores the row.  Each output's order of
-// operations depends only on (rows, cols) and the format, so a stream's
-// result is bitwise independent of the stream count and of its slot.
+// Loads run one step ahead, round by round: after computing round tt of
+// step t a wave loads round tt of step t + 1 into the buffer it just freed,
+// so T rounds per wave are always in flight.
 //
-// Used when a row has at most 16 rounds and, for Q8, an even number of blocks
-// (every row then starts on a dword boundary).
+// A wave always handles the same column slice, so it loads its T rounds of x
+// (T * 8 columns per lane, both twins) once into registers: no LDS staging,
+// no LDS reads in the loop.  Per step it sums its rounds per lane, reduces
+// over its 64 lanes (the fixed DPP tree) and parks the partial in LDS; every
+// S steps the workgroup sums the Q partials of each finished row in slice
+// order and stores the row.  A row's order of operations depends only on
+// (rows, cols).
 constexpr int kSplitMaxWaves = 16;
-#ifndef PTI_SPLIT_PREFETCH
-#define PTI_SPLIT_PREFETCH 1
-#endif
-constexpr int kSD = PTI_SPLIT_PREFETCH;  // steps of loads in flight ahead of the compute
-#ifndef PTI_SPLIT_ROUND_PIPE
-#define PTI_SPLIT_ROUND_PIPE 1
-#endif
-constexpr bool kSplitRoundPipe = PTI_SPLIT_ROUND_PIPE && kSD == 1;  // issue the next step round by round
-#ifndef PTI_SPLIT_T_SSQ
-#define PTI_SPLIT_T_SSQ 5  // rounds per wave per step (SSQ)
-#endif
-#ifndef PTI_SPLIT_T_Q8_1
-#define PTI_SPLIT_T_Q8_1 1  // rounds per wave per step (Q8, one stream)
-#endif
-#ifndef PTI_SPLIT_Q8_MAXN
-#define PTI_SPLIT_Q8_MAXN 0  // Q8 uses the row-split kernel for n_streams up to this (all or none, so results do not depend on n_streams)
-#endif
+constexpr int kSplitTMax = 5;           // rounds per wave at most (x: 80 registers)
+constexpr int kSplitWavesSmallT = 16;   // waves per workgroup when T <= 2
+constexpr int kSplitWavesBigT = 4;      // ... when T >= 3 (measured best)
+
+// Launch bound for T (the registers per wave follow from it).
+constexpr int split_bound_waves(int T) { return T >= 3 ? 8 : kSplitMaxWaves; }
 
 struct SplitArgs {
     GemvArgs g;
-    int32_t P, Q;   // rows per step, waves (= rounds) per row
-    int32_t S;      // steps per flush of finished rows
+    int32_t P, Q;         // rows per step, waves per row
+    int32_t S;            // steps per flush of finished rows
 };
 
-// Waves per workgroup at T rounds per wave: up to 16, or 8 when the x slice
-// of T rounds needs more than the 128 registers a 16-wave workgroup allows.
-#ifndef PTI_SPLIT_WG_PER_CU
-#define PTI_SPLIT_WG_PER_CU 1
-#endif
-#ifndef PTI_SPLIT_WAVES_BIG_T
-#define PTI_SPLIT_WAVES_BIG_T 4
-#endif
-constexpr int split_max_waves(int T) { return T >= 3 ? PTI_SPLIT_WAVES_BIG_T : kSplitMaxWaves; }
-
-template <int FMT, int NS, int T>
-__global__ __launch_bounds__(64 * split_max_waves(T)) void gemv_split_kernel(SplitArgs sa)
+template <int T>
+__global__ __launch_bounds__(64 * split_bound_waves(T)) void gemv_ssq_split_kernel(SplitArgs sa)
 {
-    constexpr int UC = unit_cols<FMT>();
+    constexpr int UC = unit_cols<kSSQ>();
     const GemvArgs &a = sa.g;
     const int P = sa.P, Q = sa.Q, S = sa.S;
-    extern __shared__ float part[];  // [2][S * P][Q][NS]
+    extern __shared__ float part[];  // [2][S * P][Q][2]: row partials, double-buffered
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int p = wv / Q, q = wv - (wv / Q) * Q;
@@ -736,20 +725,20 @@ __global__ __launch_bounds__(64 * split_max_waves(T)) void gemv_split_kernel(Spl
     const int steps = (int)((wg_rows + P - 1) / P);
 
     // x of this lane's units in rounds q T .. q T + T - 1 (zero past the row's
-    // last unit), all streams
-    float xv[T][UC][NS];
+    // last unit), both twins
+    float xv[T][UC][2];
 #pragma unroll
     for (int tt = 0; tt < T; tt++) {
         const int unit = (q * T + tt) * 64 + lane;
 #pragma unroll
-        for (int s = 0; s < NS; s++)
+        for (int s = 0; s < 2; s++)
 #pragma unroll
             for (int k = 0; k < UC / 4; k++) {
-                float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
                 if (unit < a.units)
-                    t = *reinterpret_cast<const float4 *>(a.x[s] + unit * UC + 4 * k);
-                xv[tt][4 * k][s] = t.x, xv[tt][4 * k + 1][s] = t.y, xv[tt][4 * k + 2][s] = t.z,
-                              xv[tt][4 * k + 3][s] = t.w;
+                    v = *reinterpret_cast<const float4 *>(a.x[s] + unit * UC + 4 * k);
+                xv[tt][4 * k][s] = v.x, xv[tt][4 * k + 1][s] = v.y, xv[tt][4 * k + 2][s] = v.z,
+                              xv[tt][4 * k + 3][s] = v.w;
             }
     }
 
@@ -758,7 +747,8 @@ __global__ __launch_bounds__(64 * split_max_waves(T)) void gemv_split_kernel(Spl
     const int64_t row_step = (int64_t)P * G * a.row_bytes;  // bytes from a wave's row to its next
     const uint8_t *row0 = a.w + (g + (int64_t)p * G) * a.row_bytes;
 
-    // Buffer resource over the row of step t (empty past the workgroup's rows).
+    // Buffer resource over the row of step t (empty past the workgroup's rows:
+    // its loads return zeros without touching memory).
     auto rsrc_for = [&](int t) {
         const int64_t m = (int64_t)t * P + p;  // row slot within the workgroup
         const int n = m < wg_rows ? (int)a.row_bytes : 0;
@@ -768,57 +758,29 @@ __global__ __launch_bounds__(64 * split_max_waves(T)) void gemv_split_kernel(Spl
     // Loads of round tt of this wave's slice.
     auto load_round = [&](__amdgpu_buffer_rsrc_t rs, int tt, Unit &u) {
         const int so = soff + tt * (int)kRoundBytes;
-        if constexpr (FMT == kSSQ) {
-            u.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.ssq_sc, so, 0);
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lo.ssq_d, so, 0);
-            u.d[0] = v.x, u.d[1] = v.y, u.d[2] = v.z, u.d[3] = v.w;
-        } else {
-            u.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.q_sc[0], so, 0);
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lo.q_d[0], so, 0);
-            u.d[0] = v.x, u.d[1] = v.y, u.d[2] = v.z, u.d[3] = v.w;
-            u.d[4] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.q_h[0], so, 0);
-        }
-    };
-    // Loads of step t into ut.
-    auto issue = [&](int t, Unit (&ut)[T]) {
-        const __amdgpu_buffer_rsrc_t rs = rsrc_for(t);
-#pragma unroll
-        for (int tt = 0; tt < T; tt++)
-            load_round(rs, tt, ut[tt]);
+        u.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.ssq_sc, so, 0);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lo.ssq_d, so, 0);
+        u.d[0] = v.x, u.d[1] = v.y, u.d[2] = v.z, u.d[3] = v.w;
     };
 
-    // The round's partial dot product of step t, reduced over the lanes and
-    // parked in LDS, in half `half` of the double buffer at step `local` of
-    // the window (steps past the workgroup's last write nothing).
-    auto compute = [&](int t, int half, int local, const Unit (&ut)[T], auto &&after_round) {
-        float acc[NS];
+    // Step t from ut: per round, the twins' 8-slot dot products, scaled and
+    // summed per lane; after round tt, load round tt of the next step into
+    // nxt.  Then the lane sums are reduced and parked in LDS (half `half` of
+    // the double buffer, step `local` of the window; steps past the
+    // workgroup's last write nothing).
+    auto step = [&](int t, int half, int local, const Unit (&ut)[T], Unit (&nxt)[T]) {
+        const __amdgpu_buffer_rsrc_t rs_next = rsrc_for(t + 1);
+        float acc[2];
 #pragma unroll
         for (int tt = 0; tt < T; tt++) {
-        const Unit &u = ut[tt];
-        float bs[NS];
-        if constexpr (FMT == kQ8) {
-            uint32_t qd[4];
-#pragma unroll
-            for (int k = 0; k < 4; k++)
-                qd[k] = __builtin_amdgcn_alignbyte(u.d[k + 1], u.d[k], lo.q_sh[0]);
-#pragma unroll
-            for (int c = 0; c < UC; c++) {
-                const float wq = sbyte(qd[c >> 2], c & 3);
-#pragma unroll
-                for (int s = 0; s < NS; s++)
-                    bs[s] = c == 0 ? wq * xv[tt][c][s] : __builtin_fmaf(wq, xv[tt][c][s], bs[s]);
-            }
-            const float d = f16_lo(u.sc >> lo.q_ssh[0]);
-#pragma unroll
-            for (int s = 0; s < NS; s++)
-                acc[s] = tt == 0 ? d * bs[s] : __builtin_fmaf(d, bs[s], acc[s]);
-        } else {
+            const Unit &u = ut[tt];
+            float bs[2];
             // slot c: dword c/2, halfword c%2; twin A = high byte, twin B = low byte
 #pragma unroll
             for (int c = 0; c < UC; c++) {
                 const uint32_t dw = u.d[c >> 1];
 #pragma unroll
-                for (int s = 0; s < NS; s++) {
+                for (int s = 0; s < 2; s++) {
                     const float wq = sbyte(dw, 2 * (c & 1) + (s == 0 ? 1 : 0));
                     bs[s] = c == 0 ? wq * xv[tt][c][s] : __builtin_fmaf(wq, xv[tt][c][s], bs[s]);
                 }
@@ -826,38 +788,37 @@ __global__ __launch_bounds__(64 * split_max_waves(T)) void gemv_split_kernel(Spl
             const float da = f16_lo(u.sc), db = f16_hi(u.sc);
             acc[0] = tt == 0 ? da * bs[0] : __builtin_fmaf(da, bs[0], acc[0]);
             acc[1] = tt == 0 ? db * bs[1] : __builtin_fmaf(db, bs[1], acc[1]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        after_round(tt);
-        __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_sched_barrier(0);
+            load_round(rs_next, tt, nxt[tt]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         const int slot = (half * S + local) * P + p;  // row slot in the double buffer
 #pragma unroll
-        for (int s = 0; s < NS; s++) {
+        for (int s = 0; s < 2; s++) {
             const float v = wave_sum(acc[s]);
             if (lane == 63 && t < steps)
-                part[(slot * Q + q) * NS + s] = v;
+                part[(slot * Q + q) * 2 + s] = v;
         }
     };
 
-    // Sum the partials of the rows of steps [t0, t1) (in half `half`) in round
+    // Sum the partials of the rows of steps [t0, t1) (in half `half`) in slice
     // order and store them.
     auto flush = [&](int t0, int t1, int half) {
         __syncthreads();
         const int n = (t1 - t0) * P;
-        // streams outermost with a compile-time index: a lane-varying index
-        // into the argument array would load the output pointer from memory,
-        // and that wait would also drain the weight loads in flight
+        // twins outermost with a compile-time index: a lane-varying index into
+        // the argument array would load the output pointer from memory, and
+        // that wait would also drain the weight loads in flight
 #pragma unroll
-        for (int s = 0; s < NS; s++)
+        for (int s = 0; s < 2; s++)
             for (int r = tid; r < n; r += 64 * P * Q) {  // r: row slot relative to step t0
                 const int64_t m = (int64_t)t0 * P + r;
                 if (m >= wg_rows)
                     continue;
                 const int slot = half * S * P + r;
-                float acc = part[(slot * Q) * NS + s];
+                float acc = part[(slot * Q) * 2 + s];
                 for (int j = 1; j < Q; j++)
-                    acc += part[((slot * Q) + j) * NS + s];
+                    acc += part[((slot * Q) + j) * 2 + s];
                 a.y[s][g + m * G] = acc;
             }
         // Stores count on the same counter as the weight loads.  Without this
@@ -868,78 +829,72 @@ __global__ __launch_bounds__(64 * split_max_waves(T)) void gemv_split_kernel(Spl
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
     };
 
-    Unit bufs[kSD + 1][T];
+    Unit bufs[2][T];
+    {
+        const __amdgpu_buffer_rsrc_t rs0 = rsrc_for(0);
 #pragma unroll
-    for (int k = 0; k < kSD; k++)
-        issue(k, bufs[k]);
-    const auto nothing = [](int) {};
-    // Windows of S steps (S a multiple of kSD + 1, so step t always uses
-    // buffer t mod (kSD + 1)); the last window is rounded up to a multiple of
-    // kSD + 1 so the loop has a single exit: its extra steps fall past the
-    // workgroup's rows, load through empty resources and write nothing.
+        for (int tt = 0; tt < T; tt++)
+            load_round(rs0, tt, bufs[0][tt]);
+    }
+    // Windows of S steps (S even, so step t always uses buffer t mod 2); the
+    // last window is rounded up to an even count so the loop has a single
+    // exit: an extra step falls past the workgroup's rows, loads through an
+    // empty resource and writes nothing.
     int half = 0;
     for (int t0 = 0; t0 < steps; t0 += S, half ^= 1) {
         const int t1 = t0 + S < steps ? t0 + S : steps;
-        const int iters = (t1 - t0 + kSD) / (kSD + 1);
+        const int iters = (t1 - t0 + 1) / 2;
         for (int it = 0; it < iters; it++) {
-            const int local = it * (kSD + 1);
-            const int tb = t0 + local;
-            if constexpr (kSplitRoundPipe) {
-                // one step ahead, round by round: after computing round tt of
-                // step t, load round tt of step t + 1 into the buffer it freed,
-                // so T rounds per wave are in flight at all times
-                [&]<int... K>(std::integer_sequence<int, K...>) {
-                    ((
-                         [&] {
-                             const __amdgpu_buffer_rsrc_t rs = rsrc_for(tb + K + 1);
-                             compute(tb + K, half, local + K, bufs[K],
-                                     [&](int tt) { load_round(rs, tt, bufs[(K + 1) % 2][tt]); });
-                         }()),
-                     ...);
-                }(std::make_integer_sequence<int, 2>{});
-            } else {
-                [&]<int... K>(std::integer_sequence<int, K...>) {
-                    ((issue(tb + K + kSD, bufs[(K + kSD) % (kSD + 1)]), __builtin_amdgcn_sched_barrier(0),
-                      compute(tb + K, half, local + K, bufs[K], nothing), __builtin_amdgcn_sched_barrier(0)),
-                     ...);
-                }(std::make_integer_sequence<int, kSD + 1>{});
-            }
+            const int local = 2 * it, tb = t0 + local;
+            step(tb, half, local, bufs[0], bufs[1]);
+            step(tb + 1, half, local + 1, bufs[1], bufs[0]);
         }
         flush(t0, t1, half);
     }
 }
 
-// Split geometry for a row of `rounds` rounds, or false if the row-split
-// kernel does not apply.
-bool split_shape(int rounds, int ns, int T, SplitArgs &sa)
+// Rounds per wave for a row of `rounds` rounds: at most kSplitTMax, spread
+// evenly over the fewest waves.
+int split_T(int rounds)
 {
-    const int Q = (rounds + T - 1) / T, W = split_max_waves(T);
+    const int q = (rounds + kSplitTMax - 1) / kSplitTMax;
+    return (rounds + q - 1) / q;
+}
+
+// Geometry for T, or false if the row needs more waves than a workgroup may
+// have.  S: steps per flush, even, with the partials' double buffer at most
+// 32 KB of LDS.
+bool split_shape(int rounds, int T, SplitArgs &sa)
+{
+    const int Q = (rounds + T - 1) / T, W = split_bound_waves(T);
     if (rounds < 1 || Q > W)
         return false;
     sa.Q = Q;
-    sa.P = W / Q;
-    // flush every S steps, S a multiple of kSD + 1: the double buffer holds
-    // 2 S P Q NS floats, at most 32 KB
-    int S = 64 - 64 % (kSD + 1);
-    while (S > kSD + 1 && 2 * S * sa.P * sa.Q * ns * 4 > 32 * 1024)
-        S -= kSD + 1;
+    sa.P = std::max(1, std::min(W, T >= 3 ? kSplitWavesBigT : kSplitWavesSmallT) / Q);
+    int S = 64;
+    while (S > 2 && 2 * S * sa.P * Q * 2 * 4 > 32 * 1024)
+        S -= 2;
     sa.S = S;
     return true;
 }
 
-template <int FMT, int NS, int T>
-int launch_split(const GemvArgs &a, const SplitArgs &sa0, hipStream_t stream)
+constexpr int kNotSplit = 1;  // the row-split kernel does not take this shape
+
+template <int T>
+int launch_ssq_split(const GemvArgs &a, hipStream_t stream)
 {
-    SplitArgs sa = sa0;
+    SplitArgs sa;
+    if (!split_shape(a.rounds, T, sa))
+        return kNotSplit;
     sa.g = a;
     const int cus = device_cus();
     if (cus <= 0) {
         pti::set_hip_error(hipGetLastError());
         return PTI_ERR_HIP;
     }
-    const int64_t grid = std::min<int64_t>((int64_t)cus * PTI_SPLIT_WG_PER_CU, a.rows);
-    const size_t lds = (size_t)2 * sa.S * sa.P * sa.Q * NS * sizeof(float);
-    hipLaunchKernelGGL((gemv_split_kernel<FMT, NS, T>), dim3((unsigned)grid), dim3((unsigned)(64 * sa.P * sa.Q)), lds,
+    const int64_t grid = std::min<int64_t>(cus, a.rows);
+    const size_t lds = (size_t)2 * sa.S * sa.P * sa.Q * 2 * sizeof(float);
+    hipLaunchKernelGGL(gemv_ssq_split_kernel<T>, dim3((unsigned)grid), dim3((unsigned)(64 * sa.P * sa.Q)), lds,
                        stream, sa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
@@ -947,6 +902,17 @@ int launch_split(const GemvArgs &a, const SplitArgs &sa0, hipStream_t stream)
         return PTI_ERR_HIP;
     }
     return PTI_OK;
+}
+
+int launch_ssq_split(const GemvArgs &a, hipStream_t stream)
+{
+    switch (split_T(a.rounds)) {
+    case 1: return launch_ssq_split<1>(a, stream);
+    case 2: return launch_ssq_split<2>(a, stream);
+    case 3: return launch_ssq_split<3>(a, stream);
+    case 4: return launch_ssq_split<4>(a, stream);
+    default: return launch_ssq_split<5>(a, stream);
+    }
 }
 
 }  // namespace
@@ -972,9 +938,9 @@ int pti_gemv_ssq(const void *w_ssq, const float *x_a, const float *x_b, float *y
     GemvArgs a = make_args<kSSQ>(w_ssq, rows, cols);
     a.x[0] = x_a, a.x[1] = x_b;
     a.y[0] = y_a, a.y[1] = y_b;
-    SplitArgs sa;
-    if (split_shape(a.rounds, 2, PTI_SPLIT_T_SSQ, sa))
-        return launch_split<kSSQ, 2, PTI_SPLIT_T_SSQ>(a, sa, static_cast<hipStream_t>(stream));
+    const int st = launch_ssq_split(a, static_cast<hipStream_t>(stream));
+    if (st != kNotSplit)
+        return st;
     return launch<kSSQ, 2, 2, true>(a, static_cast<hipStream_t>(stream));
 }
 
@@ -1000,18 +966,6 @@ int pti_gemv_q8_multi(const void *w_q8, const float *x, float *y, int64_t rows, 
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     // rows start on dword boundaries when a row holds an even number of blocks
-    SplitArgs sa;
-    if ((cols / PTI_BLOCK) % 2 == 0 && n_streams <= PTI_SPLIT_Q8_MAXN) {
-        const int T = n_streams == 1 ? PTI_SPLIT_T_Q8_1 : 1;
-        if (split_shape(a.rounds, n_streams, T, sa)) {
-            switch (n_streams) {
-            case 1: return launch_split<kQ8, 1, PTI_SPLIT_T_Q8_1>(a, sa, st);
-            case 2: return launch_split<kQ8, 2, 1>(a, sa, st);
-            case 3: return launch_split<kQ8, 3, 1>(a, sa, st);
-            default: return launch_split<kQ8, 4, 1>(a, sa, st);
-            }
-        }
-    }
     if ((cols / PTI_BLOCK) % 2 == 0) {
         switch (n_streams) {
         case 1: return launch<kQ8, 1, 1, true>(a, st);
