@@ -9,10 +9,14 @@ copies (568 MB, more than twice the 256 MB Infinity Cache), so every step
 reads its weights from HBM.
 
 Also reported on the same JSON line:
-  * roofline: the SSQ GEMV kernel alone (algorithmic bytes per launch / average
-    launch time measured with HIP events on its stream) against 8 TB/s HBM;
+  * roofline: the SSQ GEMV kernel alone (algorithmic bytes per launch / its
+    launch time, the median over 10 runs of 100 back-to-back launches timed
+    with HIP events on its stream) against 8 TB/s HBM, its HBM traffic from the
+    committed PMC summary, and its rate against a device-to-device copy of the
+    same bytes (copy_ceiling);
   * per_kernel: the Q8 multi-stream GEMV over 17408 x 5120 at N = 1, 2, 4
-    streams (effective weight GB/s, GEMV/s, and t(N=4)/t(N=1)), and the verify;
+    streams (effective weight GB/s, GEMV/s, and t(N=4)/t(N=1)), and the
+    verify, each with median / p10 / p90 over 10 runs;
   * cpu_baseline: the fp64 oracle (scalar C, one host core) running the same
     SSQ GEMV, timed on a bounded number of passes.
 
@@ -44,17 +48,27 @@ def copies_for(nbytes: int) -> int:
     return max(2, -(-2 * MALL_BYTES // nbytes))
 
 
-def timed_loop(torch, fn, n_iter, stream):
-    """Average ms per call of fn(i) for i in range(n_iter), HIP events on `stream`."""
+def timed_loop(torch, fn, n_iter, stream, i0=0):
+    """Average ms per call of fn(i) for i in range(i0, i0 + n_iter), HIP events on `stream`."""
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(n_iter):
+    for i in range(i0, i0 + n_iter):
         fn(i)
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / n_iter
+
+
+def timed_stats(torch, fn, stream, reps=10, per_rep=100, warmup=50):
+    """Per-call time over `reps` back-to-back runs of `per_rep` calls each (after
+    `warmup` calls): median, p10 and p90 in microseconds."""
+    for i in range(warmup):
+        fn(i)
+    t = sorted(timed_loop(torch, fn, per_rep, stream, i0=r * per_rep) * 1e3 for r in range(reps))
+    q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
+    return {"median_us": round(q(0.5), 3), "p10_us": round(q(0.1), 3), "p90_us": round(q(0.9), 3)}
 
 
 def cpu_baseline(d, budget_s: float):
@@ -286,9 +300,19 @@ def main():
     log(f"step: {ms_step * 1e3:.2f} us")
 
     gemv_algo_bytes = w_bytes + 2 * COLS * 4 + 2 * ROWS * 4
-    ms_gemv = timed_loop(torch, gemv, args.steps, stream)
-    ms_verify = timed_loop(torch, verify, args.steps, stream)
-    log(f"ssq gemv alone: {ms_gemv * 1e3:.2f} us; verify alone {ms_verify * 1e3:.2f} us")
+    st_gemv = timed_stats(torch, gemv, stream)
+    st_verify = timed_stats(torch, verify, stream)
+    ms_gemv = st_gemv["median_us"] * 1e-3
+    ms_verify = st_verify["median_us"] * 1e-3
+    log(f"ssq gemv alone: {st_gemv}; verify alone {st_verify}")
+
+    # device-to-device copy of the same byte count, rotated the same way: the
+    # practical ceiling (reads and writes w_bytes each)
+    dsts = [torch.empty_like(w0) for _ in range(2)]
+    st_copy = timed_stats(torch, lambda i: dsts[i % 2].copy_(ws[i % n_copies]), stream)
+    copy_GBps = 2 * w_bytes / (st_copy["median_us"] * 1e-6) / 1e9
+    del dsts
+    log(f"copy {w_bytes} B: {st_copy}, {copy_GBps:.0f} GB/s read+write")
 
     traffic = read_traffic()
     result = {
@@ -322,13 +346,16 @@ def main():
             "traffic": traffic["bytes"] if traffic else None,
             "algorithmic_bytes_per_launch": gemv_algo_bytes,
             "avg_launch_us": round(ms_gemv * 1e3, 3),
+            "launch_us_stats": st_gemv,
             "traffic_source": traffic["source"] if traffic else None,
+            "vs_copy": round(gemv_algo_bytes / (ms_gemv * 1e-3) / 1e9 / copy_GBps, 4),
         },
+        "copy_ceiling": {"GBps_read_plus_write": round(copy_GBps, 1), "bytes_each_way": w_bytes, **st_copy},
     }
-    per_kernel = {"ssq_twin_gemv": {"us": round(ms_gemv * 1e3, 3),
+    per_kernel = {"ssq_twin_gemv": {"us": round(ms_gemv * 1e3, 3), **st_gemv,
                                     "weight_GBps": round(w_bytes / (ms_gemv * 1e-3) / 1e9, 2),
                                     "gemv_per_s": round(1 / (ms_gemv * 1e-3), 1)},
-                  "verify_n2_v17408": {"us": round(ms_verify * 1e3, 3)}}
+                  "verify_n2_v17408": {"us": round(ms_verify * 1e3, 3), **st_verify}}
     del ws, w0
     torch.cuda.empty_cache()
 
@@ -347,12 +374,11 @@ def main():
                 st = L.pti_gemv_q8_multi(wqs[i % nq].data_ptr(), X.data_ptr(), Y.data_ptr(), ROWS, COLS, n, sp)
                 if st:
                     pti._check("pti_gemv_q8_multi", st)
-            for i in range(args.warmup):
-                qgemv(i)
-            t[n] = timed_loop(torch, qgemv, args.steps, stream)
+            stn = timed_stats(torch, qgemv, stream)
+            t[n] = stn["median_us"] * 1e-3
             algo = Pq.nbytes + n * (COLS + ROWS) * 4
             per_kernel[f"q8_gemv_n{n}"] = {
-                "us": round(t[n] * 1e3, 3),
+                "us": round(t[n] * 1e3, 3), **stn,
                 "weight_GBps": round(Pq.nbytes / (t[n] * 1e-3) / 1e9, 2),
                 "frac_of_hbm_peak": round(algo / (t[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "gemv_per_s": round(1 / (t[n] * 1e-3), 1),

@@ -60,17 +60,22 @@
 
 #include "pti_internal.h"
 
-#ifndef PTI_RMAX_SSQ
-#define PTI_RMAX_SSQ 1  // rows computed together by a wave (SSQ)
+// Per-wave-row kernel geometry by format and stream count: waves per
+// workgroup (a multiple of 4), steps of loads in flight, rows per wave.  None
+// of the three changes a row's arithmetic (they change which wave computes a
+// row and when), so they may differ between stream counts; the values are
+// measured optima and can be overridden at build time.
+#ifndef PTI_Q8_N1_CFG
+#define PTI_Q8_N1_CFG 12, 4, 1
 #endif
-#ifndef PTI_RMAX_Q8
-#define PTI_RMAX_Q8 2   // rows computed together by a wave (Q8)
+#ifndef PTI_Q8_N2_CFG
+#define PTI_Q8_N2_CFG 12, 4, 1
 #endif
-#ifndef PTI_WAVES
-#define PTI_WAVES 16    // waves per workgroup (one workgroup per CU)
+#ifndef PTI_Q8_N4_CFG
+#define PTI_Q8_N4_CFG 16, 4, 2
 #endif
-#ifndef PTI_PREFETCH
-#define PTI_PREFETCH 3  // steps of weight loads in flight ahead of the compute
+#ifndef PTI_SSQ_ROWWISE_CFG
+#define PTI_SSQ_ROWWISE_CFG 16, 3, 1
 #endif
 #ifndef PTI_LDS_BUDGET
 #define PTI_LDS_BUDGET (160 * 1024)
@@ -78,11 +83,7 @@
 
 namespace {
 
-constexpr int kWaves = PTI_WAVES;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kD = PTI_PREFETCH;
 constexpr uint32_t kRoundBytes = 1088;  // bytes of a row one round of 64 lanes covers (both formats)
-static_assert(kWaves % 4 == 0, "waves per workgroup must fill the four SIMDs evenly");
 
 enum Fmt { kQ8 = 0, kSSQ = 1 };
 
@@ -166,14 +167,14 @@ __device__ __forceinline__ float f16_hi(uint32_t v)
 // e = m * NSP + s (m = column within the group, s = stream); NSP = streams
 // rounded up to 1, 2 or 4 (three streams are padded with a zero fourth).
 // Staging items are (round, column group, lane), spread over the threads.
-template <int UC, int NSP, int NS, int BATCH>
+template <int UC, int NSP, int NS, int BATCH, int THREADS>
 __device__ __forceinline__ void stage_load(const GemvArgs &a, int item0, float4 (&v)[BATCH][NSP], int tid,
                                            int nitems)
 {
     constexpr int CG = UC / 4;
 #pragma unroll
     for (int i = 0; i < BATCH; i++) {
-        const int it = item0 + i * kThreads + tid;
+        const int it = item0 + i * THREADS + tid;
         const int l = it & 63, cg = (it >> 6) % CG, rd = (it >> 6) / CG;
         const int col = (rd * 64 + l) * UC + cg * 4;
 #pragma unroll
@@ -185,14 +186,14 @@ __device__ __forceinline__ void stage_load(const GemvArgs &a, int item0, float4 
     }
 }
 
-template <int UC, int NSP, int BATCH>
+template <int UC, int NSP, int BATCH, int THREADS>
 __device__ __forceinline__ void stage_store(float4 *xs, int item0, const float4 (&v)[BATCH][NSP], int tid,
                                             int nitems)
 {
     constexpr int CG = UC / 4;
 #pragma unroll
     for (int i = 0; i < BATCH; i++) {
-        const int it = item0 + i * kThreads + tid;
+        const int it = item0 + i * THREADS + tid;
         if (it >= nitems)
             break;
         const int l = it & 63, cg = (it >> 6) % CG, rd = (it >> 6) / CG;
@@ -216,7 +217,7 @@ __device__ __forceinline__ void stage_store(float4 *xs, int item0, const float4 
 
 // Stage rounds [r0, r0 + nr) of x into LDS rounds 0..nr-1 (nr at most the
 // LDS budget's chunk, which BATCH items per thread cover).
-template <int UC, int NSP, int NS, int BATCH>
+template <int UC, int NSP, int NS, int BATCH, int THREADS>
 __device__ __forceinline__ void stage_all(const GemvArgs &a0, float4 *xs, int r0, int nr, int tid)
 {
     GemvArgs a = a0;  // x pointers shifted to the chunk's first column
@@ -225,10 +226,10 @@ __device__ __forceinline__ void stage_all(const GemvArgs &a0, float4 *xs, int r0
     for (int s = 0; s < NS; s++)
         a.x[s] += c0;
     a.cols -= c0;
-    const int nitems = nr * 64 * (UC / 4);  // <= BATCH * kThreads
+    const int nitems = nr * 64 * (UC / 4);  // <= BATCH * THREADS
     float4 v[BATCH][NSP];
-    stage_load<UC, NSP, NS, BATCH>(a, 0, v, tid, nitems);
-    stage_store<UC, NSP, BATCH>(xs, 0, v, tid, nitems);
+    stage_load<UC, NSP, NS, BATCH, THREADS>(a, 0, v, tid, nitems);
+    stage_store<UC, NSP, BATCH, THREADS>(xs, 0, v, tid, nitems);
 }
 
 template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
@@ -251,7 +252,7 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-template <int FMT, int NSP, int NS, int R, bool ROWS4>
+template <int FMT, int NSP, int NS, int R, bool ROWS4, int kD>
 struct Wave {
     static constexpr int UC = unit_cols<FMT>();
     static constexpr int CG = UC / 4;
@@ -540,9 +541,11 @@ struct Wave {
     }
 };
 
-template <int FMT, int NSP, int NS, int R, bool ROWS4>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a)
+template <int FMT, int NSP, int NS, int R, bool ROWS4, int W, int D>
+__global__ __launch_bounds__(64 * W) void gemv_kernel(GemvArgs a)
 {
+    static_assert(W % 4 == 0, "waves per workgroup must fill the four SIMDs evenly");
+    constexpr int kThreads = 64 * W;
     extern __shared__ float4 xs[];
     constexpr int UC = unit_cols<FMT>();
     // Staging items per thread: enough for the largest chunk of x the LDS
@@ -558,13 +561,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a)
     // count to within one and, at any moment, the whole GPU reads one window
     // of consecutive rows.  Waves w, w + 4, w + 8, ... of a workgroup share a
     // SIMD and take turns through its rows.
-    constexpr int kPerSimd = kWaves / 4;
+    constexpr int kPerSimd = W / 4;
     const int64_t nsimd = (int64_t)gridDim.x * 4;
     const int64_t sg = (int64_t)blockIdx.x * 4 + (wv & 3);
     const int j = wv >> 2;
     const int64_t n_simd_rows = sg < a.rows ? (a.rows - sg + nsimd - 1) / nsimd : 0;
     const int nrow = (int)(n_simd_rows > j ? (n_simd_rows - j + kPerSimd - 1) / kPerSimd : 0);
-    Wave<FMT, NSP, NS, R, ROWS4> w(a, xs, lane, sg + (int64_t)j * nsimd, (int64_t)kPerSimd * nsimd, nrow);
+    Wave<FMT, NSP, NS, R, ROWS4, D> w(a, xs, lane, sg + (int64_t)j * nsimd, (int64_t)kPerSimd * nsimd, nrow);
 
     if (a.chunk_rounds >= a.rounds) {
         // All of x fits: stage it once, then run every pass.  The x loads go
@@ -572,11 +575,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a)
         // for x while the weights are already in flight.
         float4 v[BATCH][NSP];
         const int nitems = a.rounds * 64 * (UC / 4);
-        stage_load<UC, NSP, NS, BATCH>(a, 0, v, tid, nitems);
+        stage_load<UC, NSP, NS, BATCH, kThreads>(a, 0, v, tid, nitems);
         __builtin_amdgcn_sched_barrier(0);
         w.begin(0, min(w.npass, w.kGroupPasses), 0, a.rounds);
         __builtin_amdgcn_sched_barrier(0);
-        stage_store<UC, NSP, BATCH>(xs, 0, v, tid, nitems);
+        stage_store<UC, NSP, BATCH, kThreads>(xs, 0, v, tid, nitems);
         __syncthreads();
         w.begin_group(0);
         w.template loop<true>();
@@ -598,7 +601,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a)
             for (int i0 = 0; i0 < a.rounds; i0 += a.chunk_rounds) {
                 const int i1 = min(a.rounds, i0 + a.chunk_rounds);
                 __syncthreads();
-                stage_all<UC, NSP, NS, BATCH>(a, xs, i0, i1 - i0, tid);
+                stage_all<UC, NSP, NS, BATCH, kThreads>(a, xs, i0, i1 - i0, tid);
                 __syncthreads();
                 if (p < w.npass) {
                     if (i0 == 0)
@@ -626,11 +629,29 @@ int device_cus()
     return cus;
 }
 
+struct RowwiseCfg {
+    int waves, prefetch, rows;
+};
+
+template <int FMT, int NS>
+constexpr RowwiseCfg rowwise_cfg()
+{
+    if constexpr (FMT == kSSQ)
+        return {PTI_SSQ_ROWWISE_CFG};
+    else if constexpr (NS == 1)
+        return {PTI_Q8_N1_CFG};
+    else if constexpr (NS == 2)
+        return {PTI_Q8_N2_CFG};
+    else
+        return {PTI_Q8_N4_CFG};
+}
+
 template <int FMT, int NSP, int NS, bool ROWS4>
 int launch(const GemvArgs &a0, hipStream_t stream)
 {
     constexpr int UC = unit_cols<FMT>();
-    constexpr int R = FMT == kSSQ ? PTI_RMAX_SSQ : PTI_RMAX_Q8;
+    constexpr RowwiseCfg cfg = rowwise_cfg<FMT, NS>();
+    constexpr int R = cfg.rows, kWaves = cfg.waves, kThreads = 64 * kWaves;
     GemvArgs a = a0;
     const int per_round = 64 * UC * NSP * 4;  // LDS bytes per round of x
     a.chunk_rounds = max(1, min(a.rounds, PTI_LDS_BUDGET / per_round));
@@ -641,7 +662,7 @@ int launch(const GemvArgs &a0, hipStream_t stream)
         return PTI_ERR_HIP;
     }
     const int64_t grid = std::min<int64_t>(cus, (a.rows + kWaves - 1) / kWaves);
-    auto kern = gemv_kernel<FMT, NSP, NS, R, ROWS4>;
+    auto kern = gemv_kernel<FMT, NSP, NS, R, ROWS4, kWaves, cfg.prefetch>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
