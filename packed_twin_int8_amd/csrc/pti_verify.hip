@@ -11,9 +11,10 @@
 // One workgroup of 1024 threads (16 wave64s) handles all streams: the logits
 // of a step are at most 4 x vocab floats, so one CU streams them in a few
 // microseconds and no cross-workgroup combine (and no scratch memory) is
-// needed.  Each thread scans a strided slice with 16-byte loads keeping the
-// first maximum it meets; slices combine with (value larger, or equal and index
-// lower), first across a wavefront with shuffles, then across waves in LDS.
+// needed.  Each thread scans a strided slice of every stream in one pass with
+// 16-byte loads, keeping the first maximum it meets; slices combine with
+// (value larger, or equal and index lower), first across a wavefront with
+// shuffles, then across waves in LDS.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -47,61 +48,119 @@ __device__ __forceinline__ Best wave_best(Best b)
     return b;
 }
 
-template <bool VEC4>
+// All streams in one pass: a thread keeps the first maximum of its strided
+// slice of every stream, with UNROLL independent 16-byte loads per stream in
+// flight; slices combine with better() across the wave, then across waves.
+template <bool VEC4, int NS>
 __global__ __launch_bounds__(kThreads) void verify_kernel(const float *__restrict__ logits,
                                                           const int32_t *__restrict__ tokens_in,
                                                           int32_t *__restrict__ argmax_out,
-                                                          int32_t *__restrict__ accept_out, int64_t vocab,
-                                                          int n)
+                                                          int32_t *__restrict__ accept_out, int64_t vocab)
 {
-    __shared__ Best part[kWaves];
-    __shared__ int amax[4];
+    constexpr int UNROLL = 4;
+    __shared__ Best part[NS][kWaves];
+    __shared__ int amax[NS];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    for (int s = 0; s < n; s++) {
-        const float *v = logits + (int64_t)s * vocab;
-        Best b{-__builtin_inff(), INT_MAX};
-        if constexpr (VEC4) {
-            const float4 *v4 = reinterpret_cast<const float4 *>(v);
-            const int64_t n4 = vocab / 4;
-            for (int64_t k = tid; k < n4; k += kThreads) {
-                const float4 t = v4[k];
-                const int i0 = (int)(4 * k);
-                // indices rise within and across iterations: strict > keeps the first maximum,
-                // the index test admits a first element equal to the initial -inf
-                if (t.x > b.v || b.i == INT_MAX) b = Best{t.x, i0};
-                if (t.y > b.v) b = Best{t.y, i0 + 1};
-                if (t.z > b.v) b = Best{t.z, i0 + 2};
-                if (t.w > b.v) b = Best{t.w, i0 + 3};
-            }
-        } else {
-            for (int64_t k = tid; k < vocab; k += kThreads) {
-                const float t = v[k];
-                if (t > b.v || b.i == INT_MAX)
-                    b = Best{t, (int)k};
+    Best b[NS];
+#pragma unroll
+    for (int s = 0; s < NS; s++)
+        b[s] = Best{-__builtin_inff(), INT_MAX};
+    // indices rise within and across iterations: strict > keeps the first
+    // maximum, the index test admits a first element equal to the initial -inf
+    auto take = [&](Best &bb, float v, int i) {
+        if (v > bb.v || bb.i == INT_MAX)
+            bb = Best{v, i};
+    };
+    if constexpr (VEC4) {
+        const int64_t n4 = vocab / 4;
+        int64_t k = tid;
+        for (; k + (UNROLL - 1) * kThreads < n4; k += UNROLL * kThreads) {
+            float4 t[NS][UNROLL];
+#pragma unroll
+            for (int s = 0; s < NS; s++)
+#pragma unroll
+                for (int u = 0; u < UNROLL; u++)
+                    t[s][u] = reinterpret_cast<const float4 *>(logits + (int64_t)s * vocab)[k + u * kThreads];
+#pragma unroll
+            for (int u = 0; u < UNROLL; u++) {
+                const int i0 = (int)(4 * (k + u * kThreads));
+#pragma unroll
+                for (int s = 0; s < NS; s++) {
+                    take(b[s], t[s][u].x, i0);
+                    take(b[s], t[s][u].y, i0 + 1);
+                    take(b[s], t[s][u].z, i0 + 2);
+                    take(b[s], t[s][u].w, i0 + 3);
+                }
             }
         }
-        b = wave_best(b);
+        for (; k < n4; k += kThreads) {
+            const int i0 = (int)(4 * k);
+#pragma unroll
+            for (int s = 0; s < NS; s++) {
+                const float4 t = reinterpret_cast<const float4 *>(logits + (int64_t)s * vocab)[k];
+                take(b[s], t.x, i0);
+                take(b[s], t.y, i0 + 1);
+                take(b[s], t.z, i0 + 2);
+                take(b[s], t.w, i0 + 3);
+            }
+        }
+    } else {
+        for (int64_t k = tid; k < vocab; k += kThreads)
+#pragma unroll
+            for (int s = 0; s < NS; s++)
+                take(b[s], logits[(int64_t)s * vocab + k], (int)k);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; s++) {
+        b[s] = wave_best(b[s]);
         if (lane == 0)
-            part[wv] = b;
-        __syncthreads();
-        if (wv == 0) {
-            Best c = lane < kWaves ? part[lane] : Best{-__builtin_inff(), INT_MAX};
+            part[s][wv] = b[s];
+    }
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+            Best c = lane < kWaves ? part[s][lane] : Best{-__builtin_inff(), INT_MAX};
             c = wave_best(c);
             if (lane == 0) {
                 amax[s] = c.i;
                 argmax_out[s] = c.i;
             }
         }
-        __syncthreads();
     }
+    __syncthreads();
     if (tid == 0) {
         int a = 1;
-        for (int i = 1; i < n; i++) {
+        for (int i = 1; i < NS; i++) {
             if (tokens_in[i] != amax[i - 1])
                 break;
             a++;
         }
         accept_out[0] = a;
+    }
+}
+
+template <bool VEC4>
+void launch_verify(const float *logits, const int32_t *tokens_in, int32_t *argmax_out, int32_t *accept_out,
+                   int64_t vocab, int n, hipStream_t st)
+{
+    switch (n) {
+    case 1:
+        hipLaunchKernelGGL((verify_kernel<VEC4, 1>), dim3(1), dim3(kThreads), 0, st, logits, tokens_in, argmax_out,
+                           accept_out, vocab);
+        break;
+    case 2:
+        hipLaunchKernelGGL((verify_kernel<VEC4, 2>), dim3(1), dim3(kThreads), 0, st, logits, tokens_in, argmax_out,
+                           accept_out, vocab);
+        break;
+    case 3:
+        hipLaunchKernelGGL((verify_kernel<VEC4, 3>), dim3(1), dim3(kThreads), 0, st, logits, tokens_in, argmax_out,
+                           accept_out, vocab);
+        break;
+    default:
+        hipLaunchKernelGGL((verify_kernel<VEC4, 4>), dim3(1), dim3(kThreads), 0, st, logits, tokens_in, argmax_out,
+                           accept_out, vocab);
+        break;
     }
 }
 
@@ -126,11 +185,9 @@ extern "C" int pti_verify_argmax(const float *logits, const int32_t *tokens_in, 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool vec4 = vocab % 4 == 0 && pti::aligned(logits, 16);
     if (vec4)
-        hipLaunchKernelGGL(verify_kernel<true>, dim3(1), dim3(kThreads), 0, st, logits, tokens_in, argmax_out,
-                           accept_out, vocab, n_streams);
+        launch_verify<true>(logits, tokens_in, argmax_out, accept_out, vocab, n_streams, st);
     else
-        hipLaunchKernelGGL(verify_kernel<false>, dim3(1), dim3(kThreads), 0, st, logits, tokens_in, argmax_out,
-                           accept_out, vocab, n_streams);
+        launch_verify<false>(logits, tokens_in, argmax_out, accept_out, vocab, n_streams, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         pti::set_hip_error(e);
