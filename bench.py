@@ -2,21 +2,25 @@
 
 A step is one pass of the hot path over one batch of synthetic input: the SSQ
 twin GEMV over a 17408 x 5120 packed twin matrix (both twins' outputs from one
-pass over the weights) followed by the greedy verify of the two output
-vectors.  ``value`` is effective weight bandwidth: packed weight bytes per
+pass over the weights) with the greedy verify of the two output vectors fused
+in (pti_gemv_ssq_verify: the GEMV kernel keeps each workgroup's largest
+output, and a one-workgroup kernel reduces those).  ``value`` is effective weight bandwidth: packed weight bytes per
 step / step time, with inputs resident in HBM.  The weights rotate over three
 copies (568 MB, more than twice the 256 MB Infinity Cache), so every step
 reads its weights from HBM.
 
 Also reported on the same JSON line:
-  * roofline: the SSQ GEMV kernel alone (algorithmic bytes per launch / its
-    launch time, the median over 10 runs of 100 back-to-back launches timed
-    with HIP events on its stream) against 8 TB/s HBM, its HBM traffic from the
-    committed PMC summary, and its rate against a device-to-device copy of the
-    same bytes (copy_ceiling);
-  * per_kernel: the Q8 multi-stream GEMV over 17408 x 5120 at N = 1, 2, 4
-    streams (effective weight GB/s, GEMV/s, and t(N=4)/t(N=1)), and the
-    verify, each with median / p10 / p90 over 10 runs;
+  * roofline: the step's entry point, both its kernels with the gap between
+    them (algorithmic bytes per call / its time, the median over 10 runs of
+    100 back-to-back calls timed with HIP events on its stream) against 8 TB/s
+    HBM, its HBM traffic (both kernels) from the committed PMC summary, the
+    kernels' own rocprofv3 averages from the committed kernel-trace summary,
+    and its rate against a device-to-device copy of the same bytes
+    (copy_ceiling);
+  * per_kernel: the unfused pair (pti_gemv_ssq, then pti_verify_argmax), and
+    the Q8 multi-stream GEMV over 17408 x 5120 at N = 1, 2, 4 streams
+    (effective weight GB/s, GEMV/s, and t(N=4)/t(N=1)), each with median /
+    p10 / p90 over 10 runs;
   * cpu_baseline: the fp64 oracle (scalar C, one host core) running the same
     SSQ GEMV, timed on a bounded number of passes.
 
@@ -92,7 +96,10 @@ def cpu_baseline(d, budget_s: float):
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "gemv_ssq_17408x5120_pmc.txt")
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "gemv_ssq_verify_17408x5120_pmc.txt")
+KT_FILE = os.path.join(HERE, "profiles", "gemv_ssq_q8_17408x5120_kernel_stats.md")
+# the step's kernels, as rocprofv3 names them (template arguments kept)
+STEP_KERNELS = ("gemv_ssq_split_kernel<5, true>", "verify_keys_kernel")
 KERNEL_SOURCES = ("packed_twin_int8_amd/csrc/pti_gemv.hip", "packed_twin_int8_amd/build.py")
 PROFILE_CMDS = {
     "kt": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_kt -o kt -- python3 bench.py --no-cpu",
@@ -104,6 +111,12 @@ PROFILE_CMDS = {
                "gpurun_out/prof_write --profiles-out profiles",
 }
 CALIB_BYTES = 64 * 2**20 * 4  # torch.neg over 64 Mi fp32: reads and writes this many bytes
+
+
+def step_algo_bytes() -> int:
+    """Bytes the fused step must move: the packed twin matrix, both x vectors,
+    both y vectors, the two guess tokens, the two argmaxes and the accept count."""
+    return ROWS * (COLS // 32) * 68 + 2 * COLS * 4 + 2 * ROWS * 4 + 2 * 4 + 2 * 4 + 4
 
 
 def kernel_source_hash() -> str:
@@ -130,6 +143,27 @@ def read_traffic():
         return {"bytes": int(kv["traffic_bytes_per_launch"]), "fetch_bytes": int(kv["fetch_bytes_per_launch"]),
                 "write_bytes": int(kv["write_bytes_per_launch"]), "source": os.path.relpath(TRAFFIC_FILE, HERE)}
     except (OSError, KeyError, ValueError):
+        return None
+
+
+def read_kernel_avgs():
+    """rocprofv3 average duration (us) of each step kernel from the committed
+    kernel-trace summary, or None if it is missing or the source changed."""
+    try:
+        avgs, src = {}, None
+        with open(KT_FILE) as f:
+            for line in f:
+                if line.startswith("kernel_source_sha256:"):
+                    src = line.split(":", 1)[1].strip()
+                elif line.startswith("| "):
+                    cells = [c.strip() for c in line.strip().strip("|").split("|")]
+                    for k in STEP_KERNELS:
+                        if cells[0].endswith(k):
+                            avgs[k] = float(cells[2])
+        if src != kernel_source_hash() or len(avgs) != len(STEP_KERNELS):
+            return None
+        return avgs
+    except (OSError, ValueError, IndexError):
         return None
 
 
@@ -161,8 +195,8 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, out_dir):
     """Turn rocprofv3 CSV output into the text summaries kept under profiles/."""
     src_hash = kernel_source_hash()
     kt = _csv_rows(kt_dir, "kernel_stats.csv")
-    lines = ["# rocprofv3 kernel-trace statistics: bench.py default run (SSQ twin GEMV 17408x5120 + verify,",
-             "# then Q8 multi-stream GEMV 17408x5120 at N=1,2,4), one MI355X",
+    lines = ["# rocprofv3 kernel-trace statistics: bench.py default run (fused SSQ twin GEMV 17408x5120 + verify,",
+             "# the unfused GEMV and verify, then Q8 multi-stream GEMV 17408x5120 at N=1,2,4), one MI355X",
              "", "command: " + PROFILE_CMDS["kt"], "summary: " + PROFILE_CMDS["summary"],
              "kernel_source_sha256: " + src_hash, "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
@@ -191,22 +225,26 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, out_dir):
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         acc = per_kernel(d, counter)
-        gname, g_kib, g_n = pick(acc, lambda k: "gemv" in k)  # the PMC runs launch only the SSQ GEMV
+        # the PMC runs launch only the step's kernels (and the calibration copy)
+        steps = [pick(acc, lambda k, sk=sk: k.endswith(sk)) for sk in STEP_KERNELS]
         cname, c_kib, c_n = pick(acc, lambda k: "neg_kernel" in k or "neg" in k.lower())
         factor = CALIB_BYTES / 1024.0 / c_kib
-        out[counter] = dict(gname=gname, g_kib=g_kib, g_n=g_n, cname=cname, c_kib=c_kib, c_n=c_n, factor=factor,
+        g_kib = sum(k for _, k, _ in steps)
+        out[counter] = dict(steps=steps, g_kib=g_kib, cname=cname, c_kib=c_kib, c_n=c_n, factor=factor,
                             bytes=int(round(g_kib * 1024 * factor)))
-    algo = ROWS * (COLS // 32) * 68 + 2 * COLS * 4 + 2 * ROWS * 4
+    algo = step_algo_bytes()
     fb, wb = out["FETCH_SIZE"]["bytes"], out["WRITE_SIZE"]["bytes"]
-    lines = ["# HBM traffic of the SSQ twin GEMV (17408x5120), rocprofv3 PMC counters, one MI355X",
+    lines = ["# HBM traffic of the fused SSQ twin GEMV + verify (17408x5120; both kernels of one call),",
+             "# rocprofv3 PMC counters, one MI355X",
              "# Each counter is scaled by the ratio of known bytes to the counter's reading for torch.neg",
              "# over 256 MiB (reads 256 MiB, writes 256 MiB) in the same run.",
              "", "command_fetch: " + PROFILE_CMDS["fetch"], "command_write: " + PROFILE_CMDS["write"],
              "summary: " + PROFILE_CMDS["summary"], ""]
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         o = out[counter]
-        lines += [f"| {counter} | kernel | dispatches | avg KiB/dispatch |", "|---|---|---|---|",
-                  f"| | {o['gname']} | {o['g_n']} | {o['g_kib']:.1f} |",
+        lines += [f"| {counter} | kernel | dispatches | avg KiB/dispatch |", "|---|---|---|---|"]
+        lines += [f"| | {n} | {cnt} | {kib:.1f} |" for n, kib, cnt in o["steps"]]
+        lines += [f"| | step total | | {o['g_kib']:.1f} |",
                   f"| | {o['cname'][:90]} (calibration, {CALIB_BYTES} B) | {o['c_n']} | {o['c_kib']:.1f} |",
                   f"calibration factor {counter}: {o['factor']:.4f}", ""]
     lines += [f"algorithmic_bytes_per_launch: {algo}",
@@ -223,10 +261,11 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only-main", action="store_true", help="time the SSQ step only (profiling runs)")
+    ap.add_argument("--only-main", action="store_true",
+                    help="time the fused SSQ step only, no other kernels (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 3 elementwise copies of 256 MiB (reference kernel for HBM byte counters)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -265,6 +304,7 @@ def main():
     tok = torch.zeros(2, dtype=torch.int32, device=dev)
     am = torch.empty(2, dtype=torch.int32, device=dev)
     acc = torch.empty(1, dtype=torch.int32, device=dev)
+    work = pti.ssq_verify_workspace(dev)
     L = pti.lib()
     sp = pti._stream(stream)
 
@@ -280,8 +320,11 @@ def main():
             pti._check("pti_verify_argmax", st)
 
     def step(i):
-        gemv(i)
-        verify(i)
+        st = L.pti_gemv_ssq_verify(ws[i % n_copies].data_ptr(), xa.data_ptr(), xb.data_ptr(), ya.data_ptr(),
+                                   yb.data_ptr(), ROWS, COLS, tok.data_ptr(), am.data_ptr(), acc.data_ptr(),
+                                   work.data_ptr(), work.numel(), sp)
+        if st:
+            pti._check("pti_gemv_ssq_verify", st)
 
     if args.copy_calibration:
         # torch.neg: an elementwise kernel that reads and writes 256 MiB each
@@ -299,20 +342,28 @@ def main():
     ms_step = timed_loop(torch, step, args.steps, stream)
     log(f"step: {ms_step * 1e3:.2f} us")
 
-    gemv_algo_bytes = w_bytes + 2 * COLS * 4 + 2 * ROWS * 4
-    st_gemv = timed_stats(torch, gemv, stream)
-    st_verify = timed_stats(torch, verify, stream)
-    ms_gemv = st_gemv["median_us"] * 1e-3
-    ms_verify = st_verify["median_us"] * 1e-3
-    log(f"ssq gemv alone: {st_gemv}; verify alone {st_verify}")
-
-    # device-to-device copy of the same byte count, rotated the same way: the
-    # practical ceiling (reads and writes w_bytes each)
-    dsts = [torch.empty_like(w0) for _ in range(2)]
-    st_copy = timed_stats(torch, lambda i: dsts[i % 2].copy_(ws[i % n_copies]), stream)
-    copy_GBps = 2 * w_bytes / (st_copy["median_us"] * 1e-6) / 1e9
-    del dsts
-    log(f"copy {w_bytes} B: {st_copy}, {copy_GBps:.0f} GB/s read+write")
+    algo_bytes = step_algo_bytes()
+    assert algo_bytes - w_bytes == 2 * COLS * 4 + 2 * ROWS * 4 + 20
+    st_fused = timed_stats(torch, step, stream)
+    ms_fused = st_fused["median_us"] * 1e-3
+    log(f"fused gemv+verify: {st_fused}")
+    per_kernel = {}
+    copy_GBps = None
+    if not args.only_main:
+        st_gemv = timed_stats(torch, gemv, stream)
+        st_verify = timed_stats(torch, verify, stream)
+        ms_gemv = st_gemv["median_us"] * 1e-3
+        log(f"unfused: ssq gemv alone {st_gemv}; verify alone {st_verify}")
+        per_kernel["ssq_twin_gemv_unfused"] = {**st_gemv,
+                                               "weight_GBps": round(w_bytes / (ms_gemv * 1e-3) / 1e9, 2)}
+        per_kernel["verify_n2_v17408_unfused"] = st_verify
+        # device-to-device copy of the same byte count, rotated the same way:
+        # the practical ceiling (reads and writes w_bytes each)
+        dsts = [torch.empty_like(w0) for _ in range(2)]
+        st_copy = timed_stats(torch, lambda i: dsts[i % 2].copy_(ws[i % n_copies]), stream)
+        copy_GBps = 2 * w_bytes / (st_copy["median_us"] * 1e-6) / 1e9
+        del dsts
+        log(f"copy {w_bytes} B: {st_copy}, {copy_GBps:.0f} GB/s read+write")
 
     traffic = read_traffic()
     result = {
@@ -329,7 +380,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "ssq_twin_gemv_17408x5120+greedy_verify",
+            "workload": "ssq_twin_gemv_17408x5120+greedy_verify (fused)",
             "rows": ROWS, "cols": COLS, "format": "SSQ mode-16 (68 B blocks), int8 twins, f16 block scales",
             "streams": 2, "seed": synth.SEED_SSQ_FFN, "weight_copies_rotated": n_copies,
             "rotated_bytes": n_copies * w_bytes, "device": torch.cuda.get_device_name(0),
@@ -338,24 +389,23 @@ def main():
         "frac_of_hbm_peak": round(w_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemv_split_kernel<SSQ> (pti_gemv_ssq)",
-            "achieved": round(gemv_algo_bytes / (ms_gemv * 1e-3) / 1e9, 2),
+            "kernel": "pti_gemv_ssq_verify = gemv_ssq_split_kernel<5, true> + verify_keys_kernel",
+            "achieved": round(algo_bytes / (ms_fused * 1e-3) / 1e9, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(gemv_algo_bytes / (ms_gemv * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "frac": round(algo_bytes / (ms_fused * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": traffic["bytes"] if traffic else None,
-            "algorithmic_bytes_per_launch": gemv_algo_bytes,
-            "avg_launch_us": round(ms_gemv * 1e3, 3),
-            "launch_us_stats": st_gemv,
+            "algorithmic_bytes_per_launch": algo_bytes,
+            "avg_launch_us": round(ms_fused * 1e3, 3),
+            "launch_us_stats": st_fused,
             "traffic_source": traffic["source"] if traffic else None,
-            "vs_copy": round(gemv_algo_bytes / (ms_gemv * 1e-3) / 1e9 / copy_GBps, 4),
+            "vs_copy": round(algo_bytes / (ms_fused * 1e-3) / 1e9 / copy_GBps, 4) if copy_GBps else None,
+            "rocprof_avg_us": read_kernel_avgs(),
+            "rocprof_source": os.path.relpath(KT_FILE, HERE),
         },
-        "copy_ceiling": {"GBps_read_plus_write": round(copy_GBps, 1), "bytes_each_way": w_bytes, **st_copy},
     }
-    per_kernel = {"ssq_twin_gemv": {"us": round(ms_gemv * 1e3, 3), **st_gemv,
-                                    "weight_GBps": round(w_bytes / (ms_gemv * 1e-3) / 1e9, 2),
-                                    "gemv_per_s": round(1 / (ms_gemv * 1e-3), 1)},
-                  "verify_n2_v17408": {"us": round(ms_verify * 1e3, 3), **st_verify}}
+    if copy_GBps:
+        result["copy_ceiling"] = {"GBps_read_plus_write": round(copy_GBps, 1), "bytes_each_way": w_bytes, **st_copy}
     del ws, w0
     torch.cuda.empty_cache()
 

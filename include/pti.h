@@ -73,6 +73,7 @@ extern "C" {
 #define PTI_MAX_COLS (1LL << 24)
 #define PTI_MAX_VOCAB 2147483647LL
 #define PTI_MAX_ELEMS (1LL << 40)  /* element count limit of the elementwise and norm calls */
+#define PTI_SSQ_VERIFY_WORK_BYTES 16384  /* workspace of pti_gemv_ssq_verify */
 
 enum pti_status {
     PTI_OK = 0,
@@ -139,6 +140,28 @@ int pti_ssq_join(const uint8_t *q8_a, const uint8_t *q8_b, int64_t rows, int64_t
  * y_a, y_b: device fp32 [rows], distinct, not overlapping any input. */
 int pti_gemv_ssq(const void *w_ssq, const float *x_a, const float *x_b, float *y_a, float *y_b,
                  int64_t rows, int64_t cols, void *stream);
+
+/* SSQ twin GEMV fused with the greedy verify of its two outputs [README,
+ * relation to SSQ; README, how acceptance works]: the results of
+ * pti_gemv_ssq (y_a, y_b bitwise the same) and those of pti_verify_argmax
+ * over the streams (y_a, y_b) with vocab = rows, without a second pass over
+ * y: argmax_out[0] = argmax y_a, argmax_out[1] = argmax y_b (lowest index wins
+ * a tie; -0 equals +0; NaN ordering unspecified), accept_out[0] = 1 +
+ * (tokens_in[1] == argmax_out[0]).  For the twin decode rows is the
+ * vocabulary and y_a, y_b are the twins' logits; tokens_in[1] is the guess
+ * twin B ran on, tokens_in[0] is not read.  The GEMV's workgroups keep the
+ * largest output each; a one-workgroup kernel enqueued after it on the same
+ * stream reduces those.
+ * Arguments as in pti_gemv_ssq, plus: tokens_in: device int32 [2];
+ * argmax_out: device int32 [2]; accept_out: device int32 [1] (4-byte aligned);
+ * work: device scratch of at least PTI_SSQ_VERIFY_WORK_BYTES bytes, 16-byte
+ * aligned, caller-owned, any contents (overwritten; calls that may run at the
+ * same time need separate workspaces); work_bytes below
+ * PTI_SSQ_VERIFY_WORK_BYTES gives PTI_ERR_SHAPE.  No output (y_a, y_b,
+ * argmax_out, accept_out, work) may overlap an input or another output. */
+int pti_gemv_ssq_verify(const void *w_ssq, const float *x_a, const float *x_b, float *y_a, float *y_b,
+                        int64_t rows, int64_t cols, const int32_t *tokens_in, int32_t *argmax_out,
+                        int32_t *accept_out, void *work, size_t work_bytes, void *stream);
 
 /* Q8 multi-stream GEMV [README, bandwidth analysis: one weight read serves the
  * activation vectors of all streams]:

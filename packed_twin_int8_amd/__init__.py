@@ -39,7 +39,7 @@ STATUS = {0: "PTI_OK", -1: "PTI_ERR_NULL", -2: "PTI_ERR_SHAPE", -3: "PTI_ERR_NST
 EXPORTS = (
     "pti_status_str", "pti_last_hip_error", "pti_abi_version", "pti_ssq_bytes", "pti_q8_bytes", "pti_pack_ssq",
     "pti_unpack_ssq", "pti_pack_q8", "pti_unpack_q8", "pti_ssq_split", "pti_ssq_join", "pti_gemv_ssq",
-    "pti_gemv_q8_multi", "pti_verify_argmax", "pti_sample_verify", "pti_embed_q8", "pti_embed_ssq", "pti_rmsnorm",
+    "pti_gemv_ssq_verify", "pti_gemv_q8_multi", "pti_verify_argmax", "pti_sample_verify", "pti_embed_q8", "pti_embed_ssq", "pti_rmsnorm",
     "pti_silu_mul", "pti_add", "pti_toy_workspace_bytes", "pti_toy_forward", "pti_toy_decode",
 )
 
@@ -91,6 +91,7 @@ def lib() -> ctypes.CDLL:
         L.pti_ssq_split.argtypes = [_P, _I64, _I64, _P, _P]
         L.pti_ssq_join.argtypes = [_P, _P, _I64, _I64, _P]
         L.pti_gemv_ssq.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _P]
+        L.pti_gemv_ssq_verify.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.pti_gemv_q8_multi.argtypes = [_P, _P, _P, _I64, _I64, _INT, _P]
         L.pti_verify_argmax.argtypes = [_P, _P, _P, _P, _I64, _INT, _P]
         L.pti_sample_verify.argtypes = [_P, _P, _P, ctypes.c_double, _P, _P, _I64, _INT, _P]
@@ -241,6 +242,43 @@ def gemv_ssq(w, x_a, x_b, y_a=None, y_b=None, stream=None):
     _check("pti_gemv_ssq", lib().pti_gemv_ssq(w.data_ptr(), x_a.data_ptr(), x_b.data_ptr(), y_a.data_ptr(),
                                               y_b.data_ptr(), rows, cols, _stream(stream)))
     return y_a, y_b
+
+
+SSQ_VERIFY_WORK_BYTES = 16384  # PTI_SSQ_VERIFY_WORK_BYTES
+
+
+def ssq_verify_workspace(device):
+    """Scratch for gemv_ssq_verify (contents need no initialisation)."""
+    return _torch().empty(SSQ_VERIFY_WORK_BYTES, dtype=_torch().uint8, device=device)
+
+
+def gemv_ssq_verify(w, x_a, x_b, tokens_in, work, y_a=None, y_b=None, argmax_out=None, accept_out=None,
+                    stream=None):
+    """SSQ twin GEMV fused with the greedy verify of (y_a, y_b): returns
+    y_a, y_b, argmax_out [2] and accept_out [1].  tokens_in: int32 [2] (device;
+    entry 1 is the guess twin B ran on); work: from ssq_verify_workspace."""
+    torch = _torch()
+    _dev(w, "w", torch.uint8), _dev(x_a, "x_a", torch.float32), _dev(x_b, "x_b", torch.float32)
+    _dev(tokens_in, "tokens_in", torch.int32), _dev(work, "work", torch.uint8)
+    rows, cols = w.shape[0], x_a.shape[-1]
+    if w.dim() != 2 or w.shape[1] != cols // 32 * 68 or x_b.shape != x_a.shape or x_a.dim() != 1:
+        raise ValueError("gemv_ssq_verify: shape mismatch")
+    if tokens_in.numel() != 2:
+        raise ValueError("gemv_ssq_verify: tokens_in must have two entries")
+    dev = w.device
+    y_a = torch.empty(rows, dtype=torch.float32, device=dev) if y_a is None else _dev(y_a, "y_a", torch.float32)
+    y_b = torch.empty(rows, dtype=torch.float32, device=dev) if y_b is None else _dev(y_b, "y_b", torch.float32)
+    argmax_out = torch.empty(2, dtype=torch.int32, device=dev) if argmax_out is None else _dev(
+        argmax_out, "argmax_out", torch.int32)
+    accept_out = torch.empty(1, dtype=torch.int32, device=dev) if accept_out is None else _dev(
+        accept_out, "accept_out", torch.int32)
+    if y_a.numel() != rows or y_b.numel() != rows or argmax_out.numel() != 2 or accept_out.numel() != 1:
+        raise ValueError("gemv_ssq_verify: output shape mismatch")
+    _check("pti_gemv_ssq_verify", lib().pti_gemv_ssq_verify(
+        w.data_ptr(), x_a.data_ptr(), x_b.data_ptr(), y_a.data_ptr(), y_b.data_ptr(), rows, cols,
+        tokens_in.data_ptr(), argmax_out.data_ptr(), accept_out.data_ptr(), work.data_ptr(), work.numel(),
+        _stream(stream)))
+    return y_a, y_b, argmax_out, accept_out
 
 
 def gemv_q8_multi(w, x, y=None, stream=None):

@@ -368,7 +368,6 @@ struct Wave {
     // guarded.
     __device__ __forceinline__ void compute(const Unit (&buf)[R])
     {
-        const int nrows = cnrows;
         const float4 *xr = xs + ((cr - i0) * CG * NSP) * 64 + lane;
         uint32_t q[R][4];
         if constexpr (FMT == kQ8) {
@@ -725,13 +724,38 @@ constexpr int kSplitWavesBigT = 4;      // ... when T >= 3 (measured best)
 // Launch bound for T (the registers per wave follow from it).
 constexpr int split_bound_waves(int T) { return T >= 3 ? 8 : kSplitMaxWaves; }
 
+// Most workgroups of a row-split launch: one per CU, at most this many (the
+// fused verify's workspace holds one pair of keys per workgroup).
+constexpr int kSplitMaxGrid = 1024;
+static_assert(kSplitMaxGrid * 2 * 8 <= PTI_SSQ_VERIFY_WORK_BYTES, "workspace size");
+
 struct SplitArgs {
     GemvArgs g;
     int32_t P, Q;         // rows per step, waves per row
     int32_t S;            // steps per flush of finished rows
+    // fused greedy verify (VERIFY kernels only): per workgroup the largest
+    // key of each twin, keys[2 g + s]
+    unsigned long long *keys;
 };
 
-template <int T>
+// Key ordering (value, then lower row) as one unsigned 64-bit number: the
+// float's bits made monotonic (-0 counted as +0), then the row inverted.  The
+// largest key is the argmax with the lowest row among equals; no key is 0.
+__device__ __forceinline__ unsigned long long verify_key(float v, int64_t row)
+{
+    uint32_t u = __builtin_bit_cast(uint32_t, v == 0.f ? 0.f : v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)u << 32) | (0xFFFFFFFFu - (uint32_t)row);
+}
+
+// VERIFY: also the first half of the greedy verify of the two twins' outputs
+// -- each thread keeps the largest key of the rows it stores and each
+// workgroup stores the largest of its threads' (0 if it has no rows);
+// verify_keys_kernel, launched next on the same stream, reduces them.  (A
+// single kernel whose last workgroup reduces the keys needs a device-scope
+// release and acquire per workgroup to see the others' keys, and on this GPU
+// those cost more than the second launch.)
+template <int T, bool VERIFY>
 __global__ __launch_bounds__(64 * split_bound_waves(T)) void gemv_ssq_split_kernel(SplitArgs sa)
 {
     constexpr int UC = unit_cols<kSSQ>();
@@ -822,6 +846,8 @@ __global__ __launch_bounds__(64 * split_bound_waves(T)) void gemv_ssq_split_kern
         }
     };
 
+    unsigned long long vkey[2] = {0, 0};  // this thread's largest key per twin (VERIFY)
+
     // Sum the partials of the rows of steps [t0, t1) (in half `half`) in slice
     // order and store them.
     auto flush = [&](int t0, int t1, int half) {
@@ -841,6 +867,8 @@ __global__ __launch_bounds__(64 * split_bound_waves(T)) void gemv_ssq_split_kern
                 for (int j = 1; j < Q; j++)
                     acc += part[((slot * Q) + j) * 2 + s];
                 a.y[s][g + m * G] = acc;
+                if constexpr (VERIFY)
+                    vkey[s] = std::max(vkey[s], verify_key(acc, g + m * G));
             }
         // Stores count on the same counter as the weight loads.  Without this
         // wait the compiler cannot tell how many operations follow the
@@ -872,6 +900,63 @@ __global__ __launch_bounds__(64 * split_bound_waves(T)) void gemv_ssq_split_kern
         }
         flush(t0, t1, half);
     }
+
+    if constexpr (VERIFY) {
+        __shared__ unsigned long long wkey[2][kSplitMaxWaves];
+        const int nw = P * Q;
+#pragma unroll
+        for (int s = 0; s < 2; s++) {
+            unsigned long long k = vkey[s];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1)
+                k = std::max(k, __shfl_xor(k, off, 64));
+            if (lane == 0)
+                wkey[s][wv] = k;
+        }
+        __syncthreads();
+        if (tid < 2) {
+            unsigned long long k = wkey[tid][0];
+            for (int i = 1; i < nw; i++)
+                k = std::max(k, wkey[tid][i]);
+            sa.keys[2 * g + tid] = k;
+        }
+    }
+}
+
+// The rest of the fused verify: argmax of each twin from the workgroups' keys
+// (the largest key is the largest value, the lowest row among equals) and the
+// accept count of twin B's guess.  One workgroup of 256 threads.
+__global__ __launch_bounds__(256) void verify_keys_kernel(const unsigned long long *__restrict__ keys, int n_groups,
+                                                          const int32_t *__restrict__ tokens_in,
+                                                          int32_t *__restrict__ argmax_out,
+                                                          int32_t *__restrict__ accept_out)
+{
+    __shared__ unsigned long long part[2][4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    unsigned long long k[2] = {0, 0};
+    for (int i = tid; i < n_groups; i += 256) {
+        k[0] = std::max(k[0], keys[2 * i]);
+        k[1] = std::max(k[1], keys[2 * i + 1]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        k[0] = std::max(k[0], __shfl_xor(k[0], off, 64));
+        k[1] = std::max(k[1], __shfl_xor(k[1], off, 64));
+    }
+    if (lane == 0)
+        part[0][wv] = k[0], part[1][wv] = k[1];
+    __syncthreads();
+    if (tid == 0) {
+        int32_t am[2];
+#pragma unroll
+        for (int s = 0; s < 2; s++) {
+            const unsigned long long m =
+                std::max(std::max(part[s][0], part[s][1]), std::max(part[s][2], part[s][3]));
+            am[s] = (int32_t)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
+            argmax_out[s] = am[s];
+        }
+        accept_out[0] = 1 + (tokens_in[1] == am[0] ? 1 : 0);
+    }
 }
 
 // Rounds per wave for a row of `rounds` rounds: at most kSplitTMax, spread
@@ -901,22 +986,34 @@ bool split_shape(int rounds, int T, SplitArgs &sa)
 
 constexpr int kNotSplit = 1;  // the row-split kernel does not take this shape
 
-template <int T>
-int launch_ssq_split(const GemvArgs &a, hipStream_t stream)
+// Outputs of the fused verify (VERIFY launches only).
+struct VerifyOut {
+    unsigned long long *keys;  // workspace, 2 keys per workgroup
+    const int32_t *tokens_in;
+    int32_t *argmax_out, *accept_out;
+};
+
+template <int T, bool VERIFY>
+int launch_ssq_split(const GemvArgs &a, const VerifyOut *vo, hipStream_t stream)
 {
-    SplitArgs sa;
+    SplitArgs sa{};
     if (!split_shape(a.rounds, T, sa))
         return kNotSplit;
     sa.g = a;
+    if constexpr (VERIFY)
+        sa.keys = vo->keys;
     const int cus = device_cus();
     if (cus <= 0) {
         pti::set_hip_error(hipGetLastError());
         return PTI_ERR_HIP;
     }
-    const int64_t grid = std::min<int64_t>(cus, a.rows);
+    const int64_t grid = std::min<int64_t>(std::min(cus, kSplitMaxGrid), a.rows);
     const size_t lds = (size_t)2 * sa.S * sa.P * sa.Q * 2 * sizeof(float);
-    hipLaunchKernelGGL(gemv_ssq_split_kernel<T>, dim3((unsigned)grid), dim3((unsigned)(64 * sa.P * sa.Q)), lds,
-                       stream, sa);
+    hipLaunchKernelGGL((gemv_ssq_split_kernel<T, VERIFY>), dim3((unsigned)grid), dim3((unsigned)(64 * sa.P * sa.Q)),
+                       lds, stream, sa);
+    if constexpr (VERIFY)
+        hipLaunchKernelGGL(verify_keys_kernel, dim3(1), dim3(256), 0, stream, vo->keys, (int)grid, vo->tokens_in,
+                           vo->argmax_out, vo->accept_out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         pti::set_hip_error(e);
@@ -925,14 +1022,16 @@ int launch_ssq_split(const GemvArgs &a, hipStream_t stream)
     return PTI_OK;
 }
 
-int launch_ssq_split(const GemvArgs &a, hipStream_t stream)
+// vo: the verify outputs (VERIFY only, else null).
+template <bool VERIFY>
+int launch_ssq_split(const GemvArgs &a, const VerifyOut *vo, hipStream_t stream)
 {
     switch (split_T(a.rounds)) {
-    case 1: return launch_ssq_split<1>(a, stream);
-    case 2: return launch_ssq_split<2>(a, stream);
-    case 3: return launch_ssq_split<3>(a, stream);
-    case 4: return launch_ssq_split<4>(a, stream);
-    default: return launch_ssq_split<5>(a, stream);
+    case 1: return launch_ssq_split<1, VERIFY>(a, vo, stream);
+    case 2: return launch_ssq_split<2, VERIFY>(a, vo, stream);
+    case 3: return launch_ssq_split<3, VERIFY>(a, vo, stream);
+    case 4: return launch_ssq_split<4, VERIFY>(a, vo, stream);
+    default: return launch_ssq_split<5, VERIFY>(a, vo, stream);
     }
 }
 
@@ -959,10 +1058,54 @@ int pti_gemv_ssq(const void *w_ssq, const float *x_a, const float *x_b, float *y
     GemvArgs a = make_args<kSSQ>(w_ssq, rows, cols);
     a.x[0] = x_a, a.x[1] = x_b;
     a.y[0] = y_a, a.y[1] = y_b;
-    const int st = launch_ssq_split(a, static_cast<hipStream_t>(stream));
+    const int st = launch_ssq_split<false>(a, nullptr, static_cast<hipStream_t>(stream));
     if (st != kNotSplit)
         return st;
     return launch<kSSQ, 2, 2, true>(a, static_cast<hipStream_t>(stream));
+}
+
+int pti_gemv_ssq_verify(const void *w_ssq, const float *x_a, const float *x_b, float *y_a, float *y_b, int64_t rows,
+                        int64_t cols, const int32_t *tokens_in, int32_t *argmax_out, int32_t *accept_out, void *work,
+                        size_t work_bytes, void *stream)
+{
+    if (!w_ssq || !x_a || !x_b || !y_a || !y_b || !tokens_in || !argmax_out || !accept_out || !work)
+        return PTI_ERR_NULL;
+    if (!pti::shape_ok(rows, cols))
+        return PTI_ERR_SHAPE;
+    if (work_bytes < PTI_SSQ_VERIFY_WORK_BYTES)
+        return PTI_ERR_SHAPE;
+    if (!pti::aligned(w_ssq, 4) || !pti::aligned(x_a, 16) || !pti::aligned(x_b, 16) || !pti::aligned(y_a, 4) ||
+        !pti::aligned(y_b, 4) || !pti::aligned(tokens_in, 4) || !pti::aligned(argmax_out, 4) ||
+        !pti::aligned(accept_out, 4) || !pti::aligned(work, 16))
+        return PTI_ERR_ALIGN;
+    const size_t wn = pti_ssq_bytes(rows, cols), xn = size_t(cols) * 4, yn = size_t(rows) * 4;
+    // every output against every other output and every input
+    const pti::Range outs[] = {{y_a, yn}, {y_b, yn}, {argmax_out, 8}, {accept_out, 4},
+                               {work, PTI_SSQ_VERIFY_WORK_BYTES}};
+    const pti::Range ins[] = {{w_ssq, wn}, {x_a, xn}, {x_b, xn}, {tokens_in, 8}};
+    for (size_t i = 0; i < sizeof outs / sizeof outs[0]; i++) {
+        for (size_t j = i + 1; j < sizeof outs / sizeof outs[0]; j++)
+            if (pti::overlap(outs[i], outs[j]))
+                return PTI_ERR_OVERLAP;
+        for (const pti::Range &in : ins)
+            if (pti::overlap(outs[i], in))
+                return PTI_ERR_OVERLAP;
+    }
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    GemvArgs a = make_args<kSSQ>(w_ssq, rows, cols);
+    a.x[0] = x_a, a.x[1] = x_b;
+    a.y[0] = y_a, a.y[1] = y_b;
+    const VerifyOut vo{static_cast<unsigned long long *>(work), tokens_in, argmax_out, accept_out};
+    const int rc = launch_ssq_split<true>(a, &vo, st);
+    if (rc != kNotSplit)
+        return rc;
+    // shapes the row-split kernel does not take: GEMV, then the verify kernel
+    const int g = launch<kSSQ, 2, 2, true>(a, st);
+    if (g != PTI_OK)
+        return g;
+    pti::StreamRows lg{};
+    lg.p[0] = y_a, lg.p[1] = y_b;
+    return pti::launch_verify_rows(lg, tokens_in, argmax_out, accept_out, rows, 2, stream);
 }
 
 int pti_gemv_q8_multi(const void *w_q8, const float *x, float *y, int64_t rows, int64_t cols, int n_streams,

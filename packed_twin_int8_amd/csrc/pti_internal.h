@@ -25,6 +25,16 @@ struct Range {
     size_t n;
 };
 
+// The rows of up to PTI_MAX_STREAMS streams (one pointer each).
+struct StreamRows {
+    const float *p[PTI_MAX_STREAMS];
+};
+
+// Greedy verify over streams whose logits need not be contiguous; arguments
+// already validated by the caller.  Enqueues on `stream`.
+int launch_verify_rows(const StreamRows &lg, const int32_t *tokens_in, int32_t *argmax_out, int32_t *accept_out,
+                       int64_t vocab, int n_streams, void *stream);
+
 inline bool overlap(Range a, Range b)
 {
     if (a.n == 0 || b.n == 0)

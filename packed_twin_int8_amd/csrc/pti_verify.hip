@@ -52,7 +52,7 @@ __device__ __forceinline__ Best wave_best(Best b)
 // slice of every stream, with UNROLL independent 16-byte loads per stream in
 // flight; slices combine with better() across the wave, then across waves.
 template <bool VEC4, int NS>
-__global__ __launch_bounds__(kThreads) void verify_kernel(const float *__restrict__ logits,
+__global__ __launch_bounds__(kThreads) void verify_kernel(const pti::StreamRows logits,
                                                           const int32_t *__restrict__ tokens_in,
                                                           int32_t *__restrict__ argmax_out,
                                                           int32_t *__restrict__ accept_out, int64_t vocab)
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const float *__restric
             for (int s = 0; s < NS; s++)
 #pragma unroll
                 for (int u = 0; u < UNROLL; u++)
-                    t[s][u] = reinterpret_cast<const float4 *>(logits + (int64_t)s * vocab)[k + u * kThreads];
+                    t[s][u] = reinterpret_cast<const float4 *>(logits.p[s])[k + u * kThreads];
 #pragma unroll
             for (int u = 0; u < UNROLL; u++) {
                 const int i0 = (int)(4 * (k + u * kThreads));
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const float *__restric
             const int i0 = (int)(4 * k);
 #pragma unroll
             for (int s = 0; s < NS; s++) {
-                const float4 t = reinterpret_cast<const float4 *>(logits + (int64_t)s * vocab)[k];
+                const float4 t = reinterpret_cast<const float4 *>(logits.p[s])[k];
                 take(b[s], t.x, i0);
                 take(b[s], t.y, i0 + 1);
                 take(b[s], t.z, i0 + 2);
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const float *__restric
         for (int64_t k = tid; k < vocab; k += kThreads)
 #pragma unroll
             for (int s = 0; s < NS; s++)
-                take(b[s], logits[(int64_t)s * vocab + k], (int)k);
+                take(b[s], logits.p[s][k], (int)k);
     }
 #pragma unroll
     for (int s = 0; s < NS; s++) {
@@ -141,24 +141,24 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const float *__restric
 }
 
 template <bool VEC4>
-void launch_verify(const float *logits, const int32_t *tokens_in, int32_t *argmax_out, int32_t *accept_out,
+void launch_verify(const pti::StreamRows &lg, const int32_t *tokens_in, int32_t *argmax_out, int32_t *accept_out,
                    int64_t vocab, int n, hipStream_t st)
 {
     switch (n) {
     case 1:
-        hipLaunchKernelGGL((verify_kernel<VEC4, 1>), dim3(1), dim3(kThreads), 0, st, logits, tokens_in, argmax_out,
+        hipLaunchKernelGGL((verify_kernel<VEC4, 1>), dim3(1), dim3(kThreads), 0, st, lg, tokens_in, argmax_out,
                            accept_out, vocab);
         break;
     case 2:
-        hipLaunchKernelGGL((verify_kernel<VEC4, 2>), dim3(1), dim3(kThreads), 0, st, logits, tokens_in, argmax_out,
+        hipLaunchKernelGGL((verify_kernel<VEC4, 2>), dim3(1), dim3(kThreads), 0, st, lg, tokens_in, argmax_out,
                            accept_out, vocab);
         break;
     case 3:
-        hipLaunchKernelGGL((verify_kernel<VEC4, 3>), dim3(1), dim3(kThreads), 0, st, logits, tokens_in, argmax_out,
+        hipLaunchKernelGGL((verify_kernel<VEC4, 3>), dim3(1), dim3(kThreads), 0, st, lg, tokens_in, argmax_out,
                            accept_out, vocab);
         break;
     default:
-        hipLaunchKernelGGL((verify_kernel<VEC4, 4>), dim3(1), dim3(kThreads), 0, st, logits, tokens_in, argmax_out,
+        hipLaunchKernelGGL((verify_kernel<VEC4, 4>), dim3(1), dim3(kThreads), 0, st, lg, tokens_in, argmax_out,
                            accept_out, vocab);
         break;
     }
@@ -182,16 +182,29 @@ extern "C" int pti_verify_argmax(const float *logits, const int32_t *tokens_in, 
         A{argmax_out, size_t(n_streams) * 4}, C{accept_out, 4};
     if (pti::overlap(A, L) || pti::overlap(A, T) || pti::overlap(C, L) || pti::overlap(C, T) || pti::overlap(A, C))
         return PTI_ERR_OVERLAP;
+    pti::StreamRows lg{};
+    for (int s = 0; s < n_streams; s++)
+        lg.p[s] = logits + (int64_t)s * vocab;
+    return pti::launch_verify_rows(lg, tokens_in, argmax_out, accept_out, vocab, n_streams, stream);
+}
+
+namespace pti {
+int launch_verify_rows(const StreamRows &lg, const int32_t *tokens_in, int32_t *argmax_out, int32_t *accept_out,
+                       int64_t vocab, int n_streams, void *stream)
+{
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const bool vec4 = vocab % 4 == 0 && pti::aligned(logits, 16);
+    bool vec4 = vocab % 4 == 0;
+    for (int s = 0; s < n_streams; s++)
+        vec4 = vec4 && aligned(lg.p[s], 16);
     if (vec4)
-        launch_verify<true>(logits, tokens_in, argmax_out, accept_out, vocab, n_streams, st);
+        launch_verify<true>(lg, tokens_in, argmax_out, accept_out, vocab, n_streams, st);
     else
-        launch_verify<false>(logits, tokens_in, argmax_out, accept_out, vocab, n_streams, st);
+        launch_verify<false>(lg, tokens_in, argmax_out, accept_out, vocab, n_streams, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
-        pti::set_hip_error(e);
+        set_hip_error(e);
         return PTI_ERR_HIP;
     }
     return PTI_OK;
 }
+}  // namespace pti

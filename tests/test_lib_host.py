@@ -135,6 +135,33 @@ def test_gemv_ssq_errors():
     assert f(_fake(A0), _fake(A1), _fake(A4), _fake(A2), _fake(A4 + 8), 8, 64, None) == OVERLAP
 
 
+def test_gemv_ssq_verify_errors():
+    L = pti.lib()
+    f = L.pti_gemv_ssq_verify
+    T, AM, AC, WK = 0x60000000, 0x61000000, 0x62000000, 0x63000000
+    W = pti.SSQ_VERIFY_WORK_BYTES
+
+    def call(w=A0, xa=A1, xb=A1, ya=A2, yb=A3, rows=8, cols=64, t=T, am=AM, ac=AC, wk=WK, wb=W):
+        return f(_fake(w) if w else None, _fake(xa) if xa else None, _fake(xb), _fake(ya), _fake(yb), rows, cols,
+                 _fake(t) if t else None, _fake(am) if am else None, _fake(ac) if ac else None,
+                 _fake(wk) if wk else None, wb, None)
+
+    for k in ("w", "xa", "t", "am", "ac", "wk"):
+        assert call(**{k: 0}) == NULL, k
+    assert call(rows=0) == SHAPE
+    assert call(cols=48) == SHAPE
+    assert call(wb=W - 1) == SHAPE        # workspace too small
+    assert call(wk=WK + 8) == ALIGN       # workspace needs 16-byte alignment
+    assert call(am=AM + 2) == ALIGN
+    assert call(xa=A1 + 4) == ALIGN
+    # argmax_out overlaps accept_out; work overlaps y_a; accept_out overlaps
+    # tokens_in; y_b overlaps w
+    assert call(ac=AM + 4) == OVERLAP
+    assert call(wk=A2 - 1024) == OVERLAP
+    assert call(ac=T + 4) == OVERLAP
+    assert call(yb=A0 + 128) == OVERLAP
+
+
 def test_gemv_q8_errors():
     L = pti.lib()
     f = L.pti_gemv_q8_multi
