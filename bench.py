@@ -20,7 +20,9 @@ Also reported on the same JSON line:
   * per_kernel: the unfused pair (pti_gemv_ssq, then pti_verify_argmax), and
     the Q8 multi-stream GEMV over 17408 x 5120 at N = 1, 2, 4 streams
     (effective weight GB/s, GEMV/s, and t(N=4)/t(N=1)), each with median /
-    p10 / p90 over 10 runs;
+    p10 / p90 over 10 runs; a decoder layer's seven GEMVs separate, grouped
+    and grouped in a graph; the toy decoder's forward pass eager and as a
+    graph;
   * cpu_baseline: the fp64 oracle (scalar C, one host core) running the same
     SSQ GEMV, timed on a bounded number of passes.
 
@@ -257,6 +259,98 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, out_dir):
     print("\n".join(lines))
 
 
+def layer_and_graph(torch, pti, dev, stream):
+    """A decoder layer's GEMVs at their real shapes (q, k, v, o, gate, up,
+    down; random packed weights, valid f16 scales): seven separate launches,
+    four grouped launches (q|k|v, o, gate|up, down), and the grouped launches
+    replayed from a captured graph.  Then the toy decoder's forward pass (Q8,
+    four streams), eager against its native graph."""
+    import synth
+    out = {}
+    shapes = {name: (r, c) for name, r, c in synth.LAYER_SHAPES}
+
+    def packed(rows, cols, block):
+        w = torch.randint(0, 256, (rows, cols // 32, block), dtype=torch.uint8, device=dev)
+        w[:, :, 0] = 0x00
+        w[:, :, 1] = 0x20  # f16 2^-7 in every scale slot
+        if block == 68:
+            w[:, :, 2] = 0x00
+            w[:, :, 3] = 0x20
+        return w.view(rows, -1)
+
+    for fmt, block in (("q8", 34), ("ssq", 68)):
+        W = {k: packed(*shapes[k], block) for k in shapes}
+        wbytes = sum(t.numel() for t in W.values())
+        for n in ((1, 4) if fmt == "q8" else (2,)):
+            x5 = torch.randn((n, 5120), device=dev)
+            x17 = torch.randn((n, 17408), device=dev)
+            y = {k: torch.empty((n, shapes[k][0]), device=dev) for k in shapes}
+            yqkv = torch.empty((n, 7168), device=dev)
+            ygu = torch.empty((n, 34816), device=dev)
+            if fmt == "q8":
+                # launches go to the current stream: the bench stream, or the
+                # capture stream inside torch.cuda.graph
+                def one(k, x):
+                    pti.gemv_q8_multi(W[k], x, y[k])
+
+                def grp(ks, x, yy):
+                    pti.gemv_q8_multi_grouped([W[k] for k in ks], x, yy)
+            else:
+                def one(k, x):
+                    pti.gemv_ssq(W[k], x[0], x[1], y[k][0], y[k][1])
+
+                def grp(ks, x, yy):
+                    pti.gemv_ssq_grouped([W[k] for k in ks], x[0], x[1], yy[0], yy[1])
+
+            def separate(i):
+                for k in ("q", "k", "v", "o", "gate", "up"):
+                    one(k, x5)
+                one("down", x17)
+
+            def grouped(i):
+                grp(("q", "k", "v"), x5, yqkv)
+                one("o", x5)
+                grp(("gate", "up"), x5, ygu)
+                one("down", x17)
+
+            st_sep = timed_stats(torch, separate, stream, reps=5, per_rep=50, warmup=10)
+            st_grp = timed_stats(torch, grouped, stream, reps=5, per_rep=50, warmup=10)
+            g = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                grouped(0)
+            st_graph = timed_stats(torch, lambda i: g.replay(), stream, reps=5, per_rep=50, warmup=10)
+            key = f"layer_{fmt}_n{n}"
+            out[key] = {"weight_bytes": wbytes, "separate_us": st_sep["median_us"], "grouped_us": st_grp["median_us"],
+                        "graph_us": st_graph["median_us"],
+                        "graph_weight_GBps": round(wbytes / (st_graph["median_us"] * 1e-6) / 1e9, 1)}
+            log(f"{key}: {out[key]}")
+            del g
+        del W
+        torch.cuda.empty_cache()
+
+    # toy decoder forward pass (hidden 2048, ffn 5632, 4 layers, vocab 32000), Q8, N = 4
+    raw = synth.toy_weights(synth.SEED_TOY)
+    q = lambda m: torch.from_numpy(pti.pack_q8(m["Q"], m["S"])).to(dev)
+    mats = {"emb": q(raw["emb"]), "head": q(raw["head"]), "gate": [q(l["gate"]) for l in raw["layers"]],
+            "up": [q(l["up"]) for l in raw["layers"]], "down": [q(l["down"]) for l in raw["layers"]]}
+    stack = pti.ToyStack(mats, 2048, 5632, 32000, pti.FMT_Q8, 1e-6)
+    toks = torch.tensor([1, 2, 3, 4], dtype=torch.int32, device=dev)
+    logits = torch.empty((4, 32000), device=dev)
+    work = stack.workspace(4)
+    st_eager = timed_stats(torch, lambda i: stack.forward(toks, logits, work, stream=stream), stream, reps=5,
+                           per_rep=50, warmup=10)
+    graph = stack.forward_graph(toks, logits, work)
+    st_g = timed_stats(torch, lambda i: graph.launch(stream=stream), stream, reps=5, per_rep=50, warmup=10)
+    graph.destroy()
+    wbytes = sum(t.numel() for t in [mats["head"]] + mats["gate"] + mats["up"] + mats["down"])
+    out["toy_forward_q8_n4"] = {"eager_us": st_eager["median_us"], "graph_us": st_g["median_us"],
+                                "gemv_weight_bytes": wbytes,
+                                "graph_weight_GBps": round(wbytes / (st_g["median_us"] * 1e-6) / 1e9, 1)}
+    log(f"toy forward: {out['toy_forward_q8_n4']}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -437,6 +531,8 @@ def main():
             log(f"q8 n={n}: {t[n] * 1e3:.2f} us, {Pq.nbytes / (t[n] * 1e-3) / 1e9:.1f} GB/s")
         per_kernel["q8_step_cost_n4_over_n1"] = round(t[4] / t[1], 4)
         del wqs, wq0
+        torch.cuda.empty_cache()
+        per_kernel.update(layer_and_graph(torch, pti, dev, stream))
     result["per_kernel"] = per_kernel
 
     if not args.no_cpu:

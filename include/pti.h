@@ -69,6 +69,7 @@ extern "C" {
 #define PTI_SSQ_BLOCK_BYTES 68  /* [scale_A f16][scale_B f16][32 x uint16] */
 #define PTI_Q8_BLOCK_BYTES 34   /* [scale f16][32 x int8] */
 #define PTI_MAX_STREAMS 4
+#define PTI_MAX_GROUP 4         /* matrices per grouped GEMV launch */
 #define PTI_MAX_ROWS 2147483647LL
 #define PTI_MAX_COLS (1LL << 24)
 #define PTI_MAX_VOCAB 2147483647LL
@@ -172,6 +173,27 @@ int pti_gemv_ssq_verify(const void *w_ssq, const float *x_a, const float *x_b, f
  * 1 <= n_streams <= 4. */
 int pti_gemv_q8_multi(const void *w_q8, const float *x, float *y, int64_t rows, int64_t cols,
                       int n_streams, void *stream);
+
+/* Grouped GEMVs [README, bandwidth analysis: the per-token dispatch path is
+ * where the pages' own implementation lost its time]: n_mats matrices with
+ * the same column count and the same activations (q|k|v, gate|up) in one
+ * launch, as if their rows were stacked in order into one matrix of
+ * sum(rows) rows.  Every output is bitwise the one the single-matrix call
+ * gives for its matrix.
+ * w_ssq / w_q8: HOST array [n_mats] of device pointers, each 4-byte aligned,
+ * matrix m of rows[m] rows (HOST array [n_mats], each >= 1);
+ * 1 <= n_mats <= PTI_MAX_GROUP (else PTI_ERR_SHAPE), sum(rows) <=
+ * PTI_MAX_ROWS.  Outputs over the stacked rows: matrix m's rows start at
+ * row rows[0] + ... + rows[m-1].
+ *   pti_gemv_ssq_grouped: y_a, y_b: device fp32 [sum(rows)]; x_a, x_b as in
+ *     pti_gemv_ssq.
+ *   pti_gemv_q8_multi_grouped: y: device fp32 [n_streams][sum(rows)]
+ *     contiguous; x as in pti_gemv_q8_multi.
+ * No output may overlap a matrix, an activation vector or the other output. */
+int pti_gemv_ssq_grouped(const void *const *w_ssq, const int64_t *rows, int n_mats, const float *x_a,
+                         const float *x_b, float *y_a, float *y_b, int64_t cols, void *stream);
+int pti_gemv_q8_multi_grouped(const void *const *w_q8, const int64_t *rows, int n_mats, const float *x, float *y,
+                              int64_t cols, int n_streams, void *stream);
 
 /* Greedy verify [README, how acceptance works; Digest, implementation
  * architecture, step 3]: per stream n, argmax_out[n] = the index of the largest
@@ -279,6 +301,21 @@ size_t pti_toy_workspace_bytes(const pti_toy_model *m, int n_streams);
  * overlapping tokens or logits.  Enqueued on `stream`, no synchronisation. */
 int pti_toy_forward(const pti_toy_model *m, const int32_t *tokens, float *logits, void *work, size_t work_bytes,
                     int n_streams, void *stream);
+
+/* One pass of pti_toy_forward captured into an instantiated HIP graph
+ * [README, bandwidth analysis: the per-token dispatch path], so that a pass
+ * is one launch call however many kernels it has.  Arguments as in
+ * pti_toy_forward; the graph reads tokens and writes logits and work at
+ * these addresses on every replay (write new tokens into the same buffer).
+ * *graph_out: an opaque handle for pti_graph_launch (NULL on error); the
+ * caller owns it and frees it with pti_graph_destroy.  Nothing is enqueued
+ * or run by this call (the capture uses a private stream). */
+int pti_toy_forward_graph(const pti_toy_model *m, const int32_t *tokens, float *logits, void *work,
+                          size_t work_bytes, int n_streams, void **graph_out);
+/* Enqueue one replay of a graph on `stream`. */
+int pti_graph_launch(void *graph, void *stream);
+/* Free a graph handle (NULL is a no-op). */
+int pti_graph_destroy(void *graph);
 
 /* The staggered decode loop, n_steps steps after first_token.
  *   - Ramp-up (step 0): stream i >= 1 gets its first input from single-stream

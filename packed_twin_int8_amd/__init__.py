@@ -39,8 +39,9 @@ STATUS = {0: "PTI_OK", -1: "PTI_ERR_NULL", -2: "PTI_ERR_SHAPE", -3: "PTI_ERR_NST
 EXPORTS = (
     "pti_status_str", "pti_last_hip_error", "pti_abi_version", "pti_ssq_bytes", "pti_q8_bytes", "pti_pack_ssq",
     "pti_unpack_ssq", "pti_pack_q8", "pti_unpack_q8", "pti_ssq_split", "pti_ssq_join", "pti_gemv_ssq",
-    "pti_gemv_ssq_verify", "pti_gemv_q8_multi", "pti_verify_argmax", "pti_sample_verify", "pti_embed_q8", "pti_embed_ssq", "pti_rmsnorm",
+    "pti_gemv_ssq_verify", "pti_gemv_q8_multi", "pti_gemv_ssq_grouped", "pti_gemv_q8_multi_grouped", "pti_verify_argmax", "pti_sample_verify", "pti_embed_q8", "pti_embed_ssq", "pti_rmsnorm",
     "pti_silu_mul", "pti_add", "pti_toy_workspace_bytes", "pti_toy_forward", "pti_toy_decode",
+    "pti_toy_forward_graph", "pti_graph_launch", "pti_graph_destroy",
 )
 
 
@@ -93,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.pti_gemv_ssq.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _P]
         L.pti_gemv_ssq_verify.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.pti_gemv_q8_multi.argtypes = [_P, _P, _P, _I64, _I64, _INT, _P]
+        L.pti_gemv_ssq_grouped.argtypes = [_P, _P, _INT, _P, _P, _P, _P, _I64, _P]
+        L.pti_gemv_q8_multi_grouped.argtypes = [_P, _P, _INT, _P, _P, _I64, _INT, _P]
         L.pti_verify_argmax.argtypes = [_P, _P, _P, _P, _I64, _INT, _P]
         L.pti_sample_verify.argtypes = [_P, _P, _P, ctypes.c_double, _P, _P, _I64, _INT, _P]
         L.pti_embed_q8.argtypes = [_P, _P, _P, _I64, _I64, _INT, _P]
@@ -103,6 +106,10 @@ def lib() -> ctypes.CDLL:
         L.pti_toy_workspace_bytes.argtypes = [ctypes.POINTER(ToyModelC), _INT]
         L.pti_toy_workspace_bytes.restype = ctypes.c_size_t
         L.pti_toy_forward.argtypes = [ctypes.POINTER(ToyModelC), _P, _P, _P, ctypes.c_size_t, _INT, _P]
+        L.pti_toy_forward_graph.argtypes = [ctypes.POINTER(ToyModelC), _P, _P, _P, ctypes.c_size_t, _INT,
+                                            ctypes.POINTER(ctypes.c_void_p)]
+        L.pti_graph_launch.argtypes = [_P, _P]
+        L.pti_graph_destroy.argtypes = [_P]
         L.pti_toy_decode.argtypes = [ctypes.POINTER(ToyModelC), ctypes.c_int32, _INT, _INT, ctypes.c_double, _P, _P,
                                      ctypes.c_size_t, _P, _P, _P, ctypes.POINTER(ctypes.c_int64), _P]
         for name in EXPORTS:  # every declared symbol must resolve
@@ -300,6 +307,61 @@ def gemv_q8_multi(w, x, y=None, stream=None):
     return y
 
 
+def _group(ws, block_bytes, name):
+    """Host arrays of device pointers and row counts for a grouped launch."""
+    torch = _torch()
+    ws = list(ws)
+    if not ws:
+        raise ValueError(f"{name}: at least one matrix")
+    cols = ws[0].shape[1] // block_bytes * 32
+    for i, w in enumerate(ws):
+        _dev(w, f"w[{i}]", torch.uint8)
+        if w.dim() != 2 or w.shape[1] != cols // 32 * block_bytes:
+            raise ValueError(f"{name}: matrix {i} does not have {cols} columns")
+    ptrs = (ctypes.c_void_p * len(ws))(*[w.data_ptr() for w in ws])
+    rows = (ctypes.c_int64 * len(ws))(*[w.shape[0] for w in ws])
+    return ptrs, rows, sum(w.shape[0] for w in ws), cols
+
+
+def gemv_ssq_grouped(ws, x_a, x_b, y_a=None, y_b=None, stream=None):
+    """SSQ twin GEMV over several matrices with the same columns in one
+    launch; outputs over the stacked rows (matrix m's rows follow matrix
+    m-1's).  ws: list of uint8 [rows_m, cols/32*68]."""
+    torch = _torch()
+    _dev(x_a, "x_a", torch.float32), _dev(x_b, "x_b", torch.float32)
+    ptrs, rows, total, cols = _group(ws, 68, "gemv_ssq_grouped")
+    if x_a.dim() != 1 or x_a.shape[0] != cols or x_b.shape != x_a.shape:
+        raise ValueError("gemv_ssq_grouped: x shape mismatch")
+    dev = x_a.device
+    y_a = torch.empty(total, dtype=torch.float32, device=dev) if y_a is None else _dev(y_a, "y_a", torch.float32)
+    y_b = torch.empty(total, dtype=torch.float32, device=dev) if y_b is None else _dev(y_b, "y_b", torch.float32)
+    if y_a.numel() != total or y_b.numel() != total:
+        raise ValueError("gemv_ssq_grouped: output shape mismatch")
+    _check("pti_gemv_ssq_grouped", lib().pti_gemv_ssq_grouped(ptrs, rows, len(rows), x_a.data_ptr(), x_b.data_ptr(),
+                                                              y_a.data_ptr(), y_b.data_ptr(), cols, _stream(stream)))
+    return y_a, y_b
+
+
+def gemv_q8_multi_grouped(ws, x, y=None, stream=None):
+    """Q8 multi-stream GEMV over several matrices with the same columns in
+    one launch: y [N, sum(rows)], matrix m's rows following matrix m-1's.
+    ws: list of uint8 [rows_m, cols/32*34]; x: float32 [N, cols]."""
+    torch = _torch()
+    _dev(x, "x", torch.float32)
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    ptrs, rows, total, cols = _group(ws, 34, "gemv_q8_multi_grouped")
+    n = x.shape[0]
+    if x.shape[1] != cols:
+        raise ValueError("gemv_q8_multi_grouped: x shape mismatch")
+    y = torch.empty((n, total), dtype=torch.float32, device=x.device) if y is None else _dev(y, "y", torch.float32)
+    if y.numel() != n * total:
+        raise ValueError("gemv_q8_multi_grouped: output shape mismatch")
+    _check("pti_gemv_q8_multi_grouped", lib().pti_gemv_q8_multi_grouped(ptrs, rows, len(rows), x.data_ptr(),
+                                                                        y.data_ptr(), cols, n, _stream(stream)))
+    return y
+
+
 def verify_argmax(logits, tokens_in, argmax_out=None, accept_out=None, stream=None):
     """Greedy verify: argmax per stream and the accept count.
     logits: float32 [N, vocab]; tokens_in: int32 [N] (device)."""
@@ -405,6 +467,30 @@ def add(a, b, y=None, stream=None):
     return y
 
 
+class ForwardGraph:
+    """An instantiated HIP graph of one forward pass (pti_toy_forward_graph);
+    keeps the model and buffers it was captured over alive."""
+
+    def __init__(self, handle, keep):
+        self._h, self._keep = handle, keep
+
+    def launch(self, stream=None):
+        if not self._h:
+            raise RuntimeError("graph destroyed")
+        _check("pti_graph_launch", lib().pti_graph_launch(self._h, _stream(stream)))
+
+    def destroy(self):
+        if self._h:
+            _check("pti_graph_destroy", lib().pti_graph_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
 class ToyStack:
     """Device weights of the decoder stack plus the struct that names them.
 
@@ -456,6 +542,21 @@ class ToyStack:
         _check("pti_toy_forward", lib().pti_toy_forward(ctypes.byref(self.c), tokens.data_ptr(), logits.data_ptr(),
                                                         work.data_ptr(), work.numel(), n, _stream(stream)))
         return logits
+
+    def forward_graph(self, tokens, logits, work):
+        """One forward pass captured as a HIP graph over these buffers (the
+        tensors must stay alive while the graph is used); returns a
+        ForwardGraph whose launch() replays the pass."""
+        torch = _torch()
+        _dev(tokens, "tokens", torch.int32), _dev(logits, "logits", torch.float32), _dev(work, "work", torch.uint8)
+        n = tokens.numel()
+        if logits.numel() != n * self.vocab:
+            raise ValueError("forward_graph: logits must be [N, vocab]")
+        h = ctypes.c_void_p()
+        _check("pti_toy_forward_graph", lib().pti_toy_forward_graph(
+            ctypes.byref(self.c), tokens.data_ptr(), logits.data_ptr(), work.data_ptr(), work.numel(), n,
+            ctypes.byref(h)))
+        return ForwardGraph(h, (self, tokens, logits, work))
 
     def decode(self, first_token: int, n_streams: int, n_steps: int, temperature: float = 0.0, uniforms=None,
                work=None, stream=None):

@@ -90,8 +90,16 @@ enum Fmt { kQ8 = 0, kSSQ = 1 };
 template <int FMT>
 constexpr int unit_cols() { return FMT == kSSQ ? 8 : 16; }
 
+constexpr int kMaxSegs = PTI_MAX_GROUP;
+
+// The matrix of a launch: one packed matrix, or up to kMaxSegs of them with
+// the same column count stacked into one row space (a grouped launch).  Row
+// r lives in segment m (rows [seg_end[m-1], seg_end[m])) and starts at
+// seg_base[m] + r * row_bytes: seg_base[m] is segment m's pointer less its
+// first row's offset, so one formula serves every segment.
 struct GemvArgs {
-    const uint8_t *w;
+    uintptr_t seg_base[kMaxSegs];
+    int64_t seg_end[kMaxSegs];  // INT64_MAX from the last segment on
     const float *x[4];
     float *y[4];
     int64_t rows;
@@ -103,6 +111,16 @@ struct GemvArgs {
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Address of row `row` (wave-uniform in every caller, so this is scalar work).
+__device__ __forceinline__ const uint8_t *row_addr(const GemvArgs &a, int64_t row)
+{
+    uintptr_t b = a.seg_base[0];
+#pragma unroll
+    for (int m = 1; m < kMaxSegs; m++)
+        b = row >= a.seg_end[m - 1] ? a.seg_base[m] : b;
+    return reinterpret_cast<const uint8_t *>(b + (uintptr_t)row * (uintptr_t)a.row_bytes);
+}
 
 // Raw dwords of one unit of one row.
 //   SSQ: sc = [scale_A | scale_B << 16]; d[0..3] = the unit's 8 slots (slot
@@ -263,8 +281,6 @@ struct Wave {
     // Rows of this wave (wave-uniform): row(t) = first + t * stride, t < nrow.
     int64_t first, stride;
     int nrow, npass;
-    const uint8_t *wave_base;  // row first
-    int64_t row_step;          // bytes from one row of the wave to the next
     LaneOffsets lo;
     float acc[R][NS];
     float outv[NS];  // finished rows of the current group, row j of the group in lane j
@@ -289,8 +305,6 @@ struct Wave {
         : a(a_), xs(xs_), lane(lane_), first(first_), stride(stride_), nrow(nrow_)
     {
         npass = (nrow + R - 1) / R;
-        wave_base = a.w + first * a.row_bytes;
-        row_step = stride * a.row_bytes;
         lo = lane_offsets(lane_);
 #pragma unroll
         for (int r = 0; r < R; r++)
@@ -309,10 +323,9 @@ struct Wave {
     __device__ __forceinline__ void set_issue_pass(int p)
     {
         const int nr_in = p < p1 ? rows_in(p) : 0;
-        const uint8_t *base = wave_base + (int64_t)p * R * row_step;
 #pragma unroll
         for (int r = 0; r < R; r++) {
-            const uintptr_t q = reinterpret_cast<uintptr_t>(base + r * row_step);
+            const uintptr_t q = reinterpret_cast<uintptr_t>(row_addr(a, first + ((int64_t)p * R + r) * stride));
             const uint32_t e0 = (uint32_t)(q & 3);
             icls[r] = ROWS4 ? 0 : (int)(e0 >> 1);
             const uint32_t n = r < nr_in ? e0 + (uint32_t)a.row_bytes : 0u;
@@ -325,10 +338,10 @@ struct Wave {
     {
         cnrows = rows_in(p);
         if constexpr (!ROWS4) {
-            const uint8_t *base = wave_base + (int64_t)p * R * row_step;
 #pragma unroll
             for (int r = 0; r < R; r++)
-                ccls[r] = (int)((reinterpret_cast<uintptr_t>(base + r * row_step) >> 1) & 1);
+                ccls[r] = (int)((reinterpret_cast<uintptr_t>(row_addr(a, first + ((int64_t)p * R + r) * stride)) >> 1) &
+                                1);
         }
     }
 
@@ -685,7 +698,10 @@ template <int FMT>
 GemvArgs make_args(const void *w, int64_t rows, int64_t cols)
 {
     GemvArgs a{};
-    a.w = static_cast<const uint8_t *>(w);
+    for (int m = 0; m < kMaxSegs; m++) {
+        a.seg_base[m] = reinterpret_cast<uintptr_t>(w);
+        a.seg_end[m] = INT64_MAX;
+    }
     a.rows = rows;
     a.cols = (int32_t)cols;
     a.row_bytes = (cols / PTI_BLOCK) * (FMT == kSSQ ? PTI_SSQ_BLOCK_BYTES : PTI_Q8_BLOCK_BYTES);
@@ -789,16 +805,14 @@ __global__ __launch_bounds__(64 * split_bound_waves(T)) void gemv_ssq_split_kern
 
     const LaneOffsets lo = lane_offsets(lane);
     const int soff = q * T * (int)kRoundBytes;
-    const int64_t row_step = (int64_t)P * G * a.row_bytes;  // bytes from a wave's row to its next
-    const uint8_t *row0 = a.w + (g + (int64_t)p * G) * a.row_bytes;
-
     // Buffer resource over the row of step t (empty past the workgroup's rows:
     // its loads return zeros without touching memory).
     auto rsrc_for = [&](int t) {
         const int64_t m = (int64_t)t * P + p;  // row slot within the workgroup
-        const int n = m < wg_rows ? (int)a.row_bytes : 0;
-        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(m < wg_rows ? row0 + t * row_step : a.w),
-                                                 (short)0, n, 0x00020000);
+        const bool in = m < wg_rows;
+        const int n = in ? (int)a.row_bytes : 0;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(row_addr(a, in ? g + m * G : 0)), (short)0, n,
+                                                 0x00020000);
     };
     // Loads of round tt of this wave's slice.
     auto load_round = [&](__amdgpu_buffer_rsrc_t rs, int tt, Unit &u) {
@@ -1035,6 +1049,77 @@ int launch_ssq_split(const GemvArgs &a, const VerifyOut *vo, hipStream_t stream)
     }
 }
 
+// Kernel choice of each format: by shape alone, never by the stream count.
+int launch_q8(const GemvArgs &a, int n_streams, hipStream_t st)
+{
+    // rows start on dword boundaries when a row holds an even number of blocks
+    if ((a.cols / PTI_BLOCK) % 2 == 0) {
+        switch (n_streams) {
+        case 1: return launch<kQ8, 1, 1, true>(a, st);
+        case 2: return launch<kQ8, 2, 2, true>(a, st);
+        case 3: return launch<kQ8, 4, 3, true>(a, st);
+        default: return launch<kQ8, 4, 4, true>(a, st);
+        }
+    }
+    switch (n_streams) {
+    case 1: return launch<kQ8, 1, 1, false>(a, st);
+    case 2: return launch<kQ8, 2, 2, false>(a, st);
+    case 3: return launch<kQ8, 4, 3, false>(a, st);
+    default: return launch<kQ8, 4, 4, false>(a, st);
+    }
+}
+
+int launch_ssq(const GemvArgs &a, hipStream_t st)
+{
+    const int rc = launch_ssq_split<false>(a, nullptr, st);
+    if (rc != kNotSplit)
+        return rc;
+    return launch<kSSQ, 2, 2, true>(a, st);
+}
+
+// A grouped launch's matrices: validated, then stacked into one row space.
+// bytes(rows, cols): the packed size of one matrix.  Checks: host arrays
+// present, 1 <= n <= PTI_MAX_GROUP, every matrix present, 4-byte aligned,
+// 1 <= rows[m], and the stacked shape within the limits; the outputs must
+// not overlap any matrix.
+template <int FMT>
+int group_args(const void *const *w, const int64_t *rows, int n, int64_t cols, const pti::Range *outs, int n_outs,
+               GemvArgs &a)
+{
+    if (!w || !rows)
+        return PTI_ERR_NULL;
+    if (n < 1 || n > PTI_MAX_GROUP)
+        return PTI_ERR_SHAPE;
+    int64_t total = 0;
+    for (int m = 0; m < n; m++) {
+        if (!w[m])
+            return PTI_ERR_NULL;
+        if (rows[m] < 1 || rows[m] > PTI_MAX_ROWS - total)
+            return PTI_ERR_SHAPE;
+        total += rows[m];
+    }
+    if (!pti::shape_ok(total, cols))
+        return PTI_ERR_SHAPE;
+    for (int m = 0; m < n; m++) {
+        if (!pti::aligned(w[m], 4))
+            return PTI_ERR_ALIGN;
+        const size_t wn = FMT == kSSQ ? pti_ssq_bytes(rows[m], cols) : pti_q8_bytes(rows[m], cols);
+        for (int o = 0; o < n_outs; o++)
+            if (pti::overlap(outs[o], {w[m], wn}))
+                return PTI_ERR_OVERLAP;
+    }
+    a = make_args<FMT>(w[0], total, cols);
+    int64_t start = 0;
+    for (int m = 0; m < n; m++) {
+        a.seg_base[m] = reinterpret_cast<uintptr_t>(w[m]) - (uintptr_t)start * (uintptr_t)a.row_bytes;
+        start += rows[m];
+        a.seg_end[m] = m + 1 < n ? start : INT64_MAX;
+    }
+    for (int m = n; m < kMaxSegs; m++)
+        a.seg_base[m] = a.seg_base[n - 1], a.seg_end[m] = INT64_MAX;
+    return PTI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1058,10 +1143,31 @@ int pti_gemv_ssq(const void *w_ssq, const float *x_a, const float *x_b, float *y
     GemvArgs a = make_args<kSSQ>(w_ssq, rows, cols);
     a.x[0] = x_a, a.x[1] = x_b;
     a.y[0] = y_a, a.y[1] = y_b;
-    const int st = launch_ssq_split<false>(a, nullptr, static_cast<hipStream_t>(stream));
-    if (st != kNotSplit)
-        return st;
-    return launch<kSSQ, 2, 2, true>(a, static_cast<hipStream_t>(stream));
+    return launch_ssq(a, static_cast<hipStream_t>(stream));
+}
+
+int pti_gemv_ssq_grouped(const void *const *w_ssq, const int64_t *rows, int n_mats, const float *x_a,
+                         const float *x_b, float *y_a, float *y_b, int64_t cols, void *stream)
+{
+    if (!x_a || !x_b || !y_a || !y_b)
+        return PTI_ERR_NULL;
+    int64_t total = 0;
+    for (int m = 0; rows && m < n_mats && m < PTI_MAX_GROUP; m++)
+        total += rows[m] > 0 ? rows[m] : 0;
+    const size_t yn = size_t(total) * 4, xn = size_t(cols > 0 ? cols : 0) * 4;
+    const pti::Range outs[] = {{y_a, yn}, {y_b, yn}};
+    GemvArgs a;
+    const int rc = group_args<kSSQ>(w_ssq, rows, n_mats, cols, outs, 2, a);
+    if (rc != PTI_OK)
+        return rc;
+    if (!pti::aligned(x_a, 16) || !pti::aligned(x_b, 16) || !pti::aligned(y_a, 4) || !pti::aligned(y_b, 4))
+        return PTI_ERR_ALIGN;
+    if (pti::overlap(outs[0], outs[1]) || pti::overlap(outs[0], {x_a, xn}) || pti::overlap(outs[0], {x_b, xn}) ||
+        pti::overlap(outs[1], {x_a, xn}) || pti::overlap(outs[1], {x_b, xn}))
+        return PTI_ERR_OVERLAP;
+    a.x[0] = x_a, a.x[1] = x_b;
+    a.y[0] = y_a, a.y[1] = y_b;
+    return launch_ssq(a, static_cast<hipStream_t>(stream));
 }
 
 int pti_gemv_ssq_verify(const void *w_ssq, const float *x_a, const float *x_b, float *y_a, float *y_b, int64_t rows,
@@ -1128,22 +1234,34 @@ int pti_gemv_q8_multi(const void *w_q8, const float *x, float *y, int64_t rows, 
         a.x[s] = x + (size_t)s * cols;
         a.y[s] = y + (size_t)s * rows;
     }
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    // rows start on dword boundaries when a row holds an even number of blocks
-    if ((cols / PTI_BLOCK) % 2 == 0) {
-        switch (n_streams) {
-        case 1: return launch<kQ8, 1, 1, true>(a, st);
-        case 2: return launch<kQ8, 2, 2, true>(a, st);
-        case 3: return launch<kQ8, 4, 3, true>(a, st);
-        default: return launch<kQ8, 4, 4, true>(a, st);
-        }
+    return launch_q8(a, n_streams, static_cast<hipStream_t>(stream));
+}
+
+int pti_gemv_q8_multi_grouped(const void *const *w_q8, const int64_t *rows, int n_mats, const float *x, float *y,
+                              int64_t cols, int n_streams, void *stream)
+{
+    if (!x || !y)
+        return PTI_ERR_NULL;
+    if (n_streams < 1 || n_streams > PTI_MAX_STREAMS)
+        return PTI_ERR_NSTREAMS;
+    int64_t total = 0;
+    for (int m = 0; rows && m < n_mats && m < PTI_MAX_GROUP; m++)
+        total += rows[m] > 0 ? rows[m] : 0;
+    const size_t yn = size_t(n_streams) * total * 4, xn = size_t(n_streams) * (cols > 0 ? cols : 0) * 4;
+    const pti::Range outs[] = {{y, yn}};
+    GemvArgs a;
+    const int rc = group_args<kQ8>(w_q8, rows, n_mats, cols, outs, 1, a);
+    if (rc != PTI_OK)
+        return rc;
+    if (!pti::aligned(x, 16) || !pti::aligned(y, 4))
+        return PTI_ERR_ALIGN;
+    if (pti::overlap(outs[0], {x, xn}))
+        return PTI_ERR_OVERLAP;
+    for (int s = 0; s < n_streams; s++) {
+        a.x[s] = x + (size_t)s * cols;
+        a.y[s] = y + (size_t)s * a.rows;
     }
-    switch (n_streams) {
-    case 1: return launch<kQ8, 1, 1, false>(a, st);
-    case 2: return launch<kQ8, 2, 2, false>(a, st);
-    case 3: return launch<kQ8, 4, 3, false>(a, st);
-    default: return launch<kQ8, 4, 4, false>(a, st);
-    }
+    return launch_q8(a, n_streams, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -253,6 +253,61 @@ extern "C" int pti_toy_forward(const pti_toy_model *m, const int32_t *tokens, fl
     return forward(*m, L, static_cast<char *>(work), tokens, logits, n_streams, stream);
 }
 
+extern "C" int pti_toy_forward_graph(const pti_toy_model *m, const int32_t *tokens, float *logits, void *work,
+                                     size_t work_bytes, int n_streams, void **graph_out)
+{
+    if (!graph_out)
+        return PTI_ERR_NULL;
+    *graph_out = nullptr;
+    PTI_TRY(check_model(m));
+    PTI_TRY(check_streams(m, n_streams));
+    if (!tokens || !logits)
+        return PTI_ERR_NULL;
+    if (!pti::aligned(tokens, 4) || !pti::aligned(logits, 4))
+        return PTI_ERR_ALIGN;
+    const Layout L = layout(*m, n_streams);
+    PTI_TRY(check_work(L, work, work_bytes));
+    const pti::Range W{work, L.total}, T{tokens, size_t(n_streams) * 4},
+        O{logits, size_t(n_streams) * size_t(m->vocab) * 4};
+    if (pti::overlap(W, T) || pti::overlap(W, O) || pti::overlap(T, O))
+        return PTI_ERR_OVERLAP;
+    // Capture one pass on a private stream (default priority); the graph
+    // keeps the kernels and their arguments, so replays read tokens and write
+    // logits and work at these addresses.
+    hipStream_t cs = nullptr;
+    PTI_TRY(hip_status(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking)));
+    hipGraph_t g = nullptr;
+    int rc = hip_status(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
+    if (rc == PTI_OK) {
+        const int frc = forward(*m, L, static_cast<char *>(work), tokens, logits, n_streams, cs);
+        const int erc = hip_status(hipStreamEndCapture(cs, &g));  // always ends the capture
+        rc = frc != PTI_OK ? frc : erc;
+    }
+    hipGraphExec_t exec = nullptr;
+    if (rc == PTI_OK)
+        rc = hip_status(hipGraphInstantiate(&exec, g, nullptr, nullptr, 0));
+    if (g)
+        (void)hipGraphDestroy(g);
+    (void)hipStreamDestroy(cs);
+    if (rc == PTI_OK)
+        *graph_out = exec;
+    return rc;
+}
+
+extern "C" int pti_graph_launch(void *graph, void *stream)
+{
+    if (!graph)
+        return PTI_ERR_NULL;
+    return hip_status(hipGraphLaunch(static_cast<hipGraphExec_t>(graph), static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int pti_graph_destroy(void *graph)
+{
+    if (!graph)
+        return PTI_OK;
+    return hip_status(hipGraphExecDestroy(static_cast<hipGraphExec_t>(graph)));
+}
+
 extern "C" int pti_toy_decode(const pti_toy_model *m, int32_t first_token, int n_streams, int n_steps,
                               double temperature, const double *uniforms, void *work, size_t work_bytes,
                               int32_t *committed, int32_t *accepts, int32_t *passes, int64_t *n_passes, void *stream)

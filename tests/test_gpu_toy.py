@@ -377,6 +377,39 @@ def test_forward_full_ssq_self_twin(full_ssq, full_oracle):
     assert np.abs(lg - want).max() / want.std() < 1e-3  # sanity
 
 
+def _graph_replays(stack, token_sets):
+    """Capture one pass as a HIP graph, then for each token set: write the
+    tokens into the captured buffer, replay, and compare with an eager pass on
+    the same tokens (eager work runs between replays)."""
+    torch = _torch()
+    n = len(token_sets[0])
+    tokens = dev(token_sets[0], np.int32)
+    logits = torch.empty((n, stack.V), dtype=torch.float32, device=tokens.device)
+    work = stack.gpu.workspace(n)
+    graph = stack.gpu.forward_graph(tokens, logits, work)
+    try:
+        for toks in token_sets + token_sets[:1]:
+            tokens.copy_(torch.tensor(toks, dtype=torch.int32))
+            graph.launch()
+            torch.cuda.synchronize()
+            got = host(logits).copy()
+            want = host(stack.gpu.forward(dev(toks, np.int32)))
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), toks
+    finally:
+        graph.destroy()
+
+
+def test_forward_graph_replays_small(small_raw):
+    pti = _pti()
+    _graph_replays(Stack(small_raw, pti.FMT_Q8), [[0, 1, 2, 3], [1000, 3, 5, 5], [17, 17, 17, 17]])
+    other = synth.toy_weights(98, hidden=96, ffn=160, layers=3, vocab=1001)
+    _graph_replays(Stack(small_raw, pti.FMT_SSQ, raw_b=other), [[0, 0], [1000, 3]])
+
+
+def test_forward_graph_replays_full(full_q8):
+    _graph_replays(full_q8, [[1, 31999, 12345, 7], [5, 6, 7, 8]])
+
+
 # ------------------------------------------------------------------ decode loop
 
 def replay(passes, first, N, steps):

@@ -162,6 +162,41 @@ def test_gemv_ssq_verify_errors():
     assert call(yb=A0 + 128) == OVERLAP
 
 
+def test_grouped_gemv_errors():
+    L = pti.lib()
+
+    def arr(ctype, vals):
+        return (ctype * len(vals))(*vals)
+
+    W = arr(ctypes.c_void_p, [A0, A0 + 0x100000, A0 + 0x200000])
+    R = arr(ctypes.c_int64, [8, 4, 4])
+    q8 = L.pti_gemv_q8_multi_grouped
+    assert q8(None, R, 3, _fake(A1), _fake(A2), 64, 1, None) == NULL
+    assert q8(W, None, 3, _fake(A1), _fake(A2), 64, 1, None) == NULL
+    assert q8(W, R, 0, _fake(A1), _fake(A2), 64, 1, None) == SHAPE
+    assert q8(W, R, 5, _fake(A1), _fake(A2), 64, 1, None) == SHAPE
+    assert q8(W, R, 3, _fake(A1), _fake(A2), 64, 0, None) == NSTREAMS
+    assert q8(arr(ctypes.c_void_p, [A0, 0, A0]), R, 3, _fake(A1), _fake(A2), 64, 1, None) == NULL
+    assert q8(W, arr(ctypes.c_int64, [8, 0, 4]), 3, _fake(A1), _fake(A2), 64, 1, None) == SHAPE
+    assert q8(W, R, 3, _fake(A1), _fake(A2), 48, 1, None) == SHAPE
+    assert q8(arr(ctypes.c_void_p, [A0, A0 + 0x100002, A0]), R, 3, _fake(A1), _fake(A2), 64, 1, None) == ALIGN
+    # y over the second matrix
+    assert q8(W, R, 3, _fake(A1), _fake(A0 + 0x100000 + 64), 64, 1, None) == OVERLAP
+    ssq = L.pti_gemv_ssq_grouped
+    assert ssq(W, R, 3, _fake(A1), None, _fake(A2), _fake(A3), 64, None) == NULL
+    assert ssq(W, R, 5, _fake(A1), _fake(A1), _fake(A2), _fake(A3), 64, None) == SHAPE
+    assert ssq(W, arr(ctypes.c_int64, [8, -1, 4]), 3, _fake(A1), _fake(A1), _fake(A2), _fake(A3), 64, None) == SHAPE
+    assert ssq(W, R, 3, _fake(A1), _fake(A1), _fake(A2), _fake(A2 + 16), 64, None) == OVERLAP
+    assert ssq(W, R, 3, _fake(A1), _fake(A1), _fake(A0 + 0x200000), _fake(A3), 64, None) == OVERLAP
+
+
+def test_graph_handles_errors():
+    L = pti.lib()
+    assert L.pti_graph_launch(None, None) == NULL
+    assert L.pti_graph_destroy(None) == 0
+    assert L.pti_toy_forward_graph(None, _fake(A1), _fake(A2), _fake(A3), 1 << 20, 1, None) == NULL
+
+
 def test_gemv_q8_errors():
     L = pti.lib()
     f = L.pti_gemv_q8_multi
