@@ -451,6 +451,23 @@ def main():
         per_kernel["ssq_twin_gemv_unfused"] = {**st_gemv,
                                                "weight_GBps": round(w_bytes / (ms_gemv * 1e-3) / 1e9, 2)}
         per_kernel["verify_n2_v17408_unfused"] = st_verify
+        # two streams per twin: four activation vectors per weight read
+        xa2 = torch.randn((2, COLS), device=dev)
+        xb2 = torch.randn((2, COLS), device=dev)
+        ya2 = torch.empty((2, ROWS), device=dev)
+        yb2 = torch.empty((2, ROWS), device=dev)
+
+        def gemv2(i):
+            st = L.pti_gemv_ssq_multi(ws[i % n_copies].data_ptr(), xa2.data_ptr(), xb2.data_ptr(), ya2.data_ptr(),
+                                      yb2.data_ptr(), ROWS, COLS, 2, sp)
+            if st:
+                pti._check("pti_gemv_ssq_multi", st)
+        st_g2 = timed_stats(torch, gemv2, stream)
+        per_kernel["ssq_gemv_2_per_twin"] = {
+            **st_g2, "weight_GBps": round(w_bytes / (st_g2["median_us"] * 1e-6) / 1e9, 2),
+            "outputs_per_s": round(4 * ROWS / (st_g2["median_us"] * 1e-6), 1),
+            "cost_over_1_per_twin": round(st_g2["median_us"] / st_gemv["median_us"], 4)}
+        log(f"ssq 2 per twin: {st_g2}")
         # device-to-device copy of the same byte count, rotated the same way:
         # the practical ceiling (reads and writes w_bytes each)
         dsts = [torch.empty_like(w0) for _ in range(2)]

@@ -142,6 +142,20 @@ int pti_ssq_join(const uint8_t *q8_a, const uint8_t *q8_b, int64_t rows, int64_t
 int pti_gemv_ssq(const void *w_ssq, const float *x_a, const float *x_b, float *y_a, float *y_b,
                  int64_t rows, int64_t cols, void *stream);
 
+/* SSQ twin GEMV with n_per_twin streams per twin [README, relation to SSQ
+ * (one slot load feeds both twins) combined with the bandwidth analysis (one
+ * weight read feeds several activation vectors)]: one pass over the packed
+ * matrix computes, for j < n_per_twin,
+ *   y_a[j][r] = sum_c scale_A(r, c/32) * A[r][c] * x_a[j][c]
+ *   y_b[j][r] = sum_c scale_B(r, c/32) * B[r][c] * x_b[j][c]
+ * Each (twin, j) output is bitwise the one pti_gemv_ssq gives for
+ * (x_a[j], x_b[j]).  x_a, x_b: device fp32 [n_per_twin][cols] contiguous
+ * (16-byte aligned); y_a, y_b: device fp32 [n_per_twin][rows] contiguous, not
+ * overlapping each other or any input; 1 <= n_per_twin <= 2 (else
+ * PTI_ERR_NSTREAMS). */
+int pti_gemv_ssq_multi(const void *w_ssq, const float *x_a, const float *x_b, float *y_a, float *y_b,
+                       int64_t rows, int64_t cols, int n_per_twin, void *stream);
+
 /* SSQ twin GEMV fused with the greedy verify of its two outputs [README,
  * relation to SSQ; README, how acceptance works]: the results of
  * pti_gemv_ssq (y_a, y_b bitwise the same) and those of pti_verify_argmax

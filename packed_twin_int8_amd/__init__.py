@@ -39,7 +39,8 @@ STATUS = {0: "PTI_OK", -1: "PTI_ERR_NULL", -2: "PTI_ERR_SHAPE", -3: "PTI_ERR_NST
 EXPORTS = (
     "pti_status_str", "pti_last_hip_error", "pti_abi_version", "pti_ssq_bytes", "pti_q8_bytes", "pti_pack_ssq",
     "pti_unpack_ssq", "pti_pack_q8", "pti_unpack_q8", "pti_ssq_split", "pti_ssq_join", "pti_gemv_ssq",
-    "pti_gemv_ssq_verify", "pti_gemv_q8_multi", "pti_gemv_ssq_grouped", "pti_gemv_q8_multi_grouped", "pti_verify_argmax", "pti_sample_verify", "pti_embed_q8", "pti_embed_ssq", "pti_rmsnorm",
+    "pti_gemv_ssq_verify", "pti_gemv_q8_multi", "pti_gemv_ssq_grouped", "pti_gemv_q8_multi_grouped",
+    "pti_gemv_ssq_multi", "pti_verify_argmax", "pti_sample_verify", "pti_embed_q8", "pti_embed_ssq", "pti_rmsnorm",
     "pti_silu_mul", "pti_add", "pti_toy_workspace_bytes", "pti_toy_forward", "pti_toy_decode",
     "pti_toy_forward_graph", "pti_graph_launch", "pti_graph_destroy",
 )
@@ -94,6 +95,7 @@ def lib() -> ctypes.CDLL:
         L.pti_gemv_ssq.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _P]
         L.pti_gemv_ssq_verify.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.pti_gemv_q8_multi.argtypes = [_P, _P, _P, _I64, _I64, _INT, _P]
+        L.pti_gemv_ssq_multi.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _INT, _P]
         L.pti_gemv_ssq_grouped.argtypes = [_P, _P, _INT, _P, _P, _P, _P, _I64, _P]
         L.pti_gemv_q8_multi_grouped.argtypes = [_P, _P, _INT, _P, _P, _I64, _INT, _P]
         L.pti_verify_argmax.argtypes = [_P, _P, _P, _P, _I64, _INT, _P]
@@ -257,6 +259,27 @@ SSQ_VERIFY_WORK_BYTES = 16384  # PTI_SSQ_VERIFY_WORK_BYTES
 def ssq_verify_workspace(device):
     """Scratch for gemv_ssq_verify (contents need no initialisation)."""
     return _torch().empty(SSQ_VERIFY_WORK_BYTES, dtype=_torch().uint8, device=device)
+
+
+def gemv_ssq_multi(w, x_a, x_b, y_a=None, y_b=None, stream=None):
+    """SSQ twin GEMV with n streams per twin (n = 1, 2): y_a[j] = W_A x_a[j],
+    y_b[j] = W_B x_b[j], one pass over w.  x_a, x_b: float32 [n, cols]."""
+    torch = _torch()
+    _dev(w, "w", torch.uint8), _dev(x_a, "x_a", torch.float32), _dev(x_b, "x_b", torch.float32)
+    if x_a.dim() == 1:
+        x_a, x_b = x_a.unsqueeze(0), x_b.unsqueeze(0)
+    n, cols = x_a.shape
+    rows = w.shape[0]
+    if w.dim() != 2 or w.shape[1] != cols // 32 * 68 or x_b.shape != x_a.shape:
+        raise ValueError("gemv_ssq_multi: shape mismatch")
+    dev = w.device
+    y_a = torch.empty((n, rows), dtype=torch.float32, device=dev) if y_a is None else _dev(y_a, "y_a", torch.float32)
+    y_b = torch.empty((n, rows), dtype=torch.float32, device=dev) if y_b is None else _dev(y_b, "y_b", torch.float32)
+    if y_a.numel() != n * rows or y_b.numel() != n * rows:
+        raise ValueError("gemv_ssq_multi: output shape mismatch")
+    _check("pti_gemv_ssq_multi", lib().pti_gemv_ssq_multi(w.data_ptr(), x_a.data_ptr(), x_b.data_ptr(), y_a.data_ptr(),
+                                                          y_b.data_ptr(), rows, cols, n, _stream(stream)))
+    return y_a, y_b
 
 
 def gemv_ssq_verify(w, x_a, x_b, tokens_in, work, y_a=None, y_b=None, argmax_out=None, accept_out=None,

@@ -418,11 +418,12 @@ struct Wave {
                             bs[r][s] = (c == 0 && m == 0) ? wq * xv[m][s] : __builtin_fmaf(wq, xv[m][s], bs[r][s]);
                     } else {
                         // slot 4c + m of the unit: dword 2c + m/2, halfword m % 2;
-                        // twin A = high byte, twin B = low byte
+                        // twin A = high byte (even streams), twin B = low byte
+                        // (odd streams)
                         const uint32_t dw = buf[r].d[2 * c + (m >> 1)];
 #pragma unroll
                         for (int s = 0; s < NS; s++) {
-                            const float wq = sbyte(dw, 2 * (m & 1) + (s == 0 ? 1 : 0));
+                            const float wq = sbyte(dw, 2 * (m & 1) + ((s & 1) ? 0 : 1));
                             bs[r][s] = (c == 0 && m == 0) ? wq * xv[m][s] : __builtin_fmaf(wq, xv[m][s], bs[r][s]);
                         }
                     }
@@ -437,8 +438,9 @@ struct Wave {
                 for (int s = 0; s < NS; s++)
                     acc[r][s] = __builtin_fmaf(d, bs[r][s], acc[r][s]);
             } else {
-                acc[r][0] = __builtin_fmaf(f16_lo(buf[r].sc), bs[r][0], acc[r][0]);
-                acc[r][1] = __builtin_fmaf(f16_hi(buf[r].sc), bs[r][1], acc[r][1]);
+#pragma unroll
+                for (int s = 0; s < NS; s++)
+                    acc[r][s] = __builtin_fmaf((s & 1) ? f16_hi(buf[r].sc) : f16_lo(buf[r].sc), bs[r][s], acc[r][s]);
             }
         }
         if (cr == a.rounds - 1) {  // the pass's rows are complete
@@ -771,13 +773,18 @@ __device__ __forceinline__ unsigned long long verify_key(float v, int64_t row)
 // single kernel whose last workgroup reduces the keys needs a device-scope
 // release and acquire per workgroup to see the others' keys, and on this GPU
 // those cost more than the second launch.)
-template <int T, bool VERIFY>
-__global__ __launch_bounds__(64 * split_bound_waves(T)) void gemv_ssq_split_kernel(SplitArgs sa)
+//
+// BW: the launch bound in waves.  Normally split_bound_waves(T); launches of
+// at most four waves may use a bound of four, which lets a wave keep more
+// values in registers (two streams per twin at T = 5 need it).
+template <int T, int NS, bool VERIFY, int BW = split_bound_waves(T)>
+__global__ __launch_bounds__(64 * BW) void gemv_ssq_split_kernel(SplitArgs sa)
 {
+    static_assert(NS == 2 || (NS == 4 && !VERIFY), "streams: one or two per twin; verify with one");
     constexpr int UC = unit_cols<kSSQ>();
     const GemvArgs &a = sa.g;
     const int P = sa.P, Q = sa.Q, S = sa.S;
-    extern __shared__ float part[];  // [2][S * P][Q][2]: row partials, double-buffered
+    extern __shared__ float part[];  // [2][S * P][Q][NS]: row partials, double-buffered
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int p = wv / Q, q = wv - (wv / Q) * Q;
@@ -786,13 +793,13 @@ __global__ __launch_bounds__(64 * split_bound_waves(T)) void gemv_ssq_split_kern
     const int steps = (int)((wg_rows + P - 1) / P);
 
     // x of this lane's units in rounds q T .. q T + T - 1 (zero past the row's
-    // last unit), both twins
-    float xv[T][UC][2];
+    // last unit), every stream (stream s feeds twin A if s is even, twin B if odd)
+    float xv[T][UC][NS];
 #pragma unroll
     for (int tt = 0; tt < T; tt++) {
         const int unit = (q * T + tt) * 64 + lane;
 #pragma unroll
-        for (int s = 0; s < 2; s++)
+        for (int s = 0; s < NS; s++)
 #pragma unroll
             for (int k = 0; k < UC / 4; k++) {
                 float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -829,34 +836,39 @@ __global__ __launch_bounds__(64 * split_bound_waves(T)) void gemv_ssq_split_kern
     // workgroup's last write nothing).
     auto step = [&](int t, int half, int local, const Unit (&ut)[T], Unit (&nxt)[T]) {
         const __amdgpu_buffer_rsrc_t rs_next = rsrc_for(t + 1);
-        float acc[2];
+        float acc[NS];
 #pragma unroll
         for (int tt = 0; tt < T; tt++) {
             const Unit &u = ut[tt];
-            float bs[2];
-            // slot c: dword c/2, halfword c%2; twin A = high byte, twin B = low byte
+            float bs[NS];
+            // slot c: dword c/2, halfword c%2; twin A = high byte, twin B = low
+            // byte.  Each stream's chain is the same whatever NS is.
 #pragma unroll
             for (int c = 0; c < UC; c++) {
                 const uint32_t dw = u.d[c >> 1];
+                const float wa = sbyte(dw, 2 * (c & 1) + 1), wb = sbyte(dw, 2 * (c & 1));
 #pragma unroll
-                for (int s = 0; s < 2; s++) {
-                    const float wq = sbyte(dw, 2 * (c & 1) + (s == 0 ? 1 : 0));
+                for (int s = 0; s < NS; s++) {
+                    const float wq = (s & 1) ? wb : wa;
                     bs[s] = c == 0 ? wq * xv[tt][c][s] : __builtin_fmaf(wq, xv[tt][c][s], bs[s]);
                 }
             }
             const float da = f16_lo(u.sc), db = f16_hi(u.sc);
-            acc[0] = tt == 0 ? da * bs[0] : __builtin_fmaf(da, bs[0], acc[0]);
-            acc[1] = tt == 0 ? db * bs[1] : __builtin_fmaf(db, bs[1], acc[1]);
+#pragma unroll
+            for (int s = 0; s < NS; s++) {
+                const float d = (s & 1) ? db : da;
+                acc[s] = tt == 0 ? d * bs[s] : __builtin_fmaf(d, bs[s], acc[s]);
+            }
             __builtin_amdgcn_sched_barrier(0);
             load_round(rs_next, tt, nxt[tt]);
             __builtin_amdgcn_sched_barrier(0);
         }
         const int slot = (half * S + local) * P + p;  // row slot in the double buffer
 #pragma unroll
-        for (int s = 0; s < 2; s++) {
+        for (int s = 0; s < NS; s++) {
             const float v = wave_sum(acc[s]);
             if (lane == 63 && t < steps)
-                part[(slot * Q + q) * 2 + s] = v;
+                part[(slot * Q + q) * NS + s] = v;
         }
     };
 
@@ -867,22 +879,22 @@ __global__ __launch_bounds__(64 * split_bound_waves(T)) void gemv_ssq_split_kern
     auto flush = [&](int t0, int t1, int half) {
         __syncthreads();
         const int n = (t1 - t0) * P;
-        // twins outermost with a compile-time index: a lane-varying index into
-        // the argument array would load the output pointer from memory, and
-        // that wait would also drain the weight loads in flight
+        // streams outermost with a compile-time index: a lane-varying index
+        // into the argument array would load the output pointer from memory,
+        // and that wait would also drain the weight loads in flight
 #pragma unroll
-        for (int s = 0; s < 2; s++)
+        for (int s = 0; s < NS; s++)
             for (int r = tid; r < n; r += 64 * P * Q) {  // r: row slot relative to step t0
                 const int64_t m = (int64_t)t0 * P + r;
                 if (m >= wg_rows)
                     continue;
                 const int slot = half * S * P + r;
-                float acc = part[(slot * Q) * 2 + s];
+                float acc = part[(slot * Q) * NS + s];
                 for (int j = 1; j < Q; j++)
-                    acc += part[((slot * Q) + j) * 2 + s];
+                    acc += part[((slot * Q) + j) * NS + s];
                 a.y[s][g + m * G] = acc;
                 if constexpr (VERIFY)
-                    vkey[s] = std::max(vkey[s], verify_key(acc, g + m * G));
+                    vkey[s & 1] = std::max(vkey[s & 1], verify_key(acc, g + m * G));
             }
         // Stores count on the same counter as the weight loads.  Without this
         // wait the compiler cannot tell how many operations follow the
@@ -984,7 +996,7 @@ int split_T(int rounds)
 // Geometry for T, or false if the row needs more waves than a workgroup may
 // have.  S: steps per flush, even, with the partials' double buffer at most
 // 32 KB of LDS.
-bool split_shape(int rounds, int T, SplitArgs &sa)
+bool split_shape(int rounds, int T, int ns, SplitArgs &sa)
 {
     const int Q = (rounds + T - 1) / T, W = split_bound_waves(T);
     if (rounds < 1 || Q > W)
@@ -992,7 +1004,7 @@ bool split_shape(int rounds, int T, SplitArgs &sa)
     sa.Q = Q;
     sa.P = std::max(1, std::min(W, T >= 3 ? kSplitWavesBigT : kSplitWavesSmallT) / Q);
     int S = 64;
-    while (S > 2 && 2 * S * sa.P * Q * 2 * 4 > 32 * 1024)
+    while (S > 2 && 2 * S * sa.P * Q * ns * 4 > 32 * 1024)
         S -= 2;
     sa.S = S;
     return true;
@@ -1007,11 +1019,11 @@ struct VerifyOut {
     int32_t *argmax_out, *accept_out;
 };
 
-template <int T, bool VERIFY>
+template <int T, int NS, bool VERIFY>
 int launch_ssq_split(const GemvArgs &a, const VerifyOut *vo, hipStream_t stream)
 {
     SplitArgs sa{};
-    if (!split_shape(a.rounds, T, sa))
+    if (!split_shape(a.rounds, T, NS, sa))
         return kNotSplit;
     sa.g = a;
     if constexpr (VERIFY)
@@ -1022,9 +1034,18 @@ int launch_ssq_split(const GemvArgs &a, const VerifyOut *vo, hipStream_t stream)
         return PTI_ERR_HIP;
     }
     const int64_t grid = std::min<int64_t>(std::min(cus, kSplitMaxGrid), a.rows);
-    const size_t lds = (size_t)2 * sa.S * sa.P * sa.Q * 2 * sizeof(float);
-    hipLaunchKernelGGL((gemv_ssq_split_kernel<T, VERIFY>), dim3((unsigned)grid), dim3((unsigned)(64 * sa.P * sa.Q)),
-                       lds, stream, sa);
+    const size_t lds = (size_t)2 * sa.S * sa.P * sa.Q * NS * sizeof(float);
+    bool small = false;
+    if constexpr (NS == 4)
+        small = sa.P * sa.Q <= 4;
+    if constexpr (NS == 4) {
+        if (small)
+            hipLaunchKernelGGL((gemv_ssq_split_kernel<T, NS, VERIFY, 4>), dim3((unsigned)grid),
+                               dim3((unsigned)(64 * sa.P * sa.Q)), lds, stream, sa);
+    }
+    if (!small)
+        hipLaunchKernelGGL((gemv_ssq_split_kernel<T, NS, VERIFY>), dim3((unsigned)grid),
+                           dim3((unsigned)(64 * sa.P * sa.Q)), lds, stream, sa);
     if constexpr (VERIFY)
         hipLaunchKernelGGL(verify_keys_kernel, dim3(1), dim3(256), 0, stream, vo->keys, (int)grid, vo->tokens_in,
                            vo->argmax_out, vo->accept_out);
@@ -1036,16 +1057,17 @@ int launch_ssq_split(const GemvArgs &a, const VerifyOut *vo, hipStream_t stream)
     return PTI_OK;
 }
 
-// vo: the verify outputs (VERIFY only, else null).
-template <bool VERIFY>
+// vo: the verify outputs (VERIFY only, else null).  NS: 2 (one stream per
+// twin) or 4 (two per twin).
+template <int NS, bool VERIFY>
 int launch_ssq_split(const GemvArgs &a, const VerifyOut *vo, hipStream_t stream)
 {
     switch (split_T(a.rounds)) {
-    case 1: return launch_ssq_split<1, VERIFY>(a, vo, stream);
-    case 2: return launch_ssq_split<2, VERIFY>(a, vo, stream);
-    case 3: return launch_ssq_split<3, VERIFY>(a, vo, stream);
-    case 4: return launch_ssq_split<4, VERIFY>(a, vo, stream);
-    default: return launch_ssq_split<5, VERIFY>(a, vo, stream);
+    case 1: return launch_ssq_split<1, NS, VERIFY>(a, vo, stream);
+    case 2: return launch_ssq_split<2, NS, VERIFY>(a, vo, stream);
+    case 3: return launch_ssq_split<3, NS, VERIFY>(a, vo, stream);
+    case 4: return launch_ssq_split<4, NS, VERIFY>(a, vo, stream);
+    default: return launch_ssq_split<5, NS, VERIFY>(a, vo, stream);
     }
 }
 
@@ -1069,12 +1091,16 @@ int launch_q8(const GemvArgs &a, int n_streams, hipStream_t st)
     }
 }
 
-int launch_ssq(const GemvArgs &a, hipStream_t st)
+// n_per_twin: streams per twin (1 or 2); a.x / a.y hold stream s at s, twin
+// A for even s and twin B for odd s.  The kernel choice depends on the shape
+// alone, so a (twin, stream) output does not depend on n_per_twin.
+int launch_ssq(const GemvArgs &a, int n_per_twin, hipStream_t st)
 {
-    const int rc = launch_ssq_split<false>(a, nullptr, st);
+    const int rc = n_per_twin == 1 ? launch_ssq_split<2, false>(a, nullptr, st)
+                                   : launch_ssq_split<4, false>(a, nullptr, st);
     if (rc != kNotSplit)
         return rc;
-    return launch<kSSQ, 2, 2, true>(a, st);
+    return n_per_twin == 1 ? launch<kSSQ, 2, 2, true>(a, st) : launch<kSSQ, 4, 4, true>(a, st);
 }
 
 // A grouped launch's matrices: validated, then stacked into one row space.
@@ -1143,7 +1169,33 @@ int pti_gemv_ssq(const void *w_ssq, const float *x_a, const float *x_b, float *y
     GemvArgs a = make_args<kSSQ>(w_ssq, rows, cols);
     a.x[0] = x_a, a.x[1] = x_b;
     a.y[0] = y_a, a.y[1] = y_b;
-    return launch_ssq(a, static_cast<hipStream_t>(stream));
+    return launch_ssq(a, 1, static_cast<hipStream_t>(stream));
+}
+
+int pti_gemv_ssq_multi(const void *w_ssq, const float *x_a, const float *x_b, float *y_a, float *y_b, int64_t rows,
+                       int64_t cols, int n_per_twin, void *stream)
+{
+    if (!w_ssq || !x_a || !x_b || !y_a || !y_b)
+        return PTI_ERR_NULL;
+    if (!pti::shape_ok(rows, cols))
+        return PTI_ERR_SHAPE;
+    if (n_per_twin < 1 || 2 * n_per_twin > PTI_MAX_STREAMS)
+        return PTI_ERR_NSTREAMS;
+    if (!pti::aligned(w_ssq, 4) || !pti::aligned(x_a, 16) || !pti::aligned(x_b, 16) || !pti::aligned(y_a, 4) ||
+        !pti::aligned(y_b, 4))
+        return PTI_ERR_ALIGN;
+    const size_t n = size_t(n_per_twin), wn = pti_ssq_bytes(rows, cols), xn = n * cols * 4, yn = n * rows * 4;
+    const pti::Range ya{y_a, yn}, yb{y_b, yn};
+    if (pti::overlap(ya, yb) || pti::overlap(ya, {w_ssq, wn}) || pti::overlap(yb, {w_ssq, wn}) ||
+        pti::overlap(ya, {x_a, xn}) || pti::overlap(ya, {x_b, xn}) || pti::overlap(yb, {x_a, xn}) ||
+        pti::overlap(yb, {x_b, xn}))
+        return PTI_ERR_OVERLAP;
+    GemvArgs a = make_args<kSSQ>(w_ssq, rows, cols);
+    for (int j = 0; j < n_per_twin; j++) {
+        a.x[2 * j] = x_a + (size_t)j * cols, a.x[2 * j + 1] = x_b + (size_t)j * cols;
+        a.y[2 * j] = y_a + (size_t)j * rows, a.y[2 * j + 1] = y_b + (size_t)j * rows;
+    }
+    return launch_ssq(a, n_per_twin, static_cast<hipStream_t>(stream));
 }
 
 int pti_gemv_ssq_grouped(const void *const *w_ssq, const int64_t *rows, int n_mats, const float *x_a,
@@ -1167,7 +1219,7 @@ int pti_gemv_ssq_grouped(const void *const *w_ssq, const int64_t *rows, int n_ma
         return PTI_ERR_OVERLAP;
     a.x[0] = x_a, a.x[1] = x_b;
     a.y[0] = y_a, a.y[1] = y_b;
-    return launch_ssq(a, static_cast<hipStream_t>(stream));
+    return launch_ssq(a, 1, static_cast<hipStream_t>(stream));
 }
 
 int pti_gemv_ssq_verify(const void *w_ssq, const float *x_a, const float *x_b, float *y_a, float *y_b, int64_t rows,
@@ -1202,7 +1254,7 @@ int pti_gemv_ssq_verify(const void *w_ssq, const float *x_a, const float *x_b, f
     a.x[0] = x_a, a.x[1] = x_b;
     a.y[0] = y_a, a.y[1] = y_b;
     const VerifyOut vo{static_cast<unsigned long long *>(work), tokens_in, argmax_out, accept_out};
-    const int rc = launch_ssq_split<true>(a, &vo, st);
+    const int rc = launch_ssq_split<2, true>(a, &vo, st);
     if (rc != kNotSplit)
         return rc;
     // shapes the row-split kernel does not take: GEMV, then the verify kernel

@@ -197,6 +197,20 @@ def test_graph_handles_errors():
     assert L.pti_toy_forward_graph(None, _fake(A1), _fake(A2), _fake(A3), 1 << 20, 1, None) == NULL
 
 
+def test_gemv_ssq_multi_errors():
+    L = pti.lib()
+    f = L.pti_gemv_ssq_multi
+    assert f(_fake(A0), None, _fake(A1), _fake(A2), _fake(A3), 8, 64, 1, None) == NULL
+    assert f(_fake(A0), _fake(A1), _fake(A1), _fake(A2), _fake(A3), 8, 64, 0, None) == NSTREAMS
+    assert f(_fake(A0), _fake(A1), _fake(A1), _fake(A2), _fake(A3), 8, 64, 3, None) == NSTREAMS
+    assert f(_fake(A0), _fake(A1), _fake(A1), _fake(A2), _fake(A3), 8, 48, 2, None) == SHAPE
+    assert f(_fake(A0), _fake(A1 + 4), _fake(A1), _fake(A2), _fake(A3), 8, 64, 2, None) == ALIGN
+    # with two streams per twin, y_a spans 64 bytes: y_b at +32 overlaps it
+    assert f(_fake(A0), _fake(A1), _fake(A1), _fake(A2), _fake(A2 + 32), 8, 64, 2, None) == OVERLAP
+    # x_b spans two rows of 64 floats: y_a at x_b + 256 overlaps its second row
+    assert f(_fake(A0), _fake(A1), _fake(A4), _fake(A4 + 256), _fake(A3), 8, 64, 2, None) == OVERLAP
+
+
 def test_gemv_q8_errors():
     L = pti.lib()
     f = L.pti_gemv_q8_multi
