@@ -351,6 +351,35 @@ def layer_and_graph(torch, pti, dev, stream):
     return out
 
 
+def attention(torch, pti, dev, stream):
+    """Twin-KV decode attention (two streams: the twins), 40 query heads over
+    8 kv heads of 128, binary16 caches, at 4K and 32K positions: time per
+    call and the K/V bytes it must read against 8 TB/s."""
+    out = {}
+    S, H, Hkv, d = 2, 40, 8, 128
+    for L in (4096, 32768):
+        kc = [torch.randn((Hkv, L, d), device=dev).half() for _ in range(S)]
+        vc = [torch.randn((Hkv, L, d), device=dev).half() for _ in range(S)]
+        q = torch.randn((S, H, d), device=dev)
+        kn = torch.randn((S, Hkv, d), device=dev)
+        vn = torch.randn((S, Hkv, d), device=dev)
+        pos = torch.tensor([L - 2, L - 1], dtype=torch.int32, device=dev)
+        work = pti.attn_workspace(S, H, Hkv, d, L, dev)
+        o = torch.empty_like(q)
+        st = timed_stats(torch, lambda i: pti.attn_decode(q, kn, vn, kc, vc, pos, work, out=o), stream,
+                         reps=5, per_rep=50, warmup=10)
+        kv_bytes = 2 * Hkv * d * 2 * ((L - 1) + L)  # K and V rows 0..pos of both streams
+        algo = kv_bytes + 2 * S * H * d * 4 + 2 * S * Hkv * d * 4
+        out[f"attn_twin_h40_kv8_d128_ctx{L}"] = {
+            **st, "kv_bytes": kv_bytes, "algorithmic_bytes": algo,
+            "GBps": round(algo / (st["median_us"] * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(algo / (st["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"attention ctx {L}: {out[f'attn_twin_h40_kv8_d128_ctx{L}']}")
+        del kc, vc, work
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -550,6 +579,7 @@ def main():
         del wqs, wq0
         torch.cuda.empty_cache()
         per_kernel.update(layer_and_graph(torch, pti, dev, stream))
+        per_kernel.update(attention(torch, pti, dev, stream))
     result["per_kernel"] = per_kernel
 
     if not args.no_cpu:

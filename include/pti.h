@@ -75,6 +75,7 @@ extern "C" {
 #define PTI_MAX_VOCAB 2147483647LL
 #define PTI_MAX_ELEMS (1LL << 40)  /* element count limit of the elementwise and norm calls */
 #define PTI_SSQ_VERIFY_WORK_BYTES 16384  /* workspace of pti_gemv_ssq_verify */
+#define PTI_MAX_ATTN_LEN (1LL << 24)      /* KV cache positions per stream */
 
 enum pti_status {
     PTI_OK = 0,
@@ -272,6 +273,38 @@ int pti_silu_mul(const float *g, const float *u, float *y, int64_t n, void *stre
 
 /* y[i] = a[i] + b[i] in fp32 (the residual add), i < n.  y may equal a or b. */
 int pti_add(const float *a, const float *b, float *y, int64_t n, void *stream);
+
+/* ------------------------------------------------------------------------- */
+/* Twin-KV decode attention [Digest, implementation architecture: twins A and
+ * B keep separate KV caches, one pass serves both streams, an accept extends
+ * B's cache and a reject resets B's state; Notes (the LLM-inference page),
+ * from naive inference to the KV cache: a decode step appends the new key
+ * and value and attends over the cache].
+ *
+ * For each stream s < n_streams (each with its own cache):
+ *   1. store: K_s[g][pos[s]] = binary16(k_new[s][g]) and likewise V (round to
+ *      nearest even), replacing the entry there -- a reject's redraw runs at
+ *      the same position and so replaces the stale speculative entry;
+ *   2. attend: out[s][h] = sum_{j <= pos[s]} softmax_j(q[s][h] . K_s[g][j] /
+ *      sqrt(head_dim)) V_s[g][j], with kv head g = h / (n_heads / n_kv_heads).
+ * q: device fp32 [n_streams][n_heads][head_dim]; k_new, v_new: device fp32
+ * [n_streams][n_kv_heads][head_dim]; k_cache, v_cache: HOST arrays
+ * [n_streams] of device binary16 caches [n_kv_heads][max_len][head_dim]
+ * (16-byte aligned, caller-owned, distinct); pos: device int32 [n_streams]
+ * (read on the device, so a captured graph can replay with new positions; a
+ * position outside [0, max_len) makes that stream's outputs NaN and touches
+ * no cache); out: device fp32 [n_streams][n_heads][head_dim]; work: device
+ * scratch of at least pti_attn_workspace_bytes bytes (16-byte aligned), any
+ * contents.
+ * Limits: head_dim 64 or 128; n_heads a multiple of n_kv_heads, at most 8
+ * query heads per kv head; 1 <= max_len <= PTI_MAX_ATTN_LEN.  No output
+ * (out, work, any cache) may overlap an input or another output.  Two
+ * kernels are enqueued on `stream`; calls sharing a workspace must not run
+ * at the same time. */
+size_t pti_attn_workspace_bytes(int n_streams, int n_heads, int n_kv_heads, int head_dim, int64_t max_len);
+int pti_attn_decode(const float *q, const float *k_new, const float *v_new, uint16_t *const *k_cache,
+                    uint16_t *const *v_cache, const int32_t *pos, float *out, int n_streams, int n_heads,
+                    int n_kv_heads, int head_dim, int64_t max_len, void *work, size_t work_bytes, void *stream);
 
 /* ------------------------------------------------------------------------- */
 /* Toy decoder stack and the staggered multi-stream decode loop.

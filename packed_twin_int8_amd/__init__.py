@@ -40,7 +40,7 @@ EXPORTS = (
     "pti_status_str", "pti_last_hip_error", "pti_abi_version", "pti_ssq_bytes", "pti_q8_bytes", "pti_pack_ssq",
     "pti_unpack_ssq", "pti_pack_q8", "pti_unpack_q8", "pti_ssq_split", "pti_ssq_join", "pti_gemv_ssq",
     "pti_gemv_ssq_verify", "pti_gemv_q8_multi", "pti_gemv_ssq_grouped", "pti_gemv_q8_multi_grouped",
-    "pti_gemv_ssq_multi", "pti_verify_argmax", "pti_sample_verify", "pti_embed_q8", "pti_embed_ssq", "pti_rmsnorm",
+    "pti_gemv_ssq_multi", "pti_attn_workspace_bytes", "pti_attn_decode", "pti_verify_argmax", "pti_sample_verify", "pti_embed_q8", "pti_embed_ssq", "pti_rmsnorm",
     "pti_silu_mul", "pti_add", "pti_toy_workspace_bytes", "pti_toy_forward", "pti_toy_decode",
     "pti_toy_forward_graph", "pti_graph_launch", "pti_graph_destroy",
 )
@@ -96,6 +96,9 @@ def lib() -> ctypes.CDLL:
         L.pti_gemv_ssq_verify.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.pti_gemv_q8_multi.argtypes = [_P, _P, _P, _I64, _I64, _INT, _P]
         L.pti_gemv_ssq_multi.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _INT, _P]
+        L.pti_attn_workspace_bytes.argtypes = [_INT, _INT, _INT, _INT, _I64]
+        L.pti_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.pti_attn_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _INT, _INT, _INT, _INT, _I64, _P, ctypes.c_size_t, _P]
         L.pti_gemv_ssq_grouped.argtypes = [_P, _P, _INT, _P, _P, _P, _P, _I64, _P]
         L.pti_gemv_q8_multi_grouped.argtypes = [_P, _P, _INT, _P, _P, _I64, _INT, _P]
         L.pti_verify_argmax.argtypes = [_P, _P, _P, _P, _I64, _INT, _P]
@@ -383,6 +386,43 @@ def gemv_q8_multi_grouped(ws, x, y=None, stream=None):
     _check("pti_gemv_q8_multi_grouped", lib().pti_gemv_q8_multi_grouped(ptrs, rows, len(rows), x.data_ptr(),
                                                                         y.data_ptr(), cols, n, _stream(stream)))
     return y
+
+
+def attn_workspace(n_streams: int, n_heads: int, n_kv_heads: int, head_dim: int, max_len: int, device):
+    """Scratch for attn_decode (no initialisation needed)."""
+    nb = lib().pti_attn_workspace_bytes(n_streams, n_heads, n_kv_heads, head_dim, max_len)
+    if nb == 0:
+        raise PtiError("pti_attn_workspace_bytes", -2)
+    return _torch().empty(nb, dtype=_torch().uint8, device=device)
+
+
+def attn_decode(q, k_new, v_new, k_caches, v_caches, pos, work, out=None, stream=None):
+    """One decode-attention step per stream: store k_new/v_new (rounded to
+    binary16) at pos[s] of stream s's caches, then attend over positions
+    0..pos[s].  q: float32 [S, H, d]; k_new, v_new: float32 [S, Hkv, d];
+    k_caches, v_caches: lists of S float16 tensors [Hkv, max_len, d];
+    pos: int32 [S] (device)."""
+    torch = _torch()
+    _dev(q, "q", torch.float32), _dev(k_new, "k_new", torch.float32), _dev(v_new, "v_new", torch.float32)
+    _dev(pos, "pos", torch.int32), _dev(work, "work", torch.uint8)
+    S, H, d = q.shape
+    Hkv = k_new.shape[1]
+    if k_new.shape != (S, Hkv, d) or v_new.shape != k_new.shape or pos.numel() != S:
+        raise ValueError("attn_decode: shape mismatch")
+    if len(k_caches) != S or len(v_caches) != S:
+        raise ValueError("attn_decode: one K and one V cache per stream")
+    max_len = k_caches[0].shape[1]
+    for i, c in enumerate(list(k_caches) + list(v_caches)):
+        _dev(c, f"cache[{i}]", torch.float16)
+        if c.shape != (Hkv, max_len, d):
+            raise ValueError("attn_decode: caches must be [Hkv, max_len, d]")
+    out = torch.empty_like(q) if out is None else _dev(out, "out", torch.float32)
+    kp = (ctypes.c_void_p * S)(*[c.data_ptr() for c in k_caches])
+    vp = (ctypes.c_void_p * S)(*[c.data_ptr() for c in v_caches])
+    _check("pti_attn_decode", lib().pti_attn_decode(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), kp, vp,
+                                                    pos.data_ptr(), out.data_ptr(), S, H, Hkv, d, max_len,
+                                                    work.data_ptr(), work.numel(), _stream(stream)))
+    return out
 
 
 def verify_argmax(logits, tokens_in, argmax_out=None, accept_out=None, stream=None):

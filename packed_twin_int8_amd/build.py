@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpti.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["pti_host.cpp", "pti_gemv.hip", "pti_verify.hip", "pti_glue.hip", "pti_toy.cpp"]
+SOURCES = ["pti_host.cpp", "pti_gemv.hip", "pti_verify.hip", "pti_glue.hip", "pti_attn.hip", "pti_toy.cpp"]
 ARCH = os.environ.get("PTI_OFFLOAD_ARCH", "gfx950")
 
 COMMON = ["-O3", "-std=c++20", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall"]

@@ -1,0 +1,483 @@
+// Decode attention over per-stream binary16 KV caches, for the twin decode.
+//
+// [Digest = "Packed Twin Inference：无需草稿模型的推测解码新方案，实现2倍吞吐量
+// 提升", section "技术实现架构" (implementation architecture)]: twins A and B
+// keep separate KV caches; one pass serves both streams; an accept extends
+// B's cache and a reject resets B's state.  [Notes = the LLM-inference page,
+// section "从朴素推理到 KV cache" (from naive inference to the KV cache)]: a
+// decode step appends the new token's key and value and attends over the
+// cache.
+//
+// Per stream s (independent caches, one query per head):
+//   store  K_s[g][pos_s] = f16(k_new[s][g]), V_s[g][pos_s] = f16(v_new[s][g])
+//          (round to nearest even), replacing what was there: a reject's
+//          redraw at the same position overwrites the stale entry;
+//   attend out[s][h] = sum_{j <= pos_s} softmax_j(q[s][h] . K_s[g][j] / sqrt(d)) V_s[g][j],
+//          g = h / (n_heads / n_kv_heads) (grouped heads share a kv head).
+//
+// Mapped onto CDNA4 as a split-K "flash decode":
+//   * Pass 1, one workgroup of 256 threads per (key chunk of 256, kv head,
+//     stream); each wave takes 64 keys.  Cache rows are read whole: d/8
+//     lanes cover a row with 16-byte loads, so a load instruction of a wave
+//     reads 64 / (d/8) consecutive rows as one contiguous span, and all of a
+//     wave's K loads (then all its V loads) are in flight together.  A lane
+//     scores its 8 dimensions against every query head of the group (so a
+//     key is read once for all heads that share it) and a DPP row-shift tree
+//     sums the row's lanes.  The chunk's max and exp-sum per head come from
+//     a wave shuffle tree and LDS.  For V a lane sums weight x value over its
+//     rows for its 8 dimensions; the row groups of a wave, then the waves,
+//     combine in a fixed order.  The chunk's (max, sum, weighted V) per head
+//     go to the workspace.  The chunk holding pos_s stores the new entry and
+//     uses the rounded values itself, so no pass reads what another writes.
+//   * Pass 2, one workgroup per (head, stream): the chunks up to pos_s
+//     combine, rescaled by exp(m_c - M), in a fixed grouping of chunks.
+// Every sum runs in a fixed order that depends on the shapes and pos_s only.
+// Chunks past a stream's position exit at once; the grid covers max_len so
+// positions can live in device memory (capturable in a graph).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "pti_internal.h"
+
+namespace {
+
+constexpr int kChunk = 256;     // keys per pass-1 workgroup (one per thread)
+constexpr int kThreads = 256;
+constexpr int kMaxGroup = 8;    // query heads per kv head
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct AttnArgs {
+    const float *q;       // [S][H][d]
+    const float *k_new;   // [S][Hkv][d]
+    const float *v_new;
+    uint16_t *kc[PTI_MAX_STREAMS];  // [Hkv][max_len][d] binary16
+    uint16_t *vc[PTI_MAX_STREAMS];
+    const int32_t *pos;   // [S]
+    float *out;           // [S][H][d]
+    float *part;          // [S][H][n_chunks][d]: weighted V per chunk
+    float *ml;            // [S][H][n_chunks][2]: max, exp-sum per chunk (after part)
+    int H, Hkv, n_chunks;
+    int64_t max_len;
+    float scale;          // 1 / sqrt(d)
+};
+
+__device__ __forceinline__ float h2f(uint32_t bits16) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16); }
+
+__device__ __forceinline__ uint16_t f2h(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_add(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Position of stream s, or -1 when outside the cache (the pass then writes
+// NaN outputs and touches no cache memory).
+__device__ __forceinline__ int64_t stream_pos(const AttnArgs &a, int s)
+{
+    const int64_t p = a.pos[s];
+    return (p >= 0 && p < a.max_len) ? p : -1;
+}
+
+// v + the value DPP moves into each lane (row_shr by CTRL - 0x110 lanes with
+// bound_ctrl, so lanes with no source within the 16-lane row add 0).
+template <int CTRL>
+__device__ __forceinline__ float add_shr(float v)
+{
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf,
+                                                                     true));
+}
+
+// Sum over each aligned group of N lanes (N = 8 or 16) of a 16-lane row; the
+// group's last lane holds it.  A fixed tree of row shifts.
+template <int N>
+__device__ __forceinline__ float group_sum(float v)
+{
+    v = add_shr<0x111>(v);
+    v = add_shr<0x112>(v);
+    v = add_shr<0x114>(v);
+    if constexpr (N == 16)
+        v = add_shr<0x118>(v);
+    return v;
+}
+
+// The 8 halves of a uint4 as floats.
+__device__ __forceinline__ void unpack8(const uint4 t, float (&f)[8])
+{
+    const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+        f[2 * e] = h2f(w[e] & 0xFFFFu), f[2 * e + 1] = h2f(w[e] >> 16);
+}
+
+// 8 consecutive fp32 values rounded to binary16, packed as they are stored.
+__device__ __forceinline__ uint4 pack8(const float *x)
+{
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+        w[e] = (uint32_t)f2h(x[2 * e]) | ((uint32_t)f2h(x[2 * e + 1]) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a)
+{
+    constexpr int LPR = D / 8;                  // lanes per cache row: 16 bytes (8 halves) each
+    constexpr int RPI = 64 / LPR;               // rows one load instruction of a wave covers
+    constexpr int NW = kThreads / 64;
+    constexpr int KPW = kChunk / NW;            // keys per wave
+    constexpr int IT = KPW / RPI;               // loads per wave per tile
+    __shared__ float ps[G][kChunk];             // scores, then weights
+    __shared__ float red[G][NW];
+    __shared__ float vpart[NW][G][D];
+    const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t pos = stream_pos(a, s);
+    if (pos < 0 || (int64_t)c * kChunk > pos)
+        return;  // nothing of this stream in this chunk
+    const int64_t j0 = (int64_t)c * kChunk;
+    const int nk = (int)min<int64_t>(kChunk, pos + 1 - j0);  // keys in this chunk
+    const bool has_new = pos < j0 + kChunk;                  // the new entry is in this chunk
+    const uint16_t *K = a.kc[s] + ((size_t)g * a.max_len) * D;
+    const uint16_t *V = a.vc[s] + ((size_t)g * a.max_len) * D;
+    const float *kn = a.k_new + ((size_t)s * a.Hkv + g) * D;
+    const float *vn = a.v_new + ((size_t)s * a.Hkv + g) * D;
+    const int r = lane / LPR, seg = lane % LPR;  // row within a load, 8-dimension segment
+
+    // ---- K tile: rows are read whole and in order (LPR lanes x 16 bytes),
+    // every load of the wave in flight at once; the new key (rounded as it
+    // is stored) stands in for the cache row at pos
+    // Buffer resources over the chunk's valid rows: rows past them read 0
+    // without a branch, so no load waits on another.
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(K + (size_t)j0 * D), (short)0, nk * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(V + (size_t)j0 * D), (short)0, nk * D * 2, 0x00020000);
+    const int newkey = has_new ? (int)(pos - j0) : -1;  // chunk index of the new entry
+    uint4 kn8 = make_uint4(0, 0, 0, 0), vn8 = make_uint4(0, 0, 0, 0);
+    if (has_new)  // uniform
+        kn8 = pack8(kn + 8 * seg), vn8 = pack8(vn + 8 * seg);
+    uint4 kt[IT];
+#pragma unroll
+    for (int it = 0; it < IT; it++) {
+        const int key = wv * KPW + it * RPI + r;
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(krs, (key * D + 8 * seg) * 2, 0, 0);
+        kt[it] = make_uint4(t[0], t[1], t[2], t[3]);
+    }
+    float qv[G][8];
+#pragma unroll
+    for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            qv[h][e] = a.q[((size_t)s * a.H + (size_t)g * G + h) * D + 8 * seg + e];
+
+    // ---- scores: 8 dimensions per lane, then the row's LPR lanes
+#pragma unroll
+    for (int it = 0; it < IT; it++) {
+        const int key = wv * KPW + it * RPI + r;
+        float k8[8];
+        unpack8(key == newkey ? kn8 : kt[it], k8);
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            float d = qv[h][0] * k8[0];
+#pragma unroll
+            for (int e = 1; e < 8; e++)
+                d = __builtin_fmaf(qv[h][e], k8[e], d);
+            d = group_sum<LPR>(d);
+            if (seg == LPR - 1 && key < nk)
+                ps[h][key] = d * a.scale;
+        }
+    }
+
+    // ---- V tile: issued now so the loads overlap the softmax
+    uint4 vt[IT];
+#pragma unroll
+    for (int it = 0; it < IT; it++) {
+        const int key = wv * KPW + it * RPI + r;
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(vrs, (key * D + 8 * seg) * 2, 0, 0);
+        vt[it] = make_uint4(t[0], t[1], t[2], t[3]);
+    }
+    __syncthreads();
+
+    // ---- chunk max and exp-sum per head (thread tid: key tid)
+    float sc[G], m[G];
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        sc[h] = tid < nk ? ps[h][tid] : -INFINITY;
+        const float wm = wave_max(sc[h]);
+        if (lane == 0)
+            red[h][wv] = wm;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        float v = red[h][0];
+#pragma unroll
+        for (int w = 1; w < NW; w++)
+            v = fmaxf(v, red[h][w]);
+        m[h] = v;
+    }
+    __syncthreads();  // red is reused below
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        const float p = tid < nk ? expf(sc[h] - m[h]) : 0.f;
+        ps[h][tid] = p;  // only this thread reads or writes index tid
+        const float ws = wave_add(p);
+        if (lane == 0)
+            red[h][wv] = ws;
+    }
+    __syncthreads();
+
+    // ---- weighted V: a lane sums its 8 dimensions over its rows, then the
+    // RPI row groups of the wave combine (xor butterfly), then the waves
+    float acc[G][8];
+#pragma unroll
+    for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            acc[h][e] = 0.f;
+#pragma unroll
+    for (int it = 0; it < IT; it++) {
+        const int key = wv * KPW + it * RPI + r;
+        float v8[8];
+        unpack8(key == newkey ? vn8 : vt[it], v8);
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            const float p = key < nk ? ps[h][key] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                acc[h][e] = __builtin_fmaf(p, v8[e], acc[h][e]);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+#pragma unroll
+            for (int off = LPR; off < 64; off <<= 1)
+                acc[h][e] += __shfl_xor(acc[h][e], off, 64);
+            if (r == 0)
+                vpart[wv][h][8 * seg + e] = acc[h][e];
+        }
+    __syncthreads();
+
+    // ---- chunk partials: weighted V (waves in order), max, sum
+    for (int i = tid; i < G * D; i += kThreads) {
+        const int h = i / D, d = i % D;
+        float v = vpart[0][h][d];
+#pragma unroll
+        for (int w = 1; w < NW; w++)
+            v += vpart[w][h][d];
+        a.part[(((size_t)s * a.H + (size_t)g * G + h) * a.n_chunks + c) * D + d] = v;
+    }
+    if (tid < G) {
+        float l = red[tid][0];
+#pragma unroll
+        for (int w = 1; w < NW; w++)
+            l += red[tid][w];
+        float *pp = a.ml + (((size_t)s * a.H + (size_t)g * G + tid) * a.n_chunks + c) * 2;
+        pp[0] = m[tid];
+        pp[1] = l;
+    }
+
+    // ---- store the new entry (the chunk that holds pos; every reader of
+    // this position in this pass used the rounded values above)
+    if (has_new) {
+        uint16_t *kd = a.kc[s] + ((size_t)g * a.max_len + pos) * D;
+        uint16_t *vd = a.vc[s] + ((size_t)g * a.max_len + pos) * D;
+        for (int i = tid; i < D; i += kThreads) {
+            kd[i] = f2h(kn[i]);
+            vd[i] = f2h(vn[i]);
+        }
+    }
+}
+
+// Pass 2: the chunks of (head, stream) combine.  The chunk maxima are read
+// in parallel and reduced to M; then thread (cg, dg) sums, over chunks cg,
+// cg + CG, ..., the 16-byte slice dg of the chunks' weighted V rows scaled by
+// exp(m_c - M) (and the exp-sums likewise); the chunk groups add in order.
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a)
+{
+    constexpr int DG = D / 4;          // float4 slices of a row
+    constexpr int CG = kThreads / DG;  // chunk groups
+    __shared__ float redm[kThreads / 64];
+    __shared__ float4 vsum[CG][DG];
+    __shared__ float lsum[CG];
+    const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    float *o = a.out + ((size_t)s * a.H + h) * D;
+    const int64_t pos = stream_pos(a, s);
+    if (pos < 0) {
+        if (tid < D)
+            o[tid] = NAN;
+        return;
+    }
+    const int nc = (int)(pos / kChunk) + 1;
+    const float *pv = a.part + ((size_t)s * a.H + h) * a.n_chunks * D;
+    const float *pm = a.ml + ((size_t)s * a.H + h) * a.n_chunks * 2;
+    float mx = -INFINITY;
+    for (int c = tid; c < nc; c += kThreads)
+        mx = fmaxf(mx, pm[2 * c]);
+    mx = wave_max(mx);
+    if (lane == 0)
+        redm[wv] = mx;
+    __syncthreads();
+    float M = redm[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; w++)
+        M = fmaxf(M, redm[w]);
+    const int dg = tid % DG, cg = tid / DG;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float l = 0.f;
+#pragma unroll 4
+    for (int c = cg; c < nc; c += CG) {
+        const float f = expf(pm[2 * c] - M);
+        l = __builtin_fmaf(pm[2 * c + 1], f, l);
+        const float4 v = reinterpret_cast<const float4 *>(pv + (size_t)c * D)[dg];
+        acc.x = __builtin_fmaf(v.x, f, acc.x);
+        acc.y = __builtin_fmaf(v.y, f, acc.y);
+        acc.z = __builtin_fmaf(v.z, f, acc.z);
+        acc.w = __builtin_fmaf(v.w, f, acc.w);
+    }
+    vsum[cg][dg] = acc;
+    if (dg == 0)
+        lsum[cg] = l;
+    __syncthreads();
+    if (tid < DG) {
+        float4 t = vsum[0][tid];
+        float L = lsum[0];
+#pragma unroll
+        for (int k = 1; k < CG; k++) {
+            const float4 u = vsum[k][tid];
+            t.x += u.x, t.y += u.y, t.z += u.z, t.w += u.w;
+            L += lsum[k];
+        }
+        o[4 * tid] = t.x / L;
+        o[4 * tid + 1] = t.y / L;
+        o[4 * tid + 2] = t.z / L;
+        o[4 * tid + 3] = t.w / L;
+    }
+}
+
+template <int D, int G>
+void launch_g(const AttnArgs &a, int S, hipStream_t st)
+{
+    hipLaunchKernelGGL((attn_partial_kernel<D, G>), dim3((unsigned)a.n_chunks, (unsigned)a.Hkv, (unsigned)S),
+                       dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)a.H, (unsigned)S), dim3(kThreads), 0, st, a);
+}
+
+template <int D>
+void launch_d(const AttnArgs &a, int G, int S, hipStream_t st)
+{
+    switch (G) {
+    case 1: return launch_g<D, 1>(a, S, st);
+    case 2: return launch_g<D, 2>(a, S, st);
+    case 3: return launch_g<D, 3>(a, S, st);
+    case 4: return launch_g<D, 4>(a, S, st);
+    case 5: return launch_g<D, 5>(a, S, st);
+    case 6: return launch_g<D, 6>(a, S, st);
+    case 7: return launch_g<D, 7>(a, S, st);
+    default: return launch_g<D, 8>(a, S, st);
+    }
+}
+
+int64_t n_chunks(int64_t max_len) { return (max_len + kChunk - 1) / kChunk; }
+
+bool attn_shape_ok(int n_streams, int n_heads, int n_kv_heads, int head_dim, int64_t max_len)
+{
+    return n_streams >= 1 && n_streams <= PTI_MAX_STREAMS && n_kv_heads >= 1 && n_heads >= n_kv_heads &&
+           n_heads % n_kv_heads == 0 && n_heads / n_kv_heads <= kMaxGroup && n_heads <= 65535 &&
+           (head_dim == 64 || head_dim == 128) && max_len >= 1 && max_len <= PTI_MAX_ATTN_LEN;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pti_attn_workspace_bytes(int n_streams, int n_heads, int n_kv_heads, int head_dim, int64_t max_len)
+{
+    if (!attn_shape_ok(n_streams, n_heads, n_kv_heads, head_dim, max_len))
+        return 0;
+    return (size_t)n_streams * n_heads * (size_t)n_chunks(max_len) * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+int pti_attn_decode(const float *q, const float *k_new, const float *v_new, uint16_t *const *k_cache,
+                    uint16_t *const *v_cache, const int32_t *pos, float *out, int n_streams, int n_heads,
+                    int n_kv_heads, int head_dim, int64_t max_len, void *work, size_t work_bytes, void *stream)
+{
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !pos || !out || !work)
+        return PTI_ERR_NULL;
+    if (n_streams < 1 || n_streams > PTI_MAX_STREAMS)
+        return PTI_ERR_NSTREAMS;
+    if (!attn_shape_ok(n_streams, n_heads, n_kv_heads, head_dim, max_len))
+        return PTI_ERR_SHAPE;
+    const size_t need = pti_attn_workspace_bytes(n_streams, n_heads, n_kv_heads, head_dim, max_len);
+    if (work_bytes < need)
+        return PTI_ERR_SHAPE;
+    const size_t d = (size_t)head_dim, S = (size_t)n_streams;
+    const size_t cache_bytes = (size_t)n_kv_heads * (size_t)max_len * d * 2;
+    if (!pti::aligned(q, 4) || !pti::aligned(k_new, 4) || !pti::aligned(v_new, 4) || !pti::aligned(pos, 4) ||
+        !pti::aligned(out, 4) || !pti::aligned(work, 16))
+        return PTI_ERR_ALIGN;
+    for (int s = 0; s < n_streams; s++) {
+        if (!k_cache[s] || !v_cache[s])
+            return PTI_ERR_NULL;
+        if (!pti::aligned(k_cache[s], 16) || !pti::aligned(v_cache[s], 16))
+            return PTI_ERR_ALIGN;
+    }
+    // outputs: out, work, every cache; inputs: q, k_new, v_new, pos
+    const pti::Range ins[] = {{q, S * n_heads * d * 4}, {k_new, S * n_kv_heads * d * 4},
+                              {v_new, S * n_kv_heads * d * 4}, {pos, S * 4}};
+    pti::Range outs[2 + 2 * PTI_MAX_STREAMS];
+    int no = 0;
+    outs[no++] = {out, S * n_heads * d * 4};
+    outs[no++] = {work, need};
+    for (int s = 0; s < n_streams; s++) {
+        outs[no++] = {k_cache[s], cache_bytes};
+        outs[no++] = {v_cache[s], cache_bytes};
+    }
+    for (int i = 0; i < no; i++) {
+        for (int j = i + 1; j < no; j++)
+            if (pti::overlap(outs[i], outs[j]))
+                return PTI_ERR_OVERLAP;
+        for (const pti::Range &in : ins)
+            if (pti::overlap(outs[i], in))
+                return PTI_ERR_OVERLAP;
+    }
+    AttnArgs a{};
+    a.q = q, a.k_new = k_new, a.v_new = v_new, a.pos = pos, a.out = out;
+    for (int s = 0; s < n_streams; s++)
+        a.kc[s] = k_cache[s], a.vc[s] = v_cache[s];
+    a.H = n_heads, a.Hkv = n_kv_heads, a.n_chunks = (int)n_chunks(max_len), a.max_len = max_len;
+    a.part = static_cast<float *>(work);
+    a.ml = a.part + S * (size_t)n_heads * (size_t)a.n_chunks * d;
+    a.scale = 1.0f / sqrtf((float)head_dim);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int G = n_heads / n_kv_heads;
+    if (head_dim == 64)
+        launch_d<64>(a, G, n_streams, st);
+    else
+        launch_d<128>(a, G, n_streams, st);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        pti::set_hip_error(e);
+        return PTI_ERR_HIP;
+    }
+    return PTI_OK;
+}
+
+}  // extern "C"

@@ -211,6 +211,37 @@ def test_gemv_ssq_multi_errors():
     assert f(_fake(A0), _fake(A1), _fake(A4), _fake(A4 + 256), _fake(A3), 8, 64, 2, None) == OVERLAP
 
 
+def test_attn_errors():
+    L = pti.lib()
+    ws = L.pti_attn_workspace_bytes
+    assert ws(2, 40, 8, 128, 4096) == 2 * 40 * 16 * 130 * 4
+    assert ws(0, 8, 2, 128, 16) == 0 and ws(5, 8, 2, 128, 16) == 0
+    assert ws(1, 8, 3, 128, 16) == 0 and ws(1, 18, 2, 128, 16) == 0  # not a multiple; 9 heads per kv head
+    assert ws(1, 8, 2, 96, 16) == 0 and ws(1, 8, 2, 128, 0) == 0 and ws(1, 8, 2, 128, (1 << 24) + 1) == 0
+    f = L.pti_attn_decode
+    C0, C1 = 0x70000000, 0x71000000
+    KP = (ctypes.c_void_p * 1)(C0)
+    VP = (ctypes.c_void_p * 1)(C1)
+    W = 1 << 20
+
+    def call(q=A0, kn=A1, vn=A2, kp=KP, vp=VP, pos=A3, out=A4, S=1, H=8, Hkv=2, d=64, L_=16, wk=0x72000000, wb=W):
+        return f(_fake(q) if q else None, _fake(kn), _fake(vn), kp, vp, _fake(pos), _fake(out), S, H, Hkv, d, L_,
+                 _fake(wk) if wk else None, wb, None)
+
+    assert call(q=0) == NULL and call(wk=0) == NULL and call(kp=None) == NULL
+    assert call(kp=(ctypes.c_void_p * 1)(0)) == NULL
+    assert call(S=0) == NSTREAMS and call(S=5) == NSTREAMS
+    assert call(d=96) == SHAPE and call(Hkv=3) == SHAPE and call(L_=0) == SHAPE
+    assert call(wb=64) == SHAPE
+    assert call(kp=(ctypes.c_void_p * 1)(C0 + 8)) == ALIGN
+    assert call(out=A4 + 2) == ALIGN
+    assert call(wk=0x72000000 + 4) == ALIGN
+    # the V cache over the K cache; out over q; the workspace over a cache
+    assert call(vp=(ctypes.c_void_p * 1)(C0 + 64)) == OVERLAP
+    assert call(out=A0 + 64) == OVERLAP
+    assert call(wk=C1 + 128) == OVERLAP
+
+
 def test_gemv_q8_errors():
     L = pti.lib()
     f = L.pti_gemv_q8_multi
