@@ -101,7 +101,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "gemv_ssq_verify_17408x5120_pmc.txt")
 KT_FILE = os.path.join(HERE, "profiles", "gemv_ssq_q8_17408x5120_kernel_stats.md")
 # the step's kernels, as rocprofv3 names them (template arguments kept)
-STEP_KERNELS = ("gemv_ssq_split_kernel<5, true>", "verify_keys_kernel")
+STEP_KERNELS = ("gemv_ssq_split_kernel<5, 2, true, 8>", "verify_keys_kernel")
 KERNEL_SOURCES = ("packed_twin_int8_amd/csrc/pti_gemv.hip", "packed_twin_int8_amd/build.py")
 PROFILE_CMDS = {
     "kt": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_kt -o kt -- python3 bench.py --no-cpu",
@@ -197,13 +197,19 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, out_dir):
     """Turn rocprofv3 CSV output into the text summaries kept under profiles/."""
     src_hash = kernel_source_hash()
     kt = _csv_rows(kt_dir, "kernel_stats.csv")
-    lines = ["# rocprofv3 kernel-trace statistics: bench.py default run (fused SSQ twin GEMV 17408x5120 + verify,",
-             "# the unfused GEMV and verify, then Q8 multi-stream GEMV 17408x5120 at N=1,2,4), one MI355X",
+    lines = ["# rocprofv3 kernel-trace statistics: bench.py default run on one MI355X: the fused SSQ twin GEMV",
+             "# 17408x5120 + verify (the step), the unfused GEMV and verify, SSQ with two streams per twin, Q8",
+             "# multi-stream GEMV 17408x5120 at N=1,2,4, a decoder layer's GEMVs (separate, grouped, graph), the",
+             "# toy decoder forward pass, and twin-KV attention at 4K and 32K positions.  A kernel's row mixes",
+             "# every shape it ran; the step's kernels (gemv_ssq_split_kernel<5, 2, true, 8>, verify_keys_kernel)",
+             "# run only in the step.",
              "", "command: " + PROFILE_CMDS["kt"], "summary: " + PROFILE_CMDS["summary"],
              "kernel_source_sha256: " + src_hash, "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in kt:
-        lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+        name = _short(r["Name"])
+        name = name if len(name) <= 100 else name[:97] + "..."
+        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
                      f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.2f} |")
     os.makedirs(out_dir, exist_ok=True)
     with open(os.path.join(out_dir, "gemv_ssq_q8_17408x5120_kernel_stats.md"), "w") as f:
@@ -529,7 +535,7 @@ def main():
         "frac_of_hbm_peak": round(w_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "pti_gemv_ssq_verify = gemv_ssq_split_kernel<5, true> + verify_keys_kernel",
+            "kernel": "pti_gemv_ssq_verify = gemv_ssq_split_kernel<5, 2, true, 8> + verify_keys_kernel",
             "achieved": round(algo_bytes / (ms_fused * 1e-3) / 1e9, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

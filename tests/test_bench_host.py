@@ -29,7 +29,7 @@ def _write_csv(path, header, rows):
         w.writerows(rows)
 
 
-SPLIT = "void (anonymous namespace)::gemv_ssq_split_kernel<5, true>(SplitArgs)"
+SPLIT = "void (anonymous namespace)::gemv_ssq_split_kernel<5, 2, true, 8>(SplitArgs)"
 KEYS = "void (anonymous namespace)::verify_keys_kernel(unsigned long long const*, int, int const*, int*, int*)"
 NEG = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>(int, float*)"
 
@@ -54,7 +54,7 @@ def test_summarize_profiles(tmp_path, monkeypatch):
     # (1001 + 4) KiB and (100 + 2) KiB per call, times the calibration factor 2
     assert t["fetch_bytes"] == round(1005.0 * 1024 * 2) and t["write_bytes"] == round(102.0 * 1024 * 2)
     assert t["bytes"] == t["fetch_bytes"] + t["write_bytes"]
-    assert bench.read_kernel_avgs() == {"gemv_ssq_split_kernel<5, true>": 33.6, "verify_keys_kernel": 1.0}
+    assert bench.read_kernel_avgs() == {"gemv_ssq_split_kernel<5, 2, true, 8>": 33.6, "verify_keys_kernel": 1.0}
     # a summary taken from other sources is not used
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
     assert bench.read_traffic() is None and bench.read_kernel_avgs() is None
