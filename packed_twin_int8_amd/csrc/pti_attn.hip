@@ -16,8 +16,8 @@
 //          g = h / (n_heads / n_kv_heads) (grouped heads share a kv head).
 //
 // Mapped onto CDNA4 as a split-K "flash decode":
-//   * Pass 1, one workgroup of 256 threads per (key chunk of 256, kv head,
-//     stream); each wave takes 64 keys.  Cache rows are read whole: d/8
+//   * Pass 1, one workgroup of 256 threads per (key chunk of 128, kv head,
+//     stream); each wave takes 32 keys.  Cache rows are read whole: d/8
 //     lanes cover a row with 16-byte loads, so a load instruction of a wave
 //     reads 64 / (d/8) consecutive rows as one contiguous span, and all of a
 //     wave's K loads (then all its V loads) are in flight together.  A lane
@@ -42,7 +42,7 @@
 
 namespace {
 
-constexpr int kChunk = 256;     // keys per pass-1 workgroup (one per thread)
+constexpr int kChunk = 128;     // keys per pass-1 workgroup
 constexpr int kThreads = 256;
 constexpr int kMaxGroup = 8;    // query heads per kv head
 
@@ -105,6 +105,7 @@ __device__ __forceinline__ float add_shr(float v)
 template <int N>
 __device__ __forceinline__ float group_sum(float v)
 {
+    static_assert(N == 8 || N == 16, "group size");
     v = add_shr<0x111>(v);
     v = add_shr<0x112>(v);
     v = add_shr<0x114>(v);
@@ -212,11 +213,11 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a)
     }
     __syncthreads();
 
-    // ---- chunk max and exp-sum per head (thread tid: key tid)
+    // ---- chunk max and exp-sum per head (thread tid: key tid, if any)
     float sc[G], m[G];
 #pragma unroll
     for (int h = 0; h < G; h++) {
-        sc[h] = tid < nk ? ps[h][tid] : -INFINITY;
+        sc[h] = tid < nk ? ps[h][tid] : -INFINITY;  // nk <= kChunk
         const float wm = wave_max(sc[h]);
         if (lane == 0)
             red[h][wv] = wm;
@@ -234,7 +235,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a)
 #pragma unroll
     for (int h = 0; h < G; h++) {
         const float p = tid < nk ? expf(sc[h] - m[h]) : 0.f;
-        ps[h][tid] = p;  // only this thread reads or writes index tid
+        if (tid < kChunk)
+            ps[h][tid] = p;  // only this thread reads or writes index tid
         const float ws = wave_add(p);
         if (lane == 0)
             red[h][wv] = ws;
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a)
         unpack8(key == newkey ? vn8 : vt[it], v8);
 #pragma unroll
         for (int h = 0; h < G; h++) {
-            const float p = key < nk ? ps[h][key] : 0.f;
+            const float p = ps[h][key];  // 0 past the chunk's keys (and their rows read 0)
 #pragma unroll
             for (int e = 0; e < 8; e++)
                 acc[h][e] = __builtin_fmaf(p, v8[e], acc[h][e]);

@@ -25,7 +25,7 @@ from oracle import attention as A
 
 pytestmark = pytest.mark.gpu
 U = 2.0 ** -24
-CHUNK = 256
+CHUNK = 128
 
 
 @pytest.fixture(scope="module")

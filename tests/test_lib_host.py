@@ -214,7 +214,7 @@ def test_gemv_ssq_multi_errors():
 def test_attn_errors():
     L = pti.lib()
     ws = L.pti_attn_workspace_bytes
-    assert ws(2, 40, 8, 128, 4096) == 2 * 40 * 16 * 130 * 4
+    assert ws(2, 40, 8, 128, 4096) == 2 * 40 * 32 * 130 * 4  # 128-key chunks
     assert ws(0, 8, 2, 128, 16) == 0 and ws(5, 8, 2, 128, 16) == 0
     assert ws(1, 8, 3, 128, 16) == 0 and ws(1, 18, 2, 128, 16) == 0  # not a multiple; 9 heads per kv head
     assert ws(1, 8, 2, 96, 16) == 0 and ws(1, 8, 2, 128, 0) == 0 and ws(1, 8, 2, 128, (1 << 24) + 1) == 0
