@@ -354,6 +354,28 @@ def layer_and_graph(torch, pti, dev, stream):
                                 "gemv_weight_bytes": wbytes,
                                 "graph_weight_GBps": round(wbytes / (st_g["median_us"] * 1e-6) / 1e9, 1)}
     log(f"toy forward: {out['toy_forward_q8_n4']}")
+
+    # the staggered twin-decode loop itself (greedy, 64 steps, the host reads
+    # each step's draws back), N = 1 and N = 4 streams
+    for n in (1, 4):
+        w_n = stack.workspace(n)
+        stack.decode(1, n, 4, work=w_n)  # warm-up
+        torch.cuda.synchronize()
+        reps = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            committed, accepts, passes = stack.decode(1, n, 64, work=w_n)
+            reps.append(time.perf_counter() - t0)
+        t = sorted(reps)[2]
+        # passes rows are (step, slot, stream, input, output): an N-stream pass
+        # has slots 0..N-1, a single-stream (ramp-up or redraw) pass a slot >= N
+        fwd = 64 + int((passes[:, 1] >= n).sum()) if n > 1 else 64
+        out[f"toy_decode_q8_n{n}_64steps"] = {
+            "ms": round(t * 1e3, 3), "forward_passes": fwd, "us_per_step": round(t / 64 * 1e6, 2),
+            "us_per_forward_pass": round(t / fwd * 1e6, 2),
+            "steps_per_s": round(64 / t, 1),  # one committed token per step (stream 0's draw)
+            "mean_accept": round(float(accepts.mean()), 3)}  # the pages' tokens per step, 1 + p + p^2 + ...
+        log(f"toy decode n={n}: {out[f'toy_decode_q8_n{n}_64steps']}")
     return out
 
 

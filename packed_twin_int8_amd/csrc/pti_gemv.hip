@@ -102,6 +102,7 @@ struct GemvArgs {
     int64_t seg_end[kMaxSegs];  // INT64_MAX from the last segment on
     const float *x[4];
     float *y[4];
+    const float *res[4];   // when set: y[s][r] = res[s][r] + (W x[s])[r] (res may be y itself)
     int64_t rows;
     int64_t row_bytes;
     int32_t cols;
@@ -550,7 +551,7 @@ struct Wave {
             const int64_t row = first + (int64_t)(gp0 * R + lane) * stride;
 #pragma unroll
             for (int s = 0; s < NS; s++)
-                a.y[s][row] = outv[s];
+                a.y[s][row] = a.res[s] ? a.res[s][row] + outv[s] : outv[s];
         }
     }
 };
@@ -892,6 +893,8 @@ __global__ __launch_bounds__(64 * BW) void gemv_ssq_split_kernel(SplitArgs sa)
                 float acc = part[(slot * Q) * NS + s];
                 for (int j = 1; j < Q; j++)
                     acc += part[((slot * Q) + j) * NS + s];
+                if (a.res[s])
+                    acc = a.res[s][g + m * G] + acc;
                 a.y[s][g + m * G] = acc;
                 if constexpr (VERIFY)
                     vkey[s & 1] = std::max(vkey[s & 1], verify_key(acc, g + m * G));
@@ -1317,3 +1320,29 @@ int pti_gemv_q8_multi_grouped(const void *const *w_q8, const int64_t *rows, int 
 }
 
 }  // extern "C"
+
+namespace pti {
+
+int gemv_q8_res(const void *w, const float *x, float *y, const float *res, int64_t rows, int64_t cols, int n,
+                void *stream)
+{
+    GemvArgs a = make_args<kQ8>(w, rows, cols);
+    for (int s = 0; s < n; s++) {
+        a.x[s] = x + (size_t)s * cols;
+        a.y[s] = y + (size_t)s * rows;
+        a.res[s] = res + (size_t)s * rows;
+    }
+    return launch_q8(a, n, static_cast<hipStream_t>(stream));
+}
+
+int gemv_ssq_res(const void *w, const float *x_a, const float *x_b, float *y_a, float *y_b, const float *res_a,
+                 const float *res_b, int64_t rows, int64_t cols, void *stream)
+{
+    GemvArgs a = make_args<kSSQ>(w, rows, cols);
+    a.x[0] = x_a, a.x[1] = x_b;
+    a.y[0] = y_a, a.y[1] = y_b;
+    a.res[0] = res_a, a.res[1] = res_b;
+    return launch_ssq(a, 1, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace pti

@@ -136,6 +136,18 @@ __global__ void silu_mul_kernel(const float *g, const float *u, float *y, int64_
     }
 }
 
+// The same arithmetic on the rows of a stacked gate|up output: g = gu[s][j],
+// u = gu[s][cols + j].
+__global__ void silu_mul_rows_kernel(const float *gu, float *y, int64_t rows, int64_t cols)
+{
+    const int64_t n = rows * cols;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t s = i / cols, j = i - s * cols;
+        const double gv = gu[s * 2 * cols + j];
+        y[i] = float(gv / (1.0 + exp(-gv)) * double(gu[s * 2 * cols + cols + j]));
+    }
+}
+
 __global__ void add_kernel(const float *a, const float *b, float *y, int64_t n)
 {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
@@ -349,6 +361,15 @@ extern "C" int pti_silu_mul(const float *g, const float *u, float *y, int64_t n,
                        u, y, n);
     return launch_status();
 }
+
+namespace pti {
+int launch_silu_mul_rows(const float *gu, float *y, int64_t rows, int64_t cols, void *stream)
+{
+    hipLaunchKernelGGL(silu_mul_rows_kernel, dim3(elementwise_grid(rows * cols)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), gu, y, rows, cols);
+    return launch_status();
+}
+}  // namespace pti
 
 extern "C" int pti_add(const float *a, const float *b, float *y, int64_t n, void *stream)
 {

@@ -35,6 +35,19 @@ struct StreamRows {
 int launch_verify_rows(const StreamRows &lg, const int32_t *tokens_in, int32_t *argmax_out, int32_t *accept_out,
                        int64_t vocab, int n_streams, void *stream);
 
+// GEMVs whose outputs add a residual: y[s][r] = res[s][r] + (W x_s)[r], the
+// same fp32 addition pti_add makes; res may be y itself (each element is read
+// before it is written, by the same thread).  Arguments already validated.
+int gemv_q8_res(const void *w, const float *x, float *y, const float *res, int64_t rows, int64_t cols, int n,
+                void *stream);
+int gemv_ssq_res(const void *w, const float *x_a, const float *x_b, float *y_a, float *y_b, const float *res_a,
+                 const float *res_b, int64_t rows, int64_t cols, void *stream);
+
+// y[s][j] = silu(gu[s][j]) * gu[s][cols + j] for s < rows, j < cols (rows of
+// 2 cols: the stacked output of a grouped gate|up GEMV), as pti_silu_mul
+// computes it.  Arguments already validated.
+int launch_silu_mul_rows(const float *gu, float *y, int64_t rows, int64_t cols, void *stream);
+
 inline bool overlap(Range a, Range b)
 {
     if (a.n == 0 || b.n == 0)

@@ -31,7 +31,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
-    size_t h, r, g, u, d, logits, tok, out, acc, uni, total;
+    size_t h, r, gu, x, logits, tok, out, acc, uni, total;
 };
 
 Layout layout(const pti_toy_model &m, int n)
@@ -46,9 +46,8 @@ Layout layout(const pti_toy_model &m, int n)
     const size_t N = size_t(n);
     L.h = take(N * size_t(m.hidden) * 4);
     L.r = take(N * size_t(m.hidden) * 4);
-    L.g = take(N * size_t(m.ffn) * 4);
-    L.u = take(N * size_t(m.ffn) * 4);
-    L.d = take(N * size_t(m.hidden) * 4);
+    L.gu = take(N * 2 * size_t(m.ffn) * 4);  // stacked gate|up outputs, [N][2F]
+    L.x = take(N * size_t(m.ffn) * 4);
     L.logits = take(N * size_t(m.vocab) * 4);
     L.tok = take(PTI_MAX_STREAMS * 4);
     L.out = take(PTI_MAX_STREAMS * 4);
@@ -108,24 +107,34 @@ int gemv(const pti_toy_model &m, const void *w, const float *x, float *y, int64_
 }
 
 // Enqueues one pass; logits may point into the workspace or outside it.
+// Per layer: rmsnorm; gate and up in one grouped launch (outputs stacked per
+// stream); silu(gate) * up; down with the residual added as the rows are
+// stored.  Each step's results are bitwise those of the separate calls
+// (gate, up, silu_mul, down, add).
 int forward(const pti_toy_model &m, const Layout &L, char *work, const int32_t *tokens, float *logits, int n,
             void *stream)
 {
     float *h = reinterpret_cast<float *>(work + L.h), *r = reinterpret_cast<float *>(work + L.r);
-    float *g = reinterpret_cast<float *>(work + L.g), *u = reinterpret_cast<float *>(work + L.u);
-    float *d = reinterpret_cast<float *>(work + L.d);
+    float *gu = reinterpret_cast<float *>(work + L.gu), *x = reinterpret_cast<float *>(work + L.x);
     const int64_t H = m.hidden, F = m.ffn;
-    if (m.format == PTI_FMT_SSQ)
+    const bool ssq = m.format == PTI_FMT_SSQ;
+    if (ssq)
         PTI_TRY(pti_embed_ssq(m.embed, tokens, h, m.vocab, H, stream));
     else
         PTI_TRY(pti_embed_q8(m.embed, tokens, h, m.vocab, H, n, stream));
+    const int64_t rows2[2] = {F, F};
     for (int l = 0; l < m.n_layers; l++) {
         PTI_TRY(pti_rmsnorm(h, r, H, n, m.eps, stream));
-        PTI_TRY(gemv(m, m.gate[l], r, g, F, H, n, stream));
-        PTI_TRY(gemv(m, m.up[l], r, u, F, H, n, stream));
-        PTI_TRY(pti_silu_mul(g, u, g, int64_t(n) * F, stream));
-        PTI_TRY(gemv(m, m.down[l], g, d, H, F, n, stream));
-        PTI_TRY(pti_add(h, d, h, int64_t(n) * H, stream));
+        const void *gate_up[2] = {m.gate[l], m.up[l]};
+        if (ssq)
+            PTI_TRY(pti_gemv_ssq_grouped(gate_up, rows2, 2, r, r + H, gu, gu + 2 * F, H, stream));
+        else
+            PTI_TRY(pti_gemv_q8_multi_grouped(gate_up, rows2, 2, r, gu, H, n, stream));
+        PTI_TRY(pti::launch_silu_mul_rows(gu, x, n, F, stream));
+        if (ssq)
+            PTI_TRY(pti::gemv_ssq_res(m.down[l], x, x + F, h, h + H, h, h + H, H, F, stream));
+        else
+            PTI_TRY(pti::gemv_q8_res(m.down[l], x, h, h, H, F, n, stream));
     }
     PTI_TRY(pti_rmsnorm(h, r, H, n, m.eps, stream));
     return gemv(m, m.head, r, logits, m.vocab, H, n, stream);
