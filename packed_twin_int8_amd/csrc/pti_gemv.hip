@@ -81,6 +81,7 @@
 #define PTI_LDS_BUDGET (160 * 1024)
 #endif
 
+
 namespace {
 
 constexpr uint32_t kRoundBytes = 1088;  // bytes of a row one round of 64 lanes covers (both formats)
