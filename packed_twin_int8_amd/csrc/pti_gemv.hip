@@ -272,6 +272,30 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+// One step of an unsigned 64-bit max over lanes: DPP moves the low and high
+// words with the same control; lanes DPP does not write see 0 (the identity).
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ unsigned long long umax_dpp(unsigned long long k)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, ROW_MASK, 0xf, BOUND_ZERO);
+    const uint32_t hi =
+        (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, ROW_MASK, 0xf, BOUND_ZERO);
+    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+    return o > k ? o : k;
+}
+
+// Unsigned 64-bit max over the 64 lanes, in lane 63: the tree of wave_sum.
+__device__ __forceinline__ unsigned long long wave_umax(unsigned long long k)
+{
+    k = umax_dpp<0x111, 0xf, true>(k);
+    k = umax_dpp<0x112, 0xf, true>(k);
+    k = umax_dpp<0x114, 0xf, true>(k);
+    k = umax_dpp<0x118, 0xf, true>(k);
+    k = umax_dpp<0x142, 0xa, false>(k);
+    k = umax_dpp<0x143, 0xc, false>(k);
+    return k;
+}
+
 template <int FMT, int NSP, int NS, int R, bool ROWS4, int kD>
 struct Wave {
     static constexpr int UC = unit_cols<FMT>();
@@ -936,11 +960,8 @@ __global__ __launch_bounds__(64 * BW) void gemv_ssq_split_kernel(SplitArgs sa)
         const int nw = P * Q;
 #pragma unroll
         for (int s = 0; s < 2; s++) {
-            unsigned long long k = vkey[s];
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1)
-                k = std::max(k, __shfl_xor(k, off, 64));
-            if (lane == 0)
+            const unsigned long long k = wave_umax(vkey[s]);
+            if (lane == 63)
                 wkey[s][wv] = k;
         }
         __syncthreads();
@@ -968,12 +989,9 @@ __global__ __launch_bounds__(256) void verify_keys_kernel(const unsigned long lo
         k[0] = std::max(k[0], keys[2 * i]);
         k[1] = std::max(k[1], keys[2 * i + 1]);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        k[0] = std::max(k[0], __shfl_xor(k[0], off, 64));
-        k[1] = std::max(k[1], __shfl_xor(k[1], off, 64));
-    }
-    if (lane == 0)
+    k[0] = wave_umax(k[0]);
+    k[1] = wave_umax(k[1]);
+    if (lane == 63)
         part[0][wv] = k[0], part[1][wv] = k[1];
     __syncthreads();
     if (tid == 0) {
