@@ -104,13 +104,13 @@ KT_FILE = os.path.join(HERE, "profiles", "gemv_ssq_q8_17408x5120_kernel_stats.md
 STEP_KERNELS = ("gemv_ssq_split_kernel<5, 2, true, 8>", "verify_keys_kernel")
 KERNEL_SOURCES = ("packed_twin_int8_amd/csrc/pti_gemv.hip", "packed_twin_int8_amd/build.py")
 PROFILE_CMDS = {
-    "kt": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_kt -o kt -- python3 bench.py --no-cpu",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_fetch -o fetch -- "
+    "kt": "rocprofv3 --kernel-trace --stats -f csv -d rocprof_out/kt -o kt -- python3 bench.py --no-cpu",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d rocprof_out/fetch -o fetch -- "
              "python3 bench.py --only-main --no-cpu --steps 10 --warmup 2 --copy-calibration",
-    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_write -o write -- "
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d rocprof_out/write -o write -- "
              "python3 bench.py --only-main --no-cpu --steps 10 --warmup 2 --copy-calibration",
-    "summary": "python3 bench.py --summarize-profiles gpurun_out/prof_kt gpurun_out/prof_fetch "
-               "gpurun_out/prof_write --profiles-out profiles",
+    "summary": "python3 bench.py --summarize-profiles rocprof_out/kt rocprof_out/fetch "
+               "rocprof_out/write --profiles-out profiles",
 }
 CALIB_BYTES = 64 * 2**20 * 4  # torch.neg over 64 Mi fp32: reads and writes this many bytes
 

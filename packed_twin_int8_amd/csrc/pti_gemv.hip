@@ -1,10 +1,15 @@
-// Packed-weight decode GEMVs for gfx950: the SSQ twin GEMV and the Q8
-// multi-stream GEMV.
+// Packed-weight decode GEMVs for gfx950: the SSQ twin GEMV (one or two
+// streams per twin), the Q8 multi-stream GEMV, their grouped forms, and the
+// SSQ GEMV fused with the greedy verify.
 //
-// Two kernels.  The per-wave-row kernel below (gemv_kernel) serves Q8 at every
+// Kernels.  The per-wave-row kernel below (gemv_kernel) serves Q8 at every
 // stream count and SSQ rows of more than 40 rounds; the row-split kernel
-// further down (gemv_ssq_split_kernel) serves the other SSQ shapes.  Each
-// format's choice depends on the shape alone, never on n_streams.
+// further down (gemv_ssq_split_kernel) serves the other SSQ shapes, and with
+// VERIFY also keeps each workgroup's largest output per twin, which
+// verify_keys_kernel then reduces.  Each format's choice depends on the shape
+// alone, never on the stream count.  Both kernels read rows through a segment
+// table (one matrix, or several with the same column count stacked into one
+// row space) and can add a residual to the rows they store.
 //
 // What is computed [README = "打包双子推理（PTI）", section "与 SSQ（Side-by-Side
 // Quantization）的关系" (relation to SSQ); section "带宽分析：为什么会有开销"
@@ -754,7 +759,7 @@ GemvArgs make_args(const void *w, int64_t rows, int64_t cols)
 // so T rounds per wave are always in flight.
 //
 // A wave always handles the same column slice, so it loads its T rounds of x
-// (T * 8 columns per lane, both twins) once into registers: no LDS staging,
+// (T * 8 columns per lane, every stream) once into registers: no LDS staging,
 // no LDS reads in the loop.  Per step it sums its rounds per lane, reduces
 // over its 64 lanes (the fixed DPP tree) and parks the partial in LDS; every
 // S steps the workgroup sums the Q partials of each finished row in slice
@@ -797,8 +802,8 @@ __device__ __forceinline__ unsigned long long verify_key(float v, int64_t row)
 // workgroup stores the largest of its threads' (0 if it has no rows);
 // verify_keys_kernel, launched next on the same stream, reduces them.  (A
 // single kernel whose last workgroup reduces the keys needs a device-scope
-// release and acquire per workgroup to see the others' keys, and on this GPU
-// those cost more than the second launch.)
+// release and acquire per workgroup to see the others' keys; on gfx950 those
+// are L2 writebacks and invalidates, which cost more than the second launch.)
 //
 // BW: the launch bound in waves.  Normally split_bound_waves(T); launches of
 // at most four waves may use a bound of four, which lets a wave keep more

@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests cannot run on a host without a GPU: skip them with a reason
-    # rather than fail (the GPU tier is run on the GPU machine with -m gpu).
+    # rather than fail (the GPU tests run with -m gpu on a machine with an MI355X).
     try:
         import torch
         has_gpu = torch.cuda.is_available()
