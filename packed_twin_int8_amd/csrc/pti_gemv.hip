@@ -61,6 +61,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <utility>
 
 #include "pti_internal.h"
@@ -708,15 +709,22 @@ int launch(const GemvArgs &a0, hipStream_t stream)
     }
     const int64_t grid = std::min<int64_t>(cus, (a.rows + kWaves - 1) / kWaves);
     auto kern = gemv_kernel<FMT, NSP, NS, R, ROWS4, kWaves, cfg.prefetch>;
-    static bool attr_set = false;
-    if (!attr_set) {
+    // The dynamic-LDS limit is a per-device attribute of the kernel: set it once on each device this
+    // instance runs on (one bit per device; two threads racing both set it, which is harmless).
+    static std::atomic<uint64_t> attr_devs{0};
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess || dev < 0 || dev >= 64) {
+        pti::set_hip_error(e != hipSuccess ? e : hipErrorInvalidDevice);
+        return PTI_ERR_HIP;
+    }
+    if (!(attr_devs.load(std::memory_order_acquire) >> dev & 1)) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, PTI_LDS_BUDGET);
         if (e != hipSuccess) {
             pti::set_hip_error(e);
             return PTI_ERR_HIP;
         }
-        attr_set = true;
+        attr_devs.fetch_or(uint64_t{1} << dev, std::memory_order_acq_rel);
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
     hipError_t e = hipGetLastError();
