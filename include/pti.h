@@ -287,6 +287,11 @@ int pti_add(const float *a, const float *b, float *y, int64_t n, void *stream);
  *      the same position and so replaces the stale speculative entry;
  *   2. attend: out[s][h] = sum_{j <= pos[s]} softmax_j(q[s][h] . K_s[g][j] /
  *      sqrt(head_dim)) V_s[g][j], with kv head g = h / (n_heads / n_kv_heads).
+ * Accuracy is that of fp32 arithmetic: both products run on the matrix
+ * cores with q (scaled per head by a power of two) and the softmax weights
+ * each split into a high and a low binary16 part, and every binary16 product
+ * is exact in fp32.  Finite inputs of any magnitude are handled; binary16
+ * subnormals in the caches are used as they are.
  * q: device fp32 [n_streams][n_heads][head_dim]; k_new, v_new: device fp32
  * [n_streams][n_kv_heads][head_dim]; k_cache, v_cache: HOST arrays
  * [n_streams] of device binary16 caches [n_kv_heads][max_len][head_dim]

@@ -15,22 +15,34 @@
 //   attend out[s][h] = sum_{j <= pos_s} softmax_j(q[s][h] . K_s[g][j] / sqrt(d)) V_s[g][j],
 //          g = h / (n_heads / n_kv_heads) (grouped heads share a kv head).
 //
-// Mapped onto CDNA4 as a split-K "flash decode":
+// Mapped onto CDNA4 as a split-K "flash decode" with both products on the
+// matrix cores (v_mfma_f32_16x16x32_f16):
 //   * Pass 1, one workgroup of 256 threads per (key chunk of 128, kv head,
-//     stream); each wave takes 32 keys.  Cache rows are read whole: d/8
-//     lanes cover a row with 16-byte loads, so a load instruction of a wave
-//     reads 64 / (d/8) consecutive rows as one contiguous span, and all of a
-//     wave's K loads (then all its V loads) are in flight together.  A lane
-//     scores its 8 dimensions against every query head of the group (so a
-//     key is read once for all heads that share it) and a DPP row-shift tree
-//     sums the row's lanes.  The chunk's max and exp-sum per head come from
-//     a wave shuffle tree and LDS.  For V a lane sums weight x value over its
-//     rows for its 8 dimensions; the row groups of a wave, then the waves,
-//     combine in a fixed order.  The chunk's (max, sum, weighted V) per head
-//     go to the workspace.  The chunk holding pos_s stores the new entry and
-//     uses the rounded values itself, so no pass reads what another writes.
-//   * Pass 2, one workgroup per (head, stream): the chunks up to pos_s
-//     combine, rescaled by exp(m_c - M), in a fixed grouping of chunks.
+//     stream).  Cache rows are read whole: d/8 lanes cover a row with 16-byte
+//     loads, so a load instruction of a wave reads 64 / (d/8) consecutive rows
+//     as one contiguous span, and all of a wave's K loads (then all its V
+//     loads) are in flight together.  The rows go to LDS; the new entry,
+//     rounded as it is stored, replaces the row at pos_s there.
+//     Scores: each wave multiplies its 32 keys (16 per MFMA row block) by the
+//     group's queries.  q is split exactly enough for fp32: per head it is
+//     scaled by a power of two so that max |q| lies in [2^14, 2^15), then
+//     written as a high binary16 part plus a low one (22 bits in all); the
+//     16 MFMA columns hold the high parts of up to 8 heads and their low
+//     parts, and a DPP rotate adds each head's two columns.  Products of
+//     binary16 values are exact in fp32, so the only roundings are the
+//     accumulation's.  A key is read once for all heads that share it.
+//     Softmax: the chunk's max and exp-sum per head (DPP trees and LDS); the
+//     weights are kept in units of 2^-15 (exact) so both of their binary16
+//     parts stay normal.
+//     Weighted V: rows = head parts (weights split the same way), k = keys,
+//     columns = 16 dimensions read transposed from the V rows in LDS
+//     (ds_read_b64_tr_b16); each wave owns d/4 dimensions over all 128 keys,
+//     and a lane swap adds each head's two rows.  The chunk's (max, exp-sum,
+//     weighted V) per head go to the workspace.  The chunk holding pos_s
+//     stores the new entry.
+//   * Pass 2, one workgroup per (head, stream, 32 dimensions): the chunks up
+//     to pos_s combine, rescaled by exp(m_c - M), in a fixed grouping of
+//     chunks.
 // Every sum runs in a fixed order that depends on the shapes and pos_s only.
 // Chunks past a stream's position exit at once; the grid covers max_len so
 // positions can live in device memory (capturable in a graph).
@@ -47,6 +59,11 @@ constexpr int kThreads = 256;
 constexpr int kMaxGroup = 8;    // query heads per kv head
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 struct AttnArgs {
     const float *q;       // [S][H][d]
@@ -67,19 +84,37 @@ __device__ __forceinline__ float h2f(uint32_t bits16) { return (float)__builtin_
 
 __device__ __forceinline__ uint16_t f2h(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
 
+// The value DPP moves into each lane under control CTRL (rows in ROW_MASK);
+// lanes it does not write get `id`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or(float v, float id)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, id), __builtin_bit_cast(int, v),
+                                                                 CTRL, ROW_MASK, 0xf, false));
+}
+
+// Max over the 64 lanes, in lane 63: a fixed DPP tree (row shifts by 1, 2,
+// 4, 8, then the row broadcasts of lanes 15 and 31).
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v = fmaxf(v, __shfl_xor(v, off, 64));
+    v = fmaxf(v, dpp_or<0x111, 0xf>(v, -INFINITY));
+    v = fmaxf(v, dpp_or<0x112, 0xf>(v, -INFINITY));
+    v = fmaxf(v, dpp_or<0x114, 0xf>(v, -INFINITY));
+    v = fmaxf(v, dpp_or<0x118, 0xf>(v, -INFINITY));
+    v = fmaxf(v, dpp_or<0x142, 0xa>(v, -INFINITY));
+    v = fmaxf(v, dpp_or<0x143, 0xc>(v, -INFINITY));
     return v;
 }
 
+// Sum over the 64 lanes, in lane 63, by the same tree.
 __device__ __forceinline__ float wave_add(float v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v += __shfl_xor(v, off, 64);
+    v = v + dpp_or<0x111, 0xf>(v, 0.f);
+    v = v + dpp_or<0x112, 0xf>(v, 0.f);
+    v = v + dpp_or<0x114, 0xf>(v, 0.f);
+    v = v + dpp_or<0x118, 0xf>(v, 0.f);
+    v = v + dpp_or<0x142, 0xa>(v, 0.f);
+    v = v + dpp_or<0x143, 0xc>(v, 0.f);
     return v;
 }
 
@@ -114,36 +149,43 @@ __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
-// The 8 halves of a uint4 as floats.
-__device__ __forceinline__ void unpack8(const uint4 t, float (&f)[8])
-{
-    const uint32_t w[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-    for (int e = 0; e < 4; e++)
-        f[2 * e] = h2f(w[e] & 0xFFFFu), f[2 * e + 1] = h2f(w[e] >> 16);
-}
-
 // 8 consecutive fp32 values rounded to binary16, packed as they are stored.
-__device__ __forceinline__ uint4 pack8(const float *x)
+__device__ __forceinline__ u32x4 pack8(const float *x)
 {
-    uint32_t w[4];
+    u32x4 w;
 #pragma unroll
     for (int e = 0; e < 4; e++)
         w[e] = (uint32_t)f2h(x[2 * e]) | ((uint32_t)f2h(x[2 * e + 1]) << 16);
-    return make_uint4(w[0], w[1], w[2], w[3]);
+    return w;
 }
+
+// Max over the four 16-lane rows of a wave, per column (lane % 16), in every
+// lane (once per workgroup).
+__device__ __forceinline__ float col_max(float v)
+{
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+
+// For lanes l < 32: lane l's value plus lane l + 32's.
+__device__ __forceinline__ float half_sum(float v) { return v + __shfl_xor(v, 32, 64); }
 
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a)
 {
+    static_assert(G >= 1 && G <= 8, "the high and low parts of at most 8 heads fill the 16 MFMA columns");
     constexpr int LPR = D / 8;                  // lanes per cache row: 16 bytes (8 halves) each
     constexpr int RPI = 64 / LPR;               // rows one load instruction of a wave covers
     constexpr int NW = kThreads / 64;
-    constexpr int KPW = kChunk / NW;            // keys per wave
+    constexpr int KPW = kChunk / NW;            // keys per wave (scores)
     constexpr int IT = KPW / RPI;               // loads per wave per tile
-    __shared__ float ps[G][kChunk];             // scores, then weights
+    constexpr int KSTEPS = D / 32;              // MFMA steps over the dimensions (scores)
+    constexpr int NBW = D / 16 / NW;            // 16-dimension output blocks per wave (weighted V)
+    constexpr int PITCH = 2 * D + 16;           // LDS row pitch of the K and V tiles, bytes
+    static_assert(KPW == 32 && NBW >= 1, "tile shape");
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kChunk * PITCH];  // K rows, then V rows
+    __shared__ __attribute__((aligned(16))) float ps[G][kChunk];            // scores, then weights
     __shared__ float red[G][NW];
-    __shared__ float vpart[NW][G][D];
     const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t pos = stream_pos(a, s);
@@ -157,61 +199,107 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a)
     const float *kn = a.k_new + ((size_t)s * a.Hkv + g) * D;
     const float *vn = a.v_new + ((size_t)s * a.Hkv + g) * D;
     const int r = lane / LPR, seg = lane % LPR;  // row within a load, 8-dimension segment
+    const int n = lane & 15, kg = lane >> 4;     // MFMA column / row (lane % 16) and k group (lane / 16)
 
-    // ---- K tile: rows are read whole and in order (LPR lanes x 16 bytes),
-    // every load of the wave in flight at once; the new key (rounded as it
-    // is stored) stands in for the cache row at pos
-    // Buffer resources over the chunk's valid rows: rows past them read 0
-    // without a branch, so no load waits on another.
+    // ---- K and V rows are read whole and in order (LPR lanes x 16 bytes),
+    // every load of the wave in flight at once, through buffer resources over
+    // the chunk's valid rows (rows past them read 0 without a branch).  The
+    // new entry (rounded as it is stored) replaces the row at pos when the
+    // rows are written to LDS.
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(K + (size_t)j0 * D), (short)0, nk * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(V + (size_t)j0 * D), (short)0, nk * D * 2, 0x00020000);
     const int newkey = has_new ? (int)(pos - j0) : -1;  // chunk index of the new entry
-    uint4 kn8 = make_uint4(0, 0, 0, 0), vn8 = make_uint4(0, 0, 0, 0);
+    u32x4 kn8 = {0, 0, 0, 0}, vn8 = {0, 0, 0, 0};
     if (has_new)  // uniform
         kn8 = pack8(kn + 8 * seg), vn8 = pack8(vn + 8 * seg);
-    uint4 kt[IT];
+    u32x4 kt[IT];
 #pragma unroll
     for (int it = 0; it < IT; it++) {
         const int key = wv * KPW + it * RPI + r;
-        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(krs, (key * D + 8 * seg) * 2, 0, 0);
-        kt[it] = make_uint4(t[0], t[1], t[2], t[3]);
+        kt[it] = __builtin_amdgcn_raw_buffer_load_b128(krs, (key * D + 8 * seg) * 2, 0, 0);
     }
-    float qv[G][8];
-#pragma unroll
-    for (int h = 0; h < G; h++)
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-            qv[h][e] = a.q[((size_t)s * a.H + (size_t)g * G + h) * D + 8 * seg + e];
 
-    // ---- scores: 8 dimensions per lane, then the row's LPR lanes
+    // ---- q as the MFMA's B operand: column n < 8 holds the high binary16
+    // part of head n, column n + 8 the low part (q' - high), for the k
+    // group's 8 dimensions per step.  q' = q 2^sh with sh chosen per head so
+    // that max |q'| lies in [2^14, 2^15): both parts stay normal (or exactly
+    // representable) and high + low carries 22 bits of each element.
+    const int hq = n & 7;
+    float qf[KSTEPS][8];
+    float qmax = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ks++)
+#pragma unroll
+        for (int e4 = 0; e4 < 2; e4++) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (hq < G)
+                v = *reinterpret_cast<const float4 *>(a.q + ((size_t)s * a.H + (size_t)g * G + hq) * D + 32 * ks +
+                                                      8 * kg + 4 * e4);
+            qf[ks][4 * e4] = v.x, qf[ks][4 * e4 + 1] = v.y, qf[ks][4 * e4 + 2] = v.z, qf[ks][4 * e4 + 3] = v.w;
+            qmax = fmaxf(qmax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+    qmax = col_max(qmax);  // over the four k groups: the head's max |q|
+    const int sh = qmax > 0.f ? 15 - __builtin_amdgcn_frexp_expf(qmax) : 0;
+    f16x8 qb[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ks++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const float x = ldexpf(qf[ks][e], sh);
+            const _Float16 hi = (_Float16)x;
+            qb[ks][e] = n < 8 ? hi : (_Float16)(x - (float)hi);
+        }
+
+    // ---- this wave's 32 K rows to its own LDS rows, then the scores on the
+    // matrix cores: rows = keys (A, 16 per block), columns = head parts (B)
+    uint8_t *kw = tile + wv * KPW * PITCH;
 #pragma unroll
     for (int it = 0; it < IT; it++) {
-        const int key = wv * KPW + it * RPI + r;
-        float k8[8];
-        unpack8(key == newkey ? kn8 : kt[it], k8);
+        const int kk = it * RPI + r;
+        const u32x4 row = (wv * KPW + kk == newkey) ? kn8 : kt[it];
+        *reinterpret_cast<u32x4 *>(kw + kk * PITCH + 16 * seg) = row;
+    }
+    // the wave reads rows other lanes wrote: LDS serves a wave's accesses in
+    // order, and the fence keeps the compiler from moving reads above writes
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    f32x4 sacc[2];
 #pragma unroll
-        for (int h = 0; h < G; h++) {
-            float d = qv[h][0] * k8[0];
+    for (int kb = 0; kb < 2; kb++) {
+        sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 1; e < 8; e++)
-                d = __builtin_fmaf(qv[h][e], k8[e], d);
-            d = group_sum<LPR>(d);
-            if (seg == LPR - 1 && key < nk)
-                ps[h][key] = d * a.scale;
+        for (int ks = 0; ks < KSTEPS; ks++) {
+            const f16x8 ka = *reinterpret_cast<const f16x8 *>(kw + (16 * kb + n) * PITCH + 64 * ks + 16 * kg);
+            sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[ks], sacc[kb], 0, 0, 0);
         }
     }
+    // lane (n, kg) holds keys 16 kb + 4 kg + i of column n: a head's score is
+    // its high column plus its low column (8 lanes over, same 16-lane row)
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) {
+        f32x4 sc;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            // (a copy first: a bit cast of a vector element itself reads element 0)
+            const float hi = sacc[kb][i];
+            const float lo = __builtin_bit_cast(
+                float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, hi), 0x128, 0xf, 0xf, false));
+            sc[i] = ldexpf(hi + lo, -sh) * a.scale;
+        }
+        if (n < G)
+            *reinterpret_cast<f32x4 *>(&ps[n][wv * KPW + 16 * kb + 4 * kg]) = sc;
+    }
 
-    // ---- V tile: issued now so the loads overlap the softmax
-    uint4 vt[IT];
+    // ---- V rows: issued now so the loads overlap the softmax
+    u32x4 vt[IT];
 #pragma unroll
     for (int it = 0; it < IT; it++) {
         const int key = wv * KPW + it * RPI + r;
-        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(vrs, (key * D + 8 * seg) * 2, 0, 0);
-        vt[it] = make_uint4(t[0], t[1], t[2], t[3]);
+        vt[it] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (key * D + 8 * seg) * 2, 0, 0);
     }
-    __syncthreads();
+    __syncthreads();  // scores complete; every wave is done with its K rows
 
     // ---- chunk max and exp-sum per head (thread tid: key tid, if any)
     float sc[G], m[G];
@@ -219,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a)
     for (int h = 0; h < G; h++) {
         sc[h] = tid < nk ? ps[h][tid] : -INFINITY;  // nk <= kChunk
         const float wm = wave_max(sc[h]);
-        if (lane == 0)
+        if (lane == 63)
             red[h][wv] = wm;
     }
     __syncthreads();
@@ -234,56 +322,71 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a)
     __syncthreads();  // red is reused below
 #pragma unroll
     for (int h = 0; h < G; h++) {
-        const float p = tid < nk ? expf(sc[h] - m[h]) : 0.f;
+        // weights in units of 2^-15 (exact): the binary16 parts below stay normal
+        const float p = tid < nk ? expf(sc[h] - m[h]) * 32768.f : 0.f;
         if (tid < kChunk)
             ps[h][tid] = p;  // only this thread reads or writes index tid
         const float ws = wave_add(p);
-        if (lane == 0)
+        if (lane == 63)
             red[h][wv] = ws;
     }
-    __syncthreads();
-
-    // ---- weighted V: a lane sums its 8 dimensions over its rows, then the
-    // RPI row groups of the wave combine (xor butterfly), then the waves
-    float acc[G][8];
-#pragma unroll
-    for (int h = 0; h < G; h++)
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-            acc[h][e] = 0.f;
+    // V rows to LDS (over the K rows, which no wave reads any more)
 #pragma unroll
     for (int it = 0; it < IT; it++) {
         const int key = wv * KPW + it * RPI + r;
-        float v8[8];
-        unpack8(key == newkey ? vn8 : vt[it], v8);
-#pragma unroll
-        for (int h = 0; h < G; h++) {
-            const float p = ps[h][key];  // 0 past the chunk's keys (and their rows read 0)
-#pragma unroll
-            for (int e = 0; e < 8; e++)
-                acc[h][e] = __builtin_fmaf(p, v8[e], acc[h][e]);
-        }
+        const u32x4 row = (key == newkey) ? vn8 : vt[it];
+        *reinterpret_cast<u32x4 *>(tile + key * PITCH + 16 * seg) = row;
     }
-#pragma unroll
-    for (int h = 0; h < G; h++)
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-#pragma unroll
-            for (int off = LPR; off < 64; off <<= 1)
-                acc[h][e] += __shfl_xor(acc[h][e], off, 64);
-            if (r == 0)
-                vpart[wv][h][8 * seg + e] = acc[h][e];
-        }
     __syncthreads();
 
-    // ---- chunk partials: weighted V (waves in order), max, sum
-    for (int i = tid; i < G * D; i += kThreads) {
-        const int h = i / D, d = i % D;
-        float v = vpart[0][h][d];
+    // ---- weighted V on the matrix cores: rows = head parts (A: row n < 8
+    // the high binary16 part of head n's weights (units of 2^-15), n + 8 the low part),
+    // k = keys, columns = 16 dimensions (B, read transposed from the V rows).
+    // Within each 32-key step, k group kg holds keys 4 kg .. 4 kg + 3 and
+    // 16 + 4 kg .. 16 + 4 kg + 3 in both operands.
+    f32x4 oacc[NBW];
 #pragma unroll
-        for (int w = 1; w < NW; w++)
-            v += vpart[w][h][d];
-        a.part[(((size_t)s * a.H + (size_t)g * G + h) * a.n_chunks + c) * D + d] = v;
+    for (int j = 0; j < NBW; j++)
+        oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kq = 0; kq < kChunk / 32; kq++) {
+        float4 p0 = make_float4(0.f, 0.f, 0.f, 0.f), p1 = p0;
+        if (hq < G) {
+            p0 = *reinterpret_cast<const float4 *>(&ps[hq][32 * kq + 4 * kg]);
+            p1 = *reinterpret_cast<const float4 *>(&ps[hq][32 * kq + 16 + 4 * kg]);
+        }
+        const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        f16x8 pa;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const _Float16 hi = (_Float16)pv[e];
+            pa[e] = n < 8 ? hi : (_Float16)(pv[e] - (float)hi);
+        }
+#pragma unroll
+        for (int j = 0; j < NBW; j++) {
+            const int col = 2 * (16 * (wv * NBW + j) + 4 * (n & 3));  // byte offset of 4 dimensions
+            const uint8_t *t0 = tile + (32 * kq + 4 * kg + (n >> 2)) * PITCH + col;
+            const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t0));
+            const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t0 + 16 * PITCH));
+            const f16x8 vb = __builtin_bit_cast(f16x8, s16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]});
+            oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, oacc[j], 0, 0, 0);
+        }
+    }
+
+    // ---- chunk partials: weighted V (high + low parts), max, sum, both in
+    // units of 2^-15 (the combine divides one by the other).
+    // Lane l < 32 holds rows 4 (l / 16) + i (heads), column n; lane l + 32
+    // holds the low parts of the same heads.
+#pragma unroll
+    for (int j = 0; j < NBW; j++) {
+        const int d0 = 16 * (wv * NBW + j) + n;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float v = half_sum(oacc[j][i]);
+            const int h = 4 * kg + i;
+            if (kg < 2 && h < G)
+                a.part[(((size_t)s * a.H + (size_t)g * G + h) * a.n_chunks + c) * D + d0] = v;
+        }
     }
     if (tid < G) {
         float l = red[tid][0];
@@ -307,34 +410,38 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a)
     }
 }
 
-// Pass 2: the chunks of (head, stream) combine.  The chunk maxima are read
-// in parallel and reduced to M; then thread (cg, dg) sums, over chunks cg,
-// cg + CG, ..., the 16-byte slice dg of the chunks' weighted V rows scaled by
-// exp(m_c - M) (and the exp-sums likewise); the chunk groups add in order.
+// Pass 2: the chunks of (head, stream) combine, one workgroup per (head,
+// stream, 32 dimensions).  The chunk maxima are read in parallel and reduced
+// to M; then thread (cg, dg) sums, over chunks cg, cg + CG, ..., the 16-byte
+// slice dg of the chunks' weighted V rows scaled by exp(m_c - M) (and the
+// exp-sums likewise); the chunk groups add in order.
+constexpr int kCombineDims = 32;
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a)
 {
-    constexpr int DG = D / 4;          // float4 slices of a row
-    constexpr int CG = kThreads / DG;  // chunk groups
+    constexpr int DG = kCombineDims / 4;  // float4 slices of the workgroup's dimensions
+    constexpr int CG = kThreads / DG;     // chunk groups
     __shared__ float redm[kThreads / 64];
     __shared__ float4 vsum[CG][DG];
     __shared__ float lsum[CG];
     const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    float *o = a.out + ((size_t)s * a.H + h) * D;
+    const int d0 = blockIdx.z * kCombineDims;
+    float *o = a.out + ((size_t)s * a.H + h) * D + d0;
     const int64_t pos = stream_pos(a, s);
     if (pos < 0) {
-        if (tid < D)
+        if (tid < kCombineDims)
             o[tid] = NAN;
         return;
     }
     const int nc = (int)(pos / kChunk) + 1;
-    const float *pv = a.part + ((size_t)s * a.H + h) * a.n_chunks * D;
+    const float *pv = a.part + ((size_t)s * a.H + h) * a.n_chunks * D + d0;
     const float *pm = a.ml + ((size_t)s * a.H + h) * a.n_chunks * 2;
     float mx = -INFINITY;
     for (int c = tid; c < nc; c += kThreads)
         mx = fmaxf(mx, pm[2 * c]);
     mx = wave_max(mx);
-    if (lane == 0)
+    if (lane == 63)
         redm[wv] = mx;
     __syncthreads();
     float M = redm[0];
@@ -379,7 +486,8 @@ void launch_g(const AttnArgs &a, int S, hipStream_t st)
 {
     hipLaunchKernelGGL((attn_partial_kernel<D, G>), dim3((unsigned)a.n_chunks, (unsigned)a.Hkv, (unsigned)S),
                        dim3(kThreads), 0, st, a);
-    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)a.H, (unsigned)S), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)a.H, (unsigned)S, (unsigned)(D / kCombineDims)),
+                       dim3(kThreads), 0, st, a);
 }
 
 template <int D>

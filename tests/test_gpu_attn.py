@@ -4,12 +4,23 @@ fp64 oracle (oracle/attention.py).
 Bars:
   * the stored entry at pos: bit-exact binary16 of the fp32 key and value;
     every other cache entry unchanged (bitwise);
-  * outputs: |out - exact| <= tol * sum_j p_j |v_j| per output, with
-      tol = 4 eps_s + (2 (64 + 8 + n_chunks) + 16) u,  u = 2^-24,
-      eps_s = (d + 2) u max_j sum_i |q_i k_j,i| / sqrt(d)
-    (the fp32 score error, through exp into the weights, plus the rounding
-    of the weighted sums: a thread's share of a chunk, the key groups, the
-    chunk combine and the normalisation);
+  * outputs: per output (head h, dimension i), with u = 2^-24,
+      |out - exact| <= (4 eps_s + (2 (136 + n_chunks) + 16) u) sum_j p_j |v_j,i|
+                       + 2^-40 sum_j |v_j,i|,
+      eps_s = ((d + 8) u smax + 2^-39 max_i |q_i| max_j sum_i |k_j,i|) / sqrt(d),
+      smax  = max_j sum_i |q_i k_j,i|.
+    The kernel scores on the matrix cores with q split into two binary16
+    parts (q 2^sh = high + low, sh per head so that max |q 2^sh| lies in
+    [2^14, 2^15)): the split drops at most 2^-22 |q_i| + 2^-25 2^-sh per
+    element, the 128-term fp32 accumulation of exact products costs
+    d u, the sum of the two parts, the scaling by 2^-sh and the product with
+    the fp32 1/sqrt(d) one rounding each.  The weights (in units of 2^-15)
+    are split the same way, so a chunk's weighted V carries 128 u of
+    accumulation, 4 u of split and one rounding for the two parts' sum, plus
+    2^-40 |v_j| per key from the low part's binary16 spacing.  The score
+    error passes through exp into the weights (4 eps_s); the factor 2 covers
+    the numerator and the exp-sum of the normalisation, n_chunks the chunk
+    combine and 16 the exp and division roundings;
   * a stream's outputs do not depend on the other streams (bitwise), and a
     redo at the same position (the reject rule) gives what a cache that never
     held the stale entry gives (bitwise).
@@ -44,12 +55,16 @@ def _note(msg):
 
 
 def tol_of(q, K, V, H, Hkv, n):
-    """Per-output bound from the oracle's magnitudes."""
+    """Per-output bound: the oracle's magnitudes plus the split terms."""
     d = q.shape[1]
     out, vmag, smax = A.attend(q, K, V, H, Hkv)
-    eps_s = (d + 2) * U * smax / math.sqrt(d)
+    kv = np.arange(H) // (H // Hkv)
+    q64 = np.asarray(q, np.float64)
+    k1 = np.abs(np.asarray(K, np.float64)).sum(axis=2).max(axis=1)[kv]  # max_j sum_i |k_j,i| per head
+    vabs = np.abs(np.asarray(V, np.float64)).sum(axis=1)[kv]            # sum_j |v_j,i| per head
+    eps_s = ((d + 8) * U * smax + 2.0 ** -39 * np.abs(q64).max(axis=1) * k1) / math.sqrt(d)
     n_chunks = (n + CHUNK - 1) // CHUNK
-    tol = (4 * eps_s[:, None] + (2 * (64 + 8 + n_chunks) + 16) * U) * vmag
+    tol = (4 * eps_s[:, None] + (2 * (136 + n_chunks) + 16) * U) * vmag + 2.0 ** -40 * vabs
     return out, tol
 
 
@@ -117,6 +132,38 @@ def test_attn_vs_oracle(env, S, H, Hkv, d, L, pos):
     q, kn, vn = c.inputs()
     got = c.run(env, q, kn, vn)
     c.check(env, q, kn, vn, got)
+
+
+@pytest.mark.parametrize("qscale", [1e-20, 1e20], ids=["q_tiny", "q_huge"])
+def test_attn_query_magnitudes(env, qscale):
+    """The per-head power-of-two scaling of q before its split into binary16
+    parts: far outside the binary16 range either way."""
+    _note(f"attn qscale={qscale}")
+    c = Case(env, 2, 8, 2, 128, 512, [300, 301], seed=61)
+    q, kn, vn = c.inputs()
+    q = (q * np.float32(qscale)).astype(np.float32)
+    got = c.run(env, q, kn, vn)
+    c.check(env, q, kn, vn, got, what=f"qscale {qscale}")
+
+
+def test_attn_subnormal_cache_entries(env):
+    """binary16 subnormals in the caches: every K entry, and V in half of the
+    dimensions, with q large enough that the scores spread over about 0.1:
+    flushed subnormals would flatten the weights and zero those outputs."""
+    _note("attn subnormal entries")
+    torch, pti, dev = env
+    for d, G in ((128, 8), (64, 5)):
+        c = Case(env, 1, G, 1, d, 256, [200], seed=71 + d)
+        g = np.random.default_rng(72 + d)
+        for KV, t, dims in ((c.oc[0].K, c.kc[0], d), (c.oc[0].V, c.vc[0], d // 2)):
+            ints = g.integers(1, 1024, KV[..., :dims].shape) * g.choice([-1, 1], KV[..., :dims].shape)
+            KV[..., :dims] = (ints * 2.0 ** -24).astype(np.float16)
+            t.copy_(torch.from_numpy(KV.copy()))
+        q, kn, vn = c.inputs()
+        q = (q * np.float32(2.0 ** 12)).astype(np.float32)
+        kn = (kn * np.float32(2.0 ** -17)).astype(np.float32)  # the new key rounds to subnormals too
+        got = c.run(env, q, kn, vn)
+        c.check(env, q, kn, vn, got, what=f"subnormals d={d} G={G}")
 
 
 def test_attn_streams_independent(env):
