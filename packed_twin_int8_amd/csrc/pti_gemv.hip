@@ -831,24 +831,7 @@ __global__ __launch_bounds__(64 * BW) void gemv_ssq_split_kernel(SplitArgs sa)
     const int64_t wg_rows = g < a.rows ? (a.rows - g + G - 1) / G : 0;
     const int steps = (int)((wg_rows + P - 1) / P);
 
-    // x of this lane's units in rounds q T .. q T + T - 1 (zero past the row's
-    // last unit), every stream (stream s feeds twin A if s is even, twin B if odd)
-    float xv[T][UC][NS];
-#pragma unroll
-    for (int tt = 0; tt < T; tt++) {
-        const int unit = (q * T + tt) * 64 + lane;
-#pragma unroll
-        for (int s = 0; s < NS; s++)
-#pragma unroll
-            for (int k = 0; k < UC / 4; k++) {
-                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (unit < a.units)
-                    v = *reinterpret_cast<const float4 *>(a.x[s] + unit * UC + 4 * k);
-                xv[tt][4 * k][s] = v.x, xv[tt][4 * k + 1][s] = v.y, xv[tt][4 * k + 2][s] = v.z,
-                              xv[tt][4 * k + 3][s] = v.w;
-            }
-    }
-
+    float xv[T][UC][NS];  // this lane's x (filled below, after the first weight requests)
     const LaneOffsets lo = lane_offsets(lane);
     const int soff = q * T * (int)kRoundBytes;
     // Buffer resource over the row of step t (empty past the workgroup's rows:
@@ -945,12 +928,33 @@ __global__ __launch_bounds__(64 * BW) void gemv_ssq_split_kernel(SplitArgs sa)
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
     };
 
+    // The first step's weights are requested before x, so the two latencies
+    // overlap.
     Unit bufs[2][T];
     {
         const __amdgpu_buffer_rsrc_t rs0 = rsrc_for(0);
 #pragma unroll
         for (int tt = 0; tt < T; tt++)
             load_round(rs0, tt, bufs[0][tt]);
+    }
+    // x of this lane's units in rounds q T .. q T + T - 1, every stream (stream
+    // s feeds twin A if s is even, twin B if odd), through a resource over the
+    // row's units: past the last unit the loads return zero.
+#pragma unroll
+    for (int s = 0; s < NS; s++) {
+        const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(a.x[s]), (short)0, (int)(a.units * UC * 4), 0x00020000);
+#pragma unroll
+        for (int tt = 0; tt < T; tt++) {
+            const int unit = (q * T + tt) * 64 + lane;
+#pragma unroll
+            for (int k = 0; k < UC / 4; k++) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xrs, (unit * UC + 4 * k) * 4, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    xv[tt][4 * k + e][s] = __builtin_bit_cast(float, (uint32_t)v[e]);
+            }
+        }
     }
     // Windows of S steps (S even, so step t always uses buffer t mod 2); the
     // last window is rounded up to an even count so the loop has a single
