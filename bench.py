@@ -15,12 +15,12 @@ Also reported on the same JSON line:
     100 back-to-back calls timed with HIP events on its stream) against 8 TB/s
     HBM, its HBM traffic (both kernels) from the committed PMC summary, the
     kernels' own rocprofv3 averages from the committed kernel-trace summary,
-    and its rate against a device-to-device copy of the same bytes
-    (copy_ceiling);
+    their L2 hit rates from the committed TCC summary, and its rate against
+    a device-to-device copy of the same bytes (copy_ceiling);
   * per_kernel: the unfused pair (pti_gemv_ssq, then pti_verify_argmax), and
     the Q8 multi-stream GEMV over 17408 x 5120 at N = 1, 2, 4 streams
-    (effective weight GB/s, GEMV/s, and t(N=4)/t(N=1)), each with median /
-    p10 / p90 over 10 runs; a decoder layer's seven GEMVs separate, grouped
+    (effective weight GB/s, GEMV/s, L2 hit rate, and t(N=4)/t(N=1)), each
+    with median / p10 / p90 over 10 runs; a decoder layer's seven GEMVs separate, grouped
     and grouped in a graph; the toy decoder's forward pass eager and as a
     graph;
   * cpu_baseline: the fp64 oracle (scalar C, one host core) running the same
@@ -111,6 +111,19 @@ PROFILE_CMDS = {
              "python3 bench.py --only-main --no-cpu --steps 10 --warmup 2 --copy-calibration",
     "summary": "python3 bench.py --summarize-profiles rocprof_out/kt rocprof_out/fetch "
                "rocprof_out/write --profiles-out profiles",
+    "tcc": "rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum -f csv -d rocprof_out/tcc -o tcc -- "
+           "python3 bench.py --cache-profile --no-cpu",
+    "tcc_summary": "python3 bench.py --summarize-hit-rate rocprof_out/tcc --profiles-out profiles",
+}
+HIT_FILE = os.path.join(HERE, "profiles", "gemv_l2_hit_rate_17408x5120_pmc.txt")
+# kernels of the cache-profile run, as rocprofv3 names them, and what each one is there
+HIT_KERNELS = {
+    "gemv_ssq_split_kernel<5, 2, true, 8>": "step: fused SSQ twin GEMV (+ verify keys)",
+    "verify_keys_kernel": "step: verify keys",
+    "gemv_ssq_split_kernel<5, 2, false, 8>": "SSQ twin GEMV alone",
+    "gemv_kernel<0, 1, 1, 1, true, 12, 4>": "Q8 GEMV, N = 1",
+    "gemv_kernel<0, 2, 2, 1, true, 12, 4>": "Q8 GEMV, N = 2",
+    "gemv_kernel<0, 4, 4, 2, true, 16, 4>": "Q8 GEMV, N = 4",
 }
 CALIB_BYTES = 64 * 2**20 * 4  # torch.neg over 64 Mi fp32: reads and writes this many bytes
 
@@ -263,6 +276,97 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, out_dir):
     with open(os.path.join(out_dir, os.path.basename(TRAFFIC_FILE)), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def summarize_hit_rate(tcc_dir, out_dir):
+    """L2 (TCC) hit rate per kernel of the cache-profile run, from rocprofv3's
+    TCC_HIT_sum and TCC_MISS_sum: the share of L2 requests served without a
+    fetch from the Infinity Fabric (x re-reads hit; streamed weights miss)."""
+    acc = {}
+    for r in _csv_rows(tcc_dir, "counter_collection.csv"):
+        k = _short(r["Kernel_Name"])
+        acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    lines = ["# L2 (TCC) hit rate per kernel: the fused SSQ step, the SSQ GEMV alone and the Q8 GEMV at",
+             "# N = 1, 2, 4 streams over 17408x5120 (weights rotated over copies larger than the Infinity Cache),",
+             "# rocprofv3 PMC counters TCC_HIT_sum and TCC_MISS_sum, one MI355X.  hit rate = hits / (hits + misses).",
+             "", "command: " + PROFILE_CMDS["tcc"], "summary: " + PROFILE_CMDS["tcc_summary"],
+             "kernel_source_sha256: " + kernel_source_hash(), "",
+             "| kernel | what | dispatches | avg hits | avg misses | hit rate |", "|---|---|---|---|---|---|"]
+    found = 0
+    for name, what in HIT_KERNELS.items():
+        ks = [k for k in acc if k.endswith(name)]
+        if len(ks) != 1:
+            raise SystemExit(f"expected one kernel named {name}, found {ks}")
+        c = acc[ks[0]]
+        h, m = c.get("TCC_HIT_sum", []), c.get("TCC_MISS_sum", [])
+        if not h or len(h) != len(m):
+            raise SystemExit(f"{name}: missing TCC counters")
+        hh, mm = sum(h) / len(h), sum(m) / len(m)
+        lines.append(f"| {name} | {what} | {len(h)} | {hh:.0f} | {mm:.0f} | {hh / max(hh + mm, 1):.4f} |")
+        found += 1
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, os.path.basename(HIT_FILE)), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def read_hit_rates():
+    """{kernel: L2 hit rate} from the committed summary, or None if it is
+    missing or the kernel source changed since the counters were taken."""
+    try:
+        rates, src = {}, None
+        with open(HIT_FILE) as f:
+            for line in f:
+                if line.startswith("kernel_source_sha256:"):
+                    src = line.split(":", 1)[1].strip()
+                elif line.startswith("| ") and not line.startswith("| kernel"):
+                    cells = [c.strip() for c in line.strip().strip("|").split("|")]
+                    rates[cells[0]] = float(cells[5])
+        if src != kernel_source_hash() or set(rates) != set(HIT_KERNELS):
+            return None
+        return rates
+    except (OSError, ValueError, IndexError):
+        return None
+
+
+def cache_profile_run(torch, pti, dev, stream):
+    """The kernels of the L2 hit-rate profile, a few launches each: the fused
+    step, the SSQ GEMV alone, and the Q8 GEMV at N = 1, 2, 4 (17408x5120,
+    weights rotated over copies)."""
+    import synth
+    L, sp = pti.lib(), pti._stream(stream)
+    d = synth.twin(ROWS, COLS, synth.SEED_SSQ_FFN)
+    P = pti.pack_ssq(d["A"], d["B"], d["sA"], d["sB"])
+    n = copies_for(P.nbytes)
+    w0 = torch.from_numpy(P).to(dev)
+    ws = [w0] + [w0.clone() for _ in range(n - 1)]
+    xa, xb = torch.from_numpy(d["xA"]).to(dev), torch.from_numpy(d["xB"]).to(dev)
+    y2 = torch.empty((2, ROWS), dtype=torch.float32, device=dev)
+    tok = torch.zeros(2, dtype=torch.int32, device=dev)
+    am = torch.empty(2, dtype=torch.int32, device=dev)
+    acc = torch.empty(1, dtype=torch.int32, device=dev)
+    work = pti.ssq_verify_workspace(dev)
+    for i in range(12):
+        pti._check("pti_gemv_ssq_verify", L.pti_gemv_ssq_verify(
+            ws[i % n].data_ptr(), xa.data_ptr(), xb.data_ptr(), y2[0].data_ptr(), y2[1].data_ptr(), ROWS, COLS,
+            tok.data_ptr(), am.data_ptr(), acc.data_ptr(), work.data_ptr(), work.numel(), sp))
+        pti._check("pti_gemv_ssq", L.pti_gemv_ssq(ws[i % n].data_ptr(), xa.data_ptr(), xb.data_ptr(),
+                                                  y2[0].data_ptr(), y2[1].data_ptr(), ROWS, COLS, sp))
+    torch.cuda.synchronize()
+    del ws, w0
+    q = synth.q8(ROWS, COLS, 4, synth.SEED_Q8_FFN)
+    Pq = pti.pack_q8(q["Q"], q["S"])
+    nq = copies_for(Pq.nbytes)
+    wq0 = torch.from_numpy(Pq).to(dev)
+    wqs = [wq0] + [wq0.clone() for _ in range(nq - 1)]
+    X = torch.from_numpy(q["X"]).to(dev)
+    Y = torch.empty((4, ROWS), dtype=torch.float32, device=dev)
+    for ns in (1, 2, 4):
+        for i in range(12):
+            pti._check("pti_gemv_q8_multi", L.pti_gemv_q8_multi(wqs[i % nq].data_ptr(), X.data_ptr(), Y.data_ptr(),
+                                                                 ROWS, COLS, ns, sp))
+    torch.cuda.synchronize()
+    log("cache profile: 12 launches of each kernel")
 
 
 def layer_and_graph(torch, pti, dev, stream):
@@ -421,10 +525,17 @@ def main():
                     help="also run 3 elementwise copies of 256 MiB (reference kernel for HBM byte counters)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from rocprofv3 CSV output (CPU only) and exit")
+    ap.add_argument("--cache-profile", action="store_true",
+                    help="run only the kernels of the L2 hit-rate profile (a few launches each) and exit")
+    ap.add_argument("--summarize-hit-rate", metavar="TCC_DIR",
+                    help="write the L2 hit-rate summary from rocprofv3 CSV output (CPU only) and exit")
     ap.add_argument("--profiles-out", default=os.path.join(HERE, "profiles"))
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, args.profiles_out)
+        return
+    if args.summarize_hit_rate:
+        summarize_hit_rate(args.summarize_hit_rate, args.profiles_out)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; run with --gpus 1", file=sys.stderr)
@@ -438,6 +549,9 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     log(f"device {torch.cuda.get_device_name(0)}")
+    if args.cache_profile:
+        cache_profile_run(torch, pti, dev, stream)
+        return
 
     # ---------------- inputs: SSQ twin workload, seed 2
     d = synth.twin(ROWS, COLS, synth.SEED_SSQ_FFN)
@@ -505,8 +619,10 @@ def main():
         st_verify = timed_stats(torch, verify, stream)
         ms_gemv = st_gemv["median_us"] * 1e-3
         log(f"unfused: ssq gemv alone {st_gemv}; verify alone {st_verify}")
+        hr = read_hit_rates()
         per_kernel["ssq_twin_gemv_unfused"] = {**st_gemv,
-                                               "weight_GBps": round(w_bytes / (ms_gemv * 1e-3) / 1e9, 2)}
+                                               "weight_GBps": round(w_bytes / (ms_gemv * 1e-3) / 1e9, 2),
+                                               "l2_hit_rate": hr["gemv_ssq_split_kernel<5, 2, false, 8>"] if hr else None}
         per_kernel["verify_n2_v17408_unfused"] = st_verify
         # two streams per twin: four activation vectors per weight read
         xa2 = torch.randn((2, COLS), device=dev)
@@ -534,6 +650,7 @@ def main():
         log(f"copy {w_bytes} B: {st_copy}, {copy_GBps:.0f} GB/s read+write")
 
     traffic = read_traffic()
+    hit_rates = read_hit_rates()
     result = {
         "metric": METRIC,
         "value": round(w_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -570,6 +687,8 @@ def main():
             "vs_copy": round(algo_bytes / (ms_fused * 1e-3) / 1e9 / copy_GBps, 4) if copy_GBps else None,
             "rocprof_avg_us": read_kernel_avgs(),
             "rocprof_source": os.path.relpath(KT_FILE, HERE),
+            "l2_hit_rate": ({k: hit_rates[k] for k in STEP_KERNELS} if hit_rates else None),
+            "l2_hit_rate_source": os.path.relpath(HIT_FILE, HERE),
         },
     }
     if copy_GBps:
@@ -601,6 +720,7 @@ def main():
                 "frac_of_hbm_peak": round(algo / (t[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "gemv_per_s": round(1 / (t[n] * 1e-3), 1),
                 "outputs_per_s": round(n * ROWS / (t[n] * 1e-3), 1),
+                "l2_hit_rate": next((v for k, v in (hr or {}).items() if k.startswith(f"gemv_kernel<0, {n}, ")), None),
             }
             log(f"q8 n={n}: {t[n] * 1e3:.2f} us, {Pq.nbytes / (t[n] * 1e-3) / 1e9:.1f} GB/s")
         per_kernel["q8_step_cost_n4_over_n1"] = round(t[4] / t[1], 4)

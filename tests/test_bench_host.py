@@ -75,3 +75,31 @@ def test_summarize_requires_each_step_kernel(tmp_path):
 def test_step_algorithmic_bytes():
     rows, cols = bench.ROWS, bench.COLS
     assert bench.step_algo_bytes() == rows * cols // 32 * 68 + 8 * cols + 8 * rows + 20
+
+
+def test_summarize_hit_rate(tmp_path, monkeypatch):
+    d, out = str(tmp_path / "tcc"), str(tmp_path / "out")
+    rows = []
+    for i, k in enumerate(bench.HIT_KERNELS):
+        for _ in range(2):
+            rows += [[f"void (anonymous namespace)::{k}(Args)", "TCC_HIT_sum", 10.0 * (i + 1)],
+                     [f"void (anonymous namespace)::{k}(Args)", "TCC_MISS_sum", 90.0]]
+    _write_csv(os.path.join(d, "box", "tcc_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"],
+               rows)
+    bench.summarize_hit_rate(d, out)
+    monkeypatch.setattr(bench, "HIT_FILE", os.path.join(out, os.path.basename(bench.HIT_FILE)))
+    r = bench.read_hit_rates()
+    assert r is not None and set(r) == set(bench.HIT_KERNELS)
+    for i, k in enumerate(bench.HIT_KERNELS):
+        assert r[k] == round(10.0 * (i + 1) / (10.0 * (i + 1) + 90.0), 4)
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
+    assert bench.read_hit_rates() is None
+
+
+def test_summarize_hit_rate_requires_each_kernel(tmp_path):
+    d = str(tmp_path / "tcc")
+    k = next(iter(bench.HIT_KERNELS))
+    _write_csv(os.path.join(d, "c_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"],
+               [[k, "TCC_HIT_sum", 1.0], [k, "TCC_MISS_sum", 1.0]])
+    with pytest.raises(SystemExit):
+        bench.summarize_hit_rate(d, str(tmp_path / "out"))

@@ -166,6 +166,39 @@ def test_attn_subnormal_cache_entries(env):
         c.check(env, q, kn, vn, got, what=f"subnormals d={d} G={G}")
 
 
+def test_attn_bench_shape_sampled(env):
+    """The benchmark's shape and launch: two streams, 40 query heads over 8
+    kv heads of 128, 32K positions (256 chunks); sampled heads of both
+    streams against the oracle."""
+    _note("attn bench shape 2x40/8x128, 32768 positions")
+    torch, pti, dev = env
+    S, H, Hkv, d, L = 2, 40, 8, 128, 32768
+    g = np.random.default_rng(81)
+    pos = [L - 2, L - 1]
+    K = [A.f16_round(g.standard_normal((Hkv, L, d))) for _ in range(S)]
+    V = [A.f16_round(g.standard_normal((Hkv, L, d))) for _ in range(S)]
+    kc = [torch.from_numpy(k).to(dev) for k in K]
+    vc = [torch.from_numpy(v).to(dev) for v in V]
+    q = g.standard_normal((S, H, d)).astype(np.float32)
+    kn = g.standard_normal((S, Hkv, d)).astype(np.float32)
+    vn = g.standard_normal((S, Hkv, d)).astype(np.float32)
+    work = pti.attn_workspace(S, H, Hkv, d, L, dev)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    out = pti.attn_decode(t(q), t(kn), t(vn), kc, vc, torch.tensor(pos, dtype=torch.int32, device=dev), work)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    group = H // Hkv
+    for s in range(S):
+        p = pos[s]
+        K[s][:, p] = A.f16_round(kn[s])
+        V[s][:, p] = A.f16_round(vn[s])
+        for h in (0, 4, 5, 17, 23, 39):  # first and last of groups, both ends
+            gh = h // group
+            want, tol = tol_of(q[s, h:h + 1], K[s][gh:gh + 1, :p + 1], V[s][gh:gh + 1, :p + 1], 1, 1, p + 1)
+            err = np.abs(got[s, h].astype(np.float64) - want[0])
+            assert np.all(err <= tol[0]), f"stream {s} head {h}: worst err/tol {np.max(err / tol[0]):.3f}"
+
+
 def test_attn_streams_independent(env):
     torch, pti, dev = env
     c2 = Case(env, 2, 8, 2, 128, 2048, [700, 1500], seed=11)
