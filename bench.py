@@ -22,7 +22,8 @@ Also reported on the same JSON line:
     (effective weight GB/s, GEMV/s, L2 hit rate, and t(N=4)/t(N=1)), each
     with median / p10 / p90 over 10 runs; a decoder layer's seven GEMVs separate, grouped
     and grouped in a graph; the toy decoder's forward pass eager and as a
-    graph;
+    graph; twin-KV attention; the greedy and sampled verify at the toy
+    decoder's vocabulary; the host packer;
   * cpu_baseline: the fp64 oracle (scalar C, one host core) running the same
     SSQ GEMV, timed on a bounded number of passes.
 
@@ -483,6 +484,42 @@ def layer_and_graph(torch, pti, dev, stream):
     return out
 
 
+def verify_and_pack(torch, pti, dev, stream, d):
+    """The verify calls at the toy decoder's vocabulary (32000) for N = 1, 2, 4
+    streams, greedy and sampled (temperature 0.7), time per call; and the host
+    packer over the 17408x5120 twin (one call, median of three)."""
+    out = {}
+    L, sp = pti.lib(), pti._stream(stream)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    for n in (1, 2, 4):
+        logits = torch.randn((n, 32000), generator=g).to(dev)
+        tok = torch.zeros(n, dtype=torch.int32, device=dev)
+        am = torch.empty(n, dtype=torch.int32, device=dev)
+        acc = torch.empty(1, dtype=torch.int32, device=dev)
+        st = timed_stats(torch, lambda i: L.pti_verify_argmax(logits.data_ptr(), tok.data_ptr(), am.data_ptr(),
+                                                              acc.data_ptr(), 32000, n, sp),
+                         stream, reps=5, per_rep=50, warmup=10)
+        out[f"verify_greedy_n{n}_v32000"] = st
+        u = torch.rand(n, dtype=torch.float64, generator=g).to(dev)
+        st = timed_stats(torch, lambda i: L.pti_sample_verify(logits.data_ptr(), tok.data_ptr(), u.data_ptr(), 0.7,
+                                                              am.data_ptr(), acc.data_ptr(), 32000, n, sp),
+                         stream, reps=5, per_rep=50, warmup=10)
+        out[f"verify_sampled_n{n}_v32000_t0.7"] = st
+        log(f"verify n={n}: {out[f'verify_greedy_n{n}_v32000']}")
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        P = pti.pack_ssq(d["A"], d["B"], d["sA"], d["sB"])
+        ts.append(time.perf_counter() - t0)
+    t = sorted(ts)[1]
+    # the packer splits rows over std::thread workers: the host's hardware threads, at most 32
+    out["host_pack_ssq_17408x5120"] = {"ms": round(t * 1e3, 3), "out_bytes": int(P.nbytes),
+                                       "out_GBps": round(P.nbytes / t / 1e9, 3),
+                                       "threads": min(os.cpu_count() or 1, 32)}
+    log(f"host pack: {out['host_pack_ssq_17408x5120']}")
+    return out
+
+
 def attention(torch, pti, dev, stream):
     """Twin-KV decode attention (two streams: the twins), 40 query heads over
     8 kv heads of 128, binary16 caches, at 4K and 32K positions: time per
@@ -728,6 +765,7 @@ def main():
         torch.cuda.empty_cache()
         per_kernel.update(layer_and_graph(torch, pti, dev, stream))
         per_kernel.update(attention(torch, pti, dev, stream))
+        per_kernel.update(verify_and_pack(torch, pti, dev, stream, d))
     result["per_kernel"] = per_kernel
 
     if not args.no_cpu:

@@ -240,7 +240,8 @@ int pti_verify_argmax(const float *logits, const int32_t *tokens_in, int32_t *ar
  * unspecified and may be -1); tokens_in: device int32 [n_streams];
  * uniforms: device fp64 [n_streams] in [0, 1) (8-byte aligned); temperature:
  * finite, > 0; tokens_out: device int32 [n_streams]; accept_out: device int32
- * [1].  Outputs must not overlap inputs or each other. */
+ * [1].  Outputs must not overlap inputs or each other.  Two kernels are
+ * enqueued on `stream`: one workgroup per stream draws, then the accept count. */
 int pti_sample_verify(const float *logits, const int32_t *tokens_in, const double *uniforms, double temperature,
                       int32_t *tokens_out, int32_t *accept_out, int64_t vocab, int n_streams, void *stream);
 

@@ -159,100 +159,102 @@ __global__ void add_kernel(const float *a, const float *b, float *y, int64_t n)
 constexpr int kSampleThreads = 1024;
 constexpr int kSampleWaves = kSampleThreads / 64;
 
-// Sums are taken in a fixed order that never decreases along the index: each
-// thread owns a contiguous chunk of the vocabulary and sums it in index order;
-// chunk sums are prefixed sequentially within a wave, then wave totals
-// sequentially.  The drawn index is the first one, in that order, whose
-// running sum exceeds u * Z among indices of nonzero weight; if rounding
-// leaves none, the last index of nonzero weight in the chunk that holds the
-// target.
-__global__ __launch_bounds__(kSampleThreads) void sample_verify_kernel(
-    const float *__restrict__ logits, const int32_t *__restrict__ tokens_in, const double *__restrict__ uniforms,
-    double temperature, int32_t *__restrict__ tokens_out, int32_t *__restrict__ accept_out, int64_t vocab, int n)
+// One workgroup per stream draws that stream's token.  Sums are taken in a
+// fixed order that never decreases along the index: each thread owns a
+// contiguous chunk of the vocabulary and sums it in index order; chunk sums
+// are prefixed sequentially within a wave, then wave totals sequentially.
+// The drawn index is the first one, in that order, whose running sum exceeds
+// u * Z among indices of nonzero weight; if rounding leaves none, the last
+// index of nonzero weight in the chunk that holds the target.  No positive
+// weight (non-finite logits) draws -1.
+__global__ __launch_bounds__(kSampleThreads) void sample_draw_kernel(const float *__restrict__ logits,
+                                                                     const double *__restrict__ uniforms,
+                                                                     double temperature,
+                                                                     int32_t *__restrict__ tokens_out, int64_t vocab)
 {
     __shared__ double loc_s[kSampleThreads];
     __shared__ double pre_s[kSampleThreads];
     __shared__ double wbase[kSampleWaves + 1];
     __shared__ float wmax[kSampleWaves];
     __shared__ int owner;
-    __shared__ int drawn[PTI_MAX_STREAMS];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, s = blockIdx.x;
     const int64_t chunk = (vocab + kSampleThreads - 1) / kSampleThreads;
     const int64_t j0 = min(vocab, int64_t(tid) * chunk), j1 = min(vocab, j0 + chunk);
-    for (int s = 0; s < n; s++) {
-        const float *v = logits + (int64_t)s * vocab;
-        float m = -__builtin_inff();
-        for (int64_t j = j0; j < j1; j++)
-            m = fmaxf(m, v[j]);
-        m = wave_max_f32(m);
-        if (lane == 0)
-            wmax[wv] = m;
-        __syncthreads();
-        m = wmax[0];
-        for (int i = 1; i < kSampleWaves; i++)
-            m = fmaxf(m, wmax[i]);
-        const double md = m;
-        double loc = 0.0;
-        for (int64_t j = j0; j < j1; j++)
-            loc += exp((double(v[j]) - md) / temperature);
-        loc_s[tid] = loc;
-        if (tid == 0)
-            owner = -1;
-        __syncthreads();
-        if (lane == 0) {
-            double run = 0.0;
-            for (int i = 0; i < 64; i++) {
-                pre_s[tid + i] = run;
-                run += loc_s[tid + i];
-            }
-            wbase[wv + 1] = run;  // wave total, prefixed below
+    const float *v = logits + (int64_t)s * vocab;
+    float m = -__builtin_inff();
+    for (int64_t j = j0; j < j1; j++)
+        m = fmaxf(m, v[j]);
+    m = wave_max_f32(m);
+    if (lane == 0)
+        wmax[wv] = m;
+    __syncthreads();
+    m = wmax[0];
+    for (int i = 1; i < kSampleWaves; i++)
+        m = fmaxf(m, wmax[i]);
+    const double md = m;
+    double loc = 0.0;
+    for (int64_t j = j0; j < j1; j++)
+        loc += exp((double(v[j]) - md) / temperature);
+    loc_s[tid] = loc;
+    if (tid == 0)
+        owner = -1;
+    __syncthreads();
+    if (lane == 0) {
+        double run = 0.0;
+        for (int i = 0; i < 64; i++) {
+            pre_s[tid + i] = run;
+            run += loc_s[tid + i];
         }
-        __syncthreads();
-        if (tid == 0) {
-            double run = 0.0;
-            for (int w = 0; w < kSampleWaves; w++) {
-                const double tot = wbase[w + 1];
-                wbase[w] = run;
-                run += tot;
-            }
-            wbase[kSampleWaves] = run;  // Z
+        wbase[wv + 1] = run;  // wave total, prefixed below
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double run = 0.0;
+        for (int w = 0; w < kSampleWaves; w++) {
+            const double tot = wbase[w + 1];
+            wbase[w] = run;
+            run += tot;
         }
-        __syncthreads();
-        const double Z = wbase[kSampleWaves];
-        const double target = uniforms[s] * Z;
-        const double excl = wbase[wv] + pre_s[tid];
-        if (loc > 0.0 && excl <= target)
-            atomicMax(&owner, tid);
-        __syncthreads();
-        if (tid == 0 && owner < 0) {  // no positive weight: non-finite logits
-            drawn[s] = -1;
-            tokens_out[s] = -1;
-        }
-        if (tid == owner) {
-            double run = excl;
-            int64_t pick = -1, last = -1;
-            for (int64_t j = j0; j < j1; j++) {
-                const double e = exp((double(v[j]) - md) / temperature);
-                if (e > 0.0) {
-                    last = j;
-                    run += e;
-                    if (run > target) {
-                        pick = j;
-                        break;
-                    }
+        wbase[kSampleWaves] = run;  // Z
+    }
+    __syncthreads();
+    const double Z = wbase[kSampleWaves];
+    const double target = uniforms[s] * Z;
+    const double excl = wbase[wv] + pre_s[tid];
+    if (loc > 0.0 && excl <= target)
+        atomicMax(&owner, tid);
+    __syncthreads();
+    if (tid == 0 && owner < 0)  // no positive weight: non-finite logits
+        tokens_out[s] = -1;
+    if (tid == owner) {
+        double run = excl;
+        int64_t pick = -1, last = -1;
+        for (int64_t j = j0; j < j1; j++) {
+            const double e = exp((double(v[j]) - md) / temperature);
+            if (e > 0.0) {
+                last = j;
+                run += e;
+                if (run > target) {
+                    pick = j;
+                    break;
                 }
             }
-            if (pick < 0)
-                pick = last;
-            drawn[s] = int(pick);
-            tokens_out[s] = int32_t(pick);
         }
-        __syncthreads();
+        if (pick < 0)
+            pick = last;
+        tokens_out[s] = int32_t(pick);
     }
-    if (tid == 0) {
+}
+
+// The accept count from the draws: 1 + the leading run of i >= 1 with
+// tokens_in[i] == tokens_out[i - 1].
+__global__ void accept_kernel(const int32_t *__restrict__ tokens_in, const int32_t *__restrict__ tokens_out,
+                              int32_t *__restrict__ accept_out, int n)
+{
+    if (threadIdx.x == 0) {
         int a = 1;
         for (int i = 1; i < n; i++) {
-            if (tokens_in[i] != drawn[i - 1])
+            if (tokens_in[i] != tokens_out[i - 1])
                 break;
             a++;
         }
@@ -408,7 +410,9 @@ extern "C" int pti_sample_verify(const float *logits, const int32_t *tokens_in, 
             return PTI_ERR_OVERLAP;
     if (pti::overlap(O, C))
         return PTI_ERR_OVERLAP;
-    hipLaunchKernelGGL(sample_verify_kernel, dim3(1), dim3(kSampleThreads), 0, static_cast<hipStream_t>(stream),
-                       logits, tokens_in, uniforms, temperature, tokens_out, accept_out, vocab, n_streams);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(sample_draw_kernel, dim3((unsigned)n_streams), dim3(kSampleThreads), 0, st, logits, uniforms,
+                       temperature, tokens_out, vocab);
+    hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, st, tokens_in, tokens_out, accept_out, n_streams);
     return launch_status();
 }
