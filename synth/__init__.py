@@ -30,6 +30,7 @@ SEED_SSQ_FFN = 2
 SEED_Q8_FFN = 3
 SEED_LAYER = 4
 SEED_TOY = 1
+SEED_BIG = 5
 
 
 def rng(seed: int) -> np.random.Generator:

@@ -272,6 +272,59 @@ def test_layer_sweep_sampled(env, name, rows, cols):
     assert np.all(np.abs(y[0][idx].astype(np.float64) - ya[idx]) <= 2 * TOL * ta)
 
 
+# ------------------------------------------------------------ beyond 4 GiB
+
+def _tiled(env, base, rows):
+    """Device matrix of `rows` rows repeating the packed rows of `base`."""
+    torch, pti, dev = env
+    b = torch.from_numpy(base).to(dev)
+    reps = (rows + base.shape[0] - 1) // base.shape[0]
+    return b.repeat(reps, 1)[:rows].contiguous()
+
+
+def test_q8_beyond_4gib_all_rows(env):
+    """4.56 GB of Q8 weights (4,194,309 rows x 1024 cols, 1088-byte rows):
+    the byte offsets of rows pass 2^31 and 2^32.  The matrix repeats a
+    4096-row base whose period (4096 x 1088 bytes) divides neither, so a
+    wrapped offset lands on a row with other values.  Every row is checked
+    against the oracle's result for its base row."""
+    torch, pti, dev = env
+    rows, cols, period = (1 << 22) + 5, 1024, 4096
+    _note(f"q8 {rows}x{cols} tiled from {period} rows")
+    d = synth.q8(period, cols, 2, synth.SEED_BIG)
+    w = _tiled(env, pti.pack_q8(d["Q"], d["S"]), rows)
+    assert w.numel() > 2 ** 32
+    y = pti.gemv_q8_multi(w, torch.from_numpy(d["X"]).to(dev))
+    torch.cuda.synchronize()
+    del w
+    torch.cuda.empty_cache()
+    e, t = oracle.gemv_q8(oracle.pack_q8(d["Q"], d["S"]), period, cols, d["X"])
+    idx = np.arange(rows) % period
+    y = y.cpu().numpy()
+    for s in range(2):
+        check_bound(y[s], e[s][idx], t[s][idx], f"stream {s}")
+
+
+def test_ssq_beyond_4gib_all_rows(env):
+    """The SSQ twin GEMV over 4.56 GB (2,097,155 rows x 1024 cols, 2176-byte
+    rows, a 2048-row period), every row of both twins checked."""
+    torch, pti, dev = env
+    rows, cols, period = (1 << 21) + 3, 1024, 2048
+    _note(f"ssq {rows}x{cols} tiled from {period} rows")
+    d = synth.twin(period, cols, synth.SEED_BIG)
+    w = _tiled(env, pti.pack_ssq(d["A"], d["B"], d["sA"], d["sB"]), rows)
+    assert w.numel() > 2 ** 32
+    ya, yb = pti.gemv_ssq(w, torch.from_numpy(d["xA"]).to(dev), torch.from_numpy(d["xB"]).to(dev))
+    torch.cuda.synchronize()
+    del w
+    torch.cuda.empty_cache()
+    ea, eb, ta, tb = oracle.gemv_ssq(oracle.pack_ssq(d["A"], d["B"], d["sA"], d["sB"]), period, cols, d["xA"],
+                                     d["xB"])
+    idx = np.arange(rows) % period
+    check_bound(ya.cpu().numpy(), ea[idx], ta[idx], "y_A")
+    check_bound(yb.cpu().numpy(), eb[idx], tb[idx], "y_B")
+
+
 # ------------------------------------------------------------ verify
 
 def gpu_verify(env, logits, tokens):
