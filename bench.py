@@ -25,7 +25,8 @@ Also reported on the same JSON line:
     graph; twin-KV attention; the greedy and sampled verify at the toy
     decoder's vocabulary; the host packer;
   * cpu_baseline: the fp64 oracle (scalar C, one host core) running the same
-    SSQ GEMV, timed on a bounded number of passes.
+    SSQ GEMV, timed on a bounded number of passes, with the host's CPU model
+    and the same oracle code split over host threads beside it.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -92,10 +93,40 @@ def cpu_baseline(d, budget_s: float):
         if el >= budget_s:
             break
     per = el / n
-    return {"value": round(P.nbytes / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} full {ROWS}x{COLS} SSQ twin GEMVs (both twins), scalar fp64 C oracle, "
-                      f"{per:.3f} s each, {el:.1f} s total",
-            "gemv_per_s": round(1.0 / per, 4)}
+    out = {"value": round(P.nbytes / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{n} full {ROWS}x{COLS} SSQ twin GEMVs (both twins), scalar fp64 C oracle, "
+                     f"{per:.3f} s each, {el:.1f} s total",
+           "gemv_per_s": round(1.0 / per, 4), "host_nproc": os.cpu_count(), "host_cpu": _cpu_model()}
+    # the same per-row oracle code with the rows split over host threads (the
+    # C call releases the GIL), for about half the budget
+    from concurrent.futures import ThreadPoolExecutor
+    nt = max(1, min(os.cpu_count() or 1, 16))
+    parts = np.array_split(np.arange(ROWS, dtype=np.int64), nt)
+    t0 = time.perf_counter()
+    n = 0
+    with ThreadPoolExecutor(nt) as ex:
+        while True:
+            list(ex.map(lambda idx: oracle.gemv_ssq_rows(P, ROWS, COLS, d["xA"], d["xB"], idx), parts))
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s / 2:
+                break
+    per = el / n
+    out["threaded"] = {"value": round(P.nbytes / per / 1e9, 4), "unit": "GB/s", "cores": nt,
+                       "sample": f"{n} full GEMVs, rows split over {nt} threads, {per:.3f} s each",
+                       "gemv_per_s": round(1.0 / per, 4)}
+    return out
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
