@@ -12,7 +12,7 @@ reads its weights from HBM.
 Also reported on the same JSON line:
   * roofline: the step's entry point, both its kernels with the gap between
     them (algorithmic bytes per call / its time, the median over 10 runs of
-    100 back-to-back calls timed with HIP events on its stream) against 8 TB/s
+    200 back-to-back calls timed with HIP events on its stream) against 8 TB/s
     HBM, its HBM traffic (both kernels) from the committed PMC summary, the
     kernels' own rocprofv3 averages from the committed kernel-trace summary,
     their L2 hit rates from the committed TCC summary, and its rate against
@@ -69,7 +69,7 @@ def timed_loop(torch, fn, n_iter, stream, i0=0):
     return start.elapsed_time(end) / n_iter
 
 
-def timed_stats(torch, fn, stream, reps=10, per_rep=100, warmup=50):
+def timed_stats(torch, fn, stream, reps=10, per_rep=200, warmup=50):
     """Per-call time over `reps` back-to-back runs of `per_rep` calls each (after
     `warmup` calls): median, p10 and p90 in microseconds."""
     for i in range(warmup):
