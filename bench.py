@@ -532,8 +532,10 @@ def verify_and_pack(torch, pti, dev, stream, d):
                          stream, reps=5, per_rep=50, warmup=10)
         out[f"verify_greedy_n{n}_v32000"] = st
         u = torch.rand(n, dtype=torch.float64, generator=g).to(dev)
+        sw = pti.sample_verify_workspace(32000, n, dev)
         st = timed_stats(torch, lambda i: L.pti_sample_verify(logits.data_ptr(), tok.data_ptr(), u.data_ptr(), 0.7,
-                                                              am.data_ptr(), acc.data_ptr(), 32000, n, sp),
+                                                              am.data_ptr(), acc.data_ptr(), 32000, n,
+                                                              sw.data_ptr(), sw.numel(), sp),
                          stream, reps=5, per_rep=50, warmup=10)
         out[f"verify_sampled_n{n}_v32000_t0.7"] = st
         log(f"verify n={n}: {out[f'verify_greedy_n{n}_v32000']}")

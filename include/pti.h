@@ -230,20 +230,28 @@ int pti_verify_argmax(const float *logits, const int32_t *tokens_in, int32_t *ar
  * w_j = exp((logits[n][j] - max_j logits[n][j]) / temperature) in fp64, and
  * tokens_out[n] = the first index j of nonzero weight at which a running sum
  * of the weights exceeds uniforms[n] * sum_j w_j (if rounding leaves none, the
- * last index of nonzero weight before the target).  The running sum is taken
- * in a fixed, index-monotone order (per 1/1024 of the vocabulary in index
- * order, then across those parts in order), so the draw equals an in-order
- * sequential inverse-CDF draw except where u * sum lies within a few fp64 ulps
- * of a cumulative sum.  accept_out[0] as in pti_verify_argmax, with the drawn
- * tokens in place of the argmaxes.
+ * last index of nonzero weight before the target).  The vocabulary is cut
+ * into parts of 2048 indices: a part's weights are exp((l_j - m_b) / T)
+ * exp((m_b - M) / T) with m_b the part's max and M the stream's.  The running
+ * sum is taken in a fixed, index-monotone order (over the parts in index
+ * order, then inside the part that holds the target in index order), so the
+ * draw equals an in-order sequential inverse-CDF draw except where u * sum
+ * lies within a few fp64 ulps of a cumulative sum.  accept_out[0] as in
+ * pti_verify_argmax, with the drawn tokens in place of the argmaxes.
  * logits: device fp32 [n_streams][vocab] (finite; otherwise tokens_out is
  * unspecified and may be -1); tokens_in: device int32 [n_streams];
  * uniforms: device fp64 [n_streams] in [0, 1) (8-byte aligned); temperature:
  * finite, > 0; tokens_out: device int32 [n_streams]; accept_out: device int32
- * [1].  Outputs must not overlap inputs or each other.  Two kernels are
- * enqueued on `stream`: one workgroup per stream draws, then the accept count. */
+ * [1]; work: device scratch of at least
+ * pti_sample_verify_workspace_bytes(vocab, n_streams) bytes (16-byte aligned,
+ * any contents; 0 for invalid sizes).  Outputs and work must not overlap
+ * inputs or each other.  Three kernels are enqueued on `stream` (the parts'
+ * sums, one workgroup per stream for the draw, the accept count); calls
+ * sharing a workspace must not run at the same time. */
+size_t pti_sample_verify_workspace_bytes(int64_t vocab, int n_streams);
 int pti_sample_verify(const float *logits, const int32_t *tokens_in, const double *uniforms, double temperature,
-                      int32_t *tokens_out, int32_t *accept_out, int64_t vocab, int n_streams, void *stream);
+                      int32_t *tokens_out, int32_t *accept_out, int64_t vocab, int n_streams, void *work,
+                      size_t work_bytes, void *stream);
 
 /* ------------------------------------------------------------------------- */
 /* Decoder-stack glue [Digest, implementation architecture: the forward pass in

@@ -24,7 +24,7 @@ from .build import LIB as LIB_PATH
 
 __all__ = [
     "PtiError", "lib", "ssq_bytes", "q8_bytes", "pack_ssq", "unpack_ssq", "pack_q8", "unpack_q8",
-    "ssq_split", "ssq_join", "gemv_ssq", "gemv_q8_multi", "verify_argmax", "status_str", "sample_verify",
+    "ssq_split", "ssq_join", "gemv_ssq", "gemv_q8_multi", "verify_argmax", "status_str", "sample_verify", "sample_verify_workspace",
     "embed_q8", "embed_ssq", "rmsnorm", "silu_mul", "add", "ToyStack", "FMT_Q8", "FMT_SSQ",
 ]
 
@@ -40,7 +40,7 @@ EXPORTS = (
     "pti_status_str", "pti_last_hip_error", "pti_abi_version", "pti_ssq_bytes", "pti_q8_bytes", "pti_pack_ssq",
     "pti_unpack_ssq", "pti_pack_q8", "pti_unpack_q8", "pti_ssq_split", "pti_ssq_join", "pti_gemv_ssq",
     "pti_gemv_ssq_verify", "pti_gemv_q8_multi", "pti_gemv_ssq_grouped", "pti_gemv_q8_multi_grouped",
-    "pti_gemv_ssq_multi", "pti_attn_workspace_bytes", "pti_attn_decode", "pti_verify_argmax", "pti_sample_verify", "pti_embed_q8", "pti_embed_ssq", "pti_rmsnorm",
+    "pti_gemv_ssq_multi", "pti_attn_workspace_bytes", "pti_attn_decode", "pti_verify_argmax", "pti_sample_verify", "pti_sample_verify_workspace_bytes", "pti_embed_q8", "pti_embed_ssq", "pti_rmsnorm",
     "pti_silu_mul", "pti_add", "pti_toy_workspace_bytes", "pti_toy_forward", "pti_toy_decode",
     "pti_toy_forward_graph", "pti_graph_launch", "pti_graph_destroy",
 )
@@ -102,7 +102,9 @@ def lib() -> ctypes.CDLL:
         L.pti_gemv_ssq_grouped.argtypes = [_P, _P, _INT, _P, _P, _P, _P, _I64, _P]
         L.pti_gemv_q8_multi_grouped.argtypes = [_P, _P, _INT, _P, _P, _I64, _INT, _P]
         L.pti_verify_argmax.argtypes = [_P, _P, _P, _P, _I64, _INT, _P]
-        L.pti_sample_verify.argtypes = [_P, _P, _P, ctypes.c_double, _P, _P, _I64, _INT, _P]
+        L.pti_sample_verify.argtypes = [_P, _P, _P, ctypes.c_double, _P, _P, _I64, _INT, _P, ctypes.c_size_t, _P]
+        L.pti_sample_verify_workspace_bytes.argtypes = [_I64, _INT]
+        L.pti_sample_verify_workspace_bytes.restype = ctypes.c_size_t
         L.pti_embed_q8.argtypes = [_P, _P, _P, _I64, _I64, _INT, _P]
         L.pti_embed_ssq.argtypes = [_P, _P, _P, _I64, _I64, _P]
         L.pti_rmsnorm.argtypes = [_P, _P, _I64, _INT, ctypes.c_float, _P]
@@ -446,10 +448,20 @@ def verify_argmax(logits, tokens_in, argmax_out=None, accept_out=None, stream=No
     return argmax_out, accept_out
 
 
-def sample_verify(logits, tokens_in, uniforms, temperature: float, tokens_out=None, accept_out=None, stream=None):
+def sample_verify_workspace(vocab: int, n_streams: int, device):
+    """Scratch for sample_verify (no initialisation needed)."""
+    nb = lib().pti_sample_verify_workspace_bytes(vocab, n_streams)
+    if nb == 0:
+        raise PtiError("pti_sample_verify_workspace_bytes", -2)
+    return _torch().empty(nb, dtype=_torch().uint8, device=device)
+
+
+def sample_verify(logits, tokens_in, uniforms, temperature: float, tokens_out=None, accept_out=None, work=None,
+                  stream=None):
     """Sampled verify at temperature > 0: one inverse-CDF draw per stream with
     uniforms[n], then the accept count.  logits: float32 [N, vocab];
-    tokens_in: int32 [N]; uniforms: float64 [N] (device)."""
+    tokens_in: int32 [N]; uniforms: float64 [N] (device); work: from
+    sample_verify_workspace (allocated here when omitted)."""
     torch = _torch()
     _dev(logits, "logits", torch.float32), _dev(tokens_in, "tokens_in", torch.int32)
     _dev(uniforms, "uniforms", torch.float64)
@@ -463,9 +475,11 @@ def sample_verify(logits, tokens_in, uniforms, temperature: float, tokens_out=No
         tokens_out, "tokens_out", torch.int32)
     accept_out = torch.empty(1, dtype=torch.int32, device=dev) if accept_out is None else _dev(
         accept_out, "accept_out", torch.int32)
+    work = sample_verify_workspace(vocab, n, dev) if work is None else work
     _check("pti_sample_verify", lib().pti_sample_verify(logits.data_ptr(), tokens_in.data_ptr(), uniforms.data_ptr(),
                                                         float(temperature), tokens_out.data_ptr(),
-                                                        accept_out.data_ptr(), vocab, n, _stream(stream)))
+                                                        accept_out.data_ptr(), vocab, n, work.data_ptr(),
+                                                        work.numel() * work.element_size(), _stream(stream)))
     return tokens_out, accept_out
 
 

@@ -156,48 +156,71 @@ __global__ void add_kernel(const float *a, const float *b, float *y, int64_t n)
 
 // ------------------------------------------------------------------ sampled verify
 
-constexpr int kSampleThreads = 1024;
-constexpr int kSampleWaves = kSampleThreads / 64;
+// A stream's vocabulary is cut into parts of kSvPart consecutive indices.
+// Pass 1 (one workgroup per part and stream): the part's max m_b and
+// S_b = sum_j exp((l_j - m_b) / T) in fp64.  Pass 2 (one workgroup per
+// stream): M = max_b m_b; part weights W_b = S_b exp((m_b - M) / T); the
+// running sum over parts in index order locates the part that holds u * Z
+// (Z = sum_b W_b); inside it, the weights w_j = exp((l_j - m_b) / T)
+// exp((m_b - M) / T) are summed in index order from the part's start to find
+// the index.  Every sum runs in a fixed order that never decreases along the
+// index: within a workgroup each thread owns a contiguous run and the runs
+// are prefixed sequentially within a wave, then across waves.  The drawn index
+// is the first of nonzero weight whose running sum exceeds u * Z; if rounding
+// leaves none in the thread run that holds the target, the last index of
+// nonzero weight in that run.  No positive weight (non-finite logits) draws -1.
+constexpr int kSvPart = 2048;
+constexpr int kSvThreads = 256;
+constexpr int kSvWaves = kSvThreads / 64;
 
-// One workgroup per stream draws that stream's token.  Sums are taken in a
-// fixed order that never decreases along the index: each thread owns a
-// contiguous chunk of the vocabulary and sums it in index order; chunk sums
-// are prefixed sequentially within a wave, then wave totals sequentially.
-// The drawn index is the first one, in that order, whose running sum exceeds
-// u * Z among indices of nonzero weight; if rounding leaves none, the last
-// index of nonzero weight in the chunk that holds the target.  No positive
-// weight (non-finite logits) draws -1.
-__global__ __launch_bounds__(kSampleThreads) void sample_draw_kernel(const float *__restrict__ logits,
-                                                                     const double *__restrict__ uniforms,
-                                                                     double temperature,
-                                                                     int32_t *__restrict__ tokens_out, int64_t vocab)
+struct SvPart {
+    double m, s;  // the part's max logit and its exp-sum relative to that max
+};
+
+__global__ __launch_bounds__(kSvThreads) void sv_part_kernel(const float *__restrict__ logits, double temperature,
+                                                             SvPart *__restrict__ parts, int64_t vocab, int64_t nparts)
 {
-    __shared__ double loc_s[kSampleThreads];
-    __shared__ double pre_s[kSampleThreads];
-    __shared__ double wbase[kSampleWaves + 1];
-    __shared__ float wmax[kSampleWaves];
-    __shared__ int owner;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, s = blockIdx.x;
-    const int64_t chunk = (vocab + kSampleThreads - 1) / kSampleThreads;
-    const int64_t j0 = min(vocab, int64_t(tid) * chunk), j1 = min(vocab, j0 + chunk);
-    const float *v = logits + (int64_t)s * vocab;
+    __shared__ float wmax[kSvWaves];
+    __shared__ double wsum[kSvWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t b = blockIdx.x, s = blockIdx.y;
+    const int64_t j0 = b * kSvPart;
+    const int n = (int)min<int64_t>(kSvPart, vocab - j0);
+    const float *v = logits + s * vocab + j0;
     float m = -__builtin_inff();
-    for (int64_t j = j0; j < j1; j++)
-        m = fmaxf(m, v[j]);
+    for (int i = tid; i < n; i += kSvThreads)
+        m = fmaxf(m, v[i]);
     m = wave_max_f32(m);
     if (lane == 0)
         wmax[wv] = m;
     __syncthreads();
     m = wmax[0];
-    for (int i = 1; i < kSampleWaves; i++)
+    for (int i = 1; i < kSvWaves; i++)
         m = fmaxf(m, wmax[i]);
     const double md = m;
-    double loc = 0.0;
-    for (int64_t j = j0; j < j1; j++)
-        loc += exp((double(v[j]) - md) / temperature);
+    double acc = 0.0;
+    if (m > -__builtin_inff())
+        for (int i = tid; i < n; i += kSvThreads)
+            acc += exp((double(v[i]) - md) / temperature);
+    acc = wave_sum_f64(acc);
+    if (lane == 0)
+        wsum[wv] = acc;
+    __syncthreads();
+    if (tid == 0) {
+        double t = wsum[0];
+        for (int i = 1; i < kSvWaves; i++)
+            t += wsum[i];
+        parts[s * nparts + b] = SvPart{md, t};
+    }
+}
+
+// Index-monotone exclusive prefix of the threads' values `loc` (thread tid
+// owns a contiguous run): sequential over the 64 lanes of a wave, then over
+// the waves.  Returns this thread's exclusive prefix; *total gets the sum.
+__device__ __forceinline__ double block_prefix(double loc, double *loc_s, double *pre_s, double *wbase, double *total)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     loc_s[tid] = loc;
-    if (tid == 0)
-        owner = -1;
     __syncthreads();
     if (lane == 0) {
         double run = 0.0;
@@ -205,44 +228,131 @@ __global__ __launch_bounds__(kSampleThreads) void sample_draw_kernel(const float
             pre_s[tid + i] = run;
             run += loc_s[tid + i];
         }
-        wbase[wv + 1] = run;  // wave total, prefixed below
+        wbase[wv + 1] = run;
     }
     __syncthreads();
     if (tid == 0) {
         double run = 0.0;
-        for (int w = 0; w < kSampleWaves; w++) {
-            const double tot = wbase[w + 1];
+        for (int w = 0; w < kSvWaves; w++) {
+            const double t = wbase[w + 1];
             wbase[w] = run;
-            run += tot;
+            run += t;
         }
-        wbase[kSampleWaves] = run;  // Z
+        wbase[kSvWaves] = run;
     }
     __syncthreads();
-    const double Z = wbase[kSampleWaves];
+    *total = wbase[kSvWaves];
+    return wbase[wv] + pre_s[tid];
+}
+
+__global__ __launch_bounds__(kSvThreads) void sv_draw_kernel(const float *__restrict__ logits,
+                                                             const double *__restrict__ uniforms, double temperature,
+                                                             const SvPart *__restrict__ parts,
+                                                             int32_t *__restrict__ tokens_out, int64_t vocab,
+                                                             int64_t nparts)
+{
+    __shared__ double loc_s[kSvThreads];
+    __shared__ double pre_s[kSvThreads];
+    __shared__ double wbase[kSvWaves + 1];
+    __shared__ float wmax[kSvWaves];
+    __shared__ int owner;
+    __shared__ int64_t own_part;
+    __shared__ double own_excl;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t s = blockIdx.x;
+    const SvPart *ps = parts + s * nparts;
+    // M = max over the parts
+    float M = -__builtin_inff();
+    for (int64_t i = tid; i < nparts; i += kSvThreads)
+        M = fmaxf(M, (float)ps[i].m);
+    M = wave_max_f32(M);
+    if (lane == 0)
+        wmax[wv] = M;
+    __syncthreads();
+    M = wmax[0];
+    for (int i = 1; i < kSvWaves; i++)
+        M = fmaxf(M, wmax[i]);
+    const double Md = M;
+    auto factor = [&](double mb) { return mb > -__builtin_inff() ? exp((mb - Md) / temperature) : 0.0; };
+
+    // parts: thread tid owns the contiguous run [p0, p1)
+    const int64_t cp = (nparts + kSvThreads - 1) / kSvThreads;
+    const int64_t p0 = min(nparts, tid * cp), p1 = min(nparts, p0 + cp);
+    double loc = 0.0;
+    for (int64_t p = p0; p < p1; p++)
+        loc += ps[p].s * factor(ps[p].m);
+    if (tid == 0)
+        owner = -1;
+    double Z;
+    const double excl = block_prefix(loc, loc_s, pre_s, wbase, &Z);
     const double target = uniforms[s] * Z;
-    const double excl = wbase[wv] + pre_s[tid];
     if (loc > 0.0 && excl <= target)
         atomicMax(&owner, tid);
     __syncthreads();
-    if (tid == 0 && owner < 0)  // no positive weight: non-finite logits
-        tokens_out[s] = -1;
+    if (owner < 0) {  // no positive weight: non-finite logits
+        if (tid == 0)
+            tokens_out[s] = -1;
+        return;
+    }
     if (tid == owner) {
         double run = excl;
         int64_t pick = -1, last = -1;
-        for (int64_t j = j0; j < j1; j++) {
-            const double e = exp((double(v[j]) - md) / temperature);
+        double pick_excl = 0.0, last_excl = 0.0;
+        for (int64_t p = p0; p < p1; p++) {
+            const double w = ps[p].s * factor(ps[p].m);
+            if (w > 0.0) {
+                last = p, last_excl = run;
+                if (run + w > target) {
+                    pick = p, pick_excl = run;
+                    break;
+                }
+                run += w;
+            }
+        }
+        own_part = pick >= 0 ? pick : last;
+        own_excl = pick >= 0 ? pick_excl : last_excl;
+    }
+    __syncthreads();
+
+    // inside the part: thread tid owns the contiguous run [q0, q1)
+    const int64_t b = own_part;
+    const int64_t j0 = b * kSvPart;
+    const int n = (int)min<int64_t>(kSvPart, vocab - j0);
+    const float *v = logits + s * vocab + j0;
+    const double mb = ps[b].m, fb = factor(mb);
+    const int cq = (n + kSvThreads - 1) / kSvThreads;
+    const int q0 = min(n, tid * cq), q1 = min(n, q0 + cq);
+    double loc2 = 0.0;
+    for (int q = q0; q < q1; q++)
+        loc2 += exp((double(v[q]) - mb) / temperature) * fb;
+    if (tid == 0)
+        owner = -1;
+    double Zp;
+    const double excl2 = own_excl + block_prefix(loc2, loc_s, pre_s, wbase, &Zp);
+    if (loc2 > 0.0 && excl2 <= target)
+        atomicMax(&owner, tid);
+    __syncthreads();
+    const int own2 = owner;
+    if (own2 < 0) {  // cannot happen when the part's weight is positive; keep the part's first index
+        if (tid == 0)
+            tokens_out[s] = (int32_t)j0;
+        return;
+    }
+    if (tid == own2) {
+        double run = excl2;
+        int pick = -1, last = -1;
+        for (int q = q0; q < q1; q++) {
+            const double e = exp((double(v[q]) - mb) / temperature) * fb;
             if (e > 0.0) {
-                last = j;
+                last = q;
                 run += e;
                 if (run > target) {
-                    pick = j;
+                    pick = q;
                     break;
                 }
             }
         }
-        if (pick < 0)
-            pick = last;
-        tokens_out[s] = int32_t(pick);
+        tokens_out[s] = (int32_t)(j0 + (pick >= 0 ? pick : last));
     }
 }
 
@@ -261,6 +371,8 @@ __global__ void accept_kernel(const int32_t *__restrict__ tokens_in, const int32
         accept_out[0] = a;
     }
 }
+
+int64_t sv_parts(int64_t vocab) { return (vocab + kSvPart - 1) / kSvPart; }
 
 int launch_status()
 {
@@ -389,30 +501,43 @@ extern "C" int pti_add(const float *a, const float *b, float *y, int64_t n, void
     return launch_status();
 }
 
+extern "C" size_t pti_sample_verify_workspace_bytes(int64_t vocab, int n_streams)
+{
+    if (vocab < 1 || vocab > PTI_MAX_VOCAB || n_streams < 1 || n_streams > PTI_MAX_STREAMS)
+        return 0;
+    return size_t(n_streams) * size_t(sv_parts(vocab)) * sizeof(SvPart);
+}
+
 extern "C" int pti_sample_verify(const float *logits, const int32_t *tokens_in, const double *uniforms,
                                  double temperature, int32_t *tokens_out, int32_t *accept_out, int64_t vocab,
-                                 int n_streams, void *stream)
+                                 int n_streams, void *work, size_t work_bytes, void *stream)
 {
-    if (!logits || !tokens_in || !uniforms || !tokens_out || !accept_out)
+    if (!logits || !tokens_in || !uniforms || !tokens_out || !accept_out || !work)
         return PTI_ERR_NULL;
     if (vocab < 1 || vocab > PTI_MAX_VOCAB || !(temperature > 0.0) || !std::isfinite(temperature))
         return PTI_ERR_SHAPE;
     if (n_streams < 1 || n_streams > PTI_MAX_STREAMS)
         return PTI_ERR_NSTREAMS;
+    if (work_bytes < pti_sample_verify_workspace_bytes(vocab, n_streams))
+        return PTI_ERR_SHAPE;
     if (!pti::aligned(logits, 4) || !pti::aligned(tokens_in, 4) || !pti::aligned(uniforms, 8) ||
-        !pti::aligned(tokens_out, 4) || !pti::aligned(accept_out, 4))
+        !pti::aligned(tokens_out, 4) || !pti::aligned(accept_out, 4) || !pti::aligned(work, 16))
         return PTI_ERR_ALIGN;
     const size_t ns = size_t(n_streams);
     const pti::Range L{logits, ns * size_t(vocab) * 4}, T{tokens_in, ns * 4}, U{uniforms, ns * 8},
-        O{tokens_out, ns * 4}, C{accept_out, 4};
-    for (const pti::Range &out : {O, C})
+        O{tokens_out, ns * 4}, C{accept_out, 4}, W{work, pti_sample_verify_workspace_bytes(vocab, n_streams)};
+    for (const pti::Range &out : {O, C, W})
         if (pti::overlap(out, L) || pti::overlap(out, T) || pti::overlap(out, U))
             return PTI_ERR_OVERLAP;
-    if (pti::overlap(O, C))
+    if (pti::overlap(O, C) || pti::overlap(O, W) || pti::overlap(C, W))
         return PTI_ERR_OVERLAP;
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(sample_draw_kernel, dim3((unsigned)n_streams), dim3(kSampleThreads), 0, st, logits, uniforms,
-                       temperature, tokens_out, vocab);
+    SvPart *parts = static_cast<SvPart *>(work);
+    const int64_t np = sv_parts(vocab);
+    hipLaunchKernelGGL(sv_part_kernel, dim3((unsigned)np, (unsigned)n_streams), dim3(kSvThreads), 0, st, logits,
+                       temperature, parts, vocab, np);
+    hipLaunchKernelGGL(sv_draw_kernel, dim3((unsigned)n_streams), dim3(kSvThreads), 0, st, logits, uniforms,
+                       temperature, parts, tokens_out, vocab, np);
     hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, st, tokens_in, tokens_out, accept_out, n_streams);
     return launch_status();
 }

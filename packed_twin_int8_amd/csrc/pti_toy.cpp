@@ -31,7 +31,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
-    size_t h, r, gu, x, logits, tok, out, acc, uni, total;
+    size_t h, r, gu, x, logits, tok, out, acc, uni, sv, total;
 };
 
 Layout layout(const pti_toy_model &m, int n)
@@ -53,6 +53,7 @@ Layout layout(const pti_toy_model &m, int n)
     L.out = take(PTI_MAX_STREAMS * 4);
     L.acc = take(4);
     L.uni = take(PTI_MAX_STREAMS * 8);
+    L.sv = take(pti_sample_verify_workspace_bytes(m.vocab, n));  // the sampled verify's part sums
     L.total = off;
     return L;
 }
@@ -189,7 +190,8 @@ struct Decoder {
         } else {
             const double *u = uniforms + (size_t(step) * 2 * N + size_t(slot0));
             PTI_TRY(hip_status(hipMemcpyAsync(dev_uni(), u, size_t(n) * 8, hipMemcpyHostToDevice, st)));
-            PTI_TRY(pti_sample_verify(lg, dev_tok(), dev_uni(), temp, dev_out(), dev_acc(), m.vocab, n, s));
+            PTI_TRY(pti_sample_verify(lg, dev_tok(), dev_uni(), temp, dev_out(), dev_acc(), m.vocab, n, work + L.sv,
+                                      pti_sample_verify_workspace_bytes(m.vocab, n), s));
         }
         PTI_TRY(hip_status(hipMemcpyAsync(out, dev_out(), size_t(n) * 4, hipMemcpyDeviceToHost, st)));
         PTI_TRY(hip_status(hipMemcpyAsync(accept, dev_acc(), 4, hipMemcpyDeviceToHost, st)));

@@ -285,7 +285,10 @@ def test_no_device_reports_hip_error():
 def test_sample_verify_errors():
     L = pti.lib()
     f = L.pti_sample_verify
-    ok = (_fake(A0), _fake(A1), _fake(A2), 0.7, _fake(A3), _fake(A4), 100, 2, None)
+    wb = L.pti_sample_verify_workspace_bytes
+    assert wb(100, 2) == 2 * 16 and wb(2049, 4) == 4 * 2 * 16 and wb(32000, 4) == 4 * 16 * 16
+    assert wb(0, 1) == 0 and wb(100, 0) == 0 and wb(100, 5) == 0
+    ok = (_fake(A0), _fake(A1), _fake(A2), 0.7, _fake(A3), _fake(A4), 100, 2, _fake(A4 + 0x1000), 32, None)
 
     def call(**kw):
         a = list(ok)
@@ -301,6 +304,11 @@ def test_sample_verify_errors():
     assert call(a2=_fake(A2 + 4)) == ALIGN
     assert call(a4=_fake(A2 + 8)) == OVERLAP  # tokens_out inside uniforms [A2, A2+16)
     assert call(a5=_fake(A3 + 4)) == OVERLAP  # accept_out inside tokens_out
+    assert call(a8=None) == NULL
+    assert call(a9=31) == SHAPE  # workspace too small
+    assert call(a8=_fake(A4 + 0x1008)) == ALIGN
+    assert call(a8=_fake(A2)) == OVERLAP  # workspace over the uniforms
+    assert call(a8=_fake(A4 - 16)) == OVERLAP  # workspace over accept_out
 
 
 def test_glue_errors():
@@ -341,8 +349,8 @@ def test_toy_errors():
     m = _toy()
     n = ws(ctypes.byref(m), 4)
     # h, r: 4*64*4 = 1024 each; stacked gate|up 4*2*96*4 = 3072; silu*up 4*96*4 = 1536;
-    # logits 1600 (-> 1792); four small regions
-    assert n == 2 * 1024 + 3072 + 1536 + 1792 + 4 * 256
+    # logits 1600 (-> 1792); four small regions and the sampled verify's part sums (4 x 16 -> 256)
+    assert n == 2 * 1024 + 3072 + 1536 + 1792 + 5 * 256
     assert ws(ctypes.byref(m), 0) == 0 and ws(ctypes.byref(m), 5) == 0
     assert ws(ctypes.byref(_toy(fmt=pti.FMT_SSQ)), 4) == 0 and ws(ctypes.byref(_toy(fmt=pti.FMT_SSQ)), 2) > 0
     for bad in (_toy(fmt=2), _toy(layers=0), _toy(layers=65), _toy(hidden=48), _toy(ffn=0), _toy(vocab=0),
