@@ -38,7 +38,6 @@ uniforms are inputs: the caller supplies them, one per pass slot.
 
 from __future__ import annotations
 
-import math
 from typing import Callable, Sequence
 
 import numpy as np

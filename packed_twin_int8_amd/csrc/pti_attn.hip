@@ -80,8 +80,6 @@ struct AttnArgs {
     float scale;          // 1 / sqrt(d)
 };
 
-__device__ __forceinline__ float h2f(uint32_t bits16) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16); }
-
 __device__ __forceinline__ uint16_t f2h(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
 
 // The value DPP moves into each lane under control CTRL (rows in ROW_MASK);

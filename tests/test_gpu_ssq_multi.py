@@ -6,7 +6,6 @@ depend on the stream count), and the full-size case is within
 1e-5 * sum |terms| of the oracle on sampled rows.
 """
 
-import sys
 
 import numpy as np
 import pytest

@@ -3,9 +3,6 @@
 Also builds copies of oracle.c with one plausible mistake planted in each and
 checks that at least one pin fails for every copy."""
 
-import os
-import tempfile
-
 import pytest
 
 import oracle

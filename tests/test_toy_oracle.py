@@ -13,7 +13,6 @@ import math
 from fractions import Fraction
 
 import numpy as np
-import pytest
 
 import oracle
 from oracle import accept as acc
