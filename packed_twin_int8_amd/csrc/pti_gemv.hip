@@ -928,15 +928,6 @@ __global__ __launch_bounds__(64 * BW) void gemv_ssq_split_kernel(SplitArgs sa)
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
     };
 
-    // The first step's weights are requested before x, so the two latencies
-    // overlap.
-    Unit bufs[2][T];
-    {
-        const __amdgpu_buffer_rsrc_t rs0 = rsrc_for(0);
-#pragma unroll
-        for (int tt = 0; tt < T; tt++)
-            load_round(rs0, tt, bufs[0][tt]);
-    }
     // x of this lane's units in rounds q T .. q T + T - 1, every stream (stream
     // s feeds twin A if s is even, twin B if odd), through a resource over the
     // row's units: past the last unit the loads return zero.
@@ -956,6 +947,24 @@ __global__ __launch_bounds__(64 * BW) void gemv_ssq_split_kernel(SplitArgs sa)
             }
         }
     }
+    // The first step's weights (2 loads per round), then a wait for x alone:
+    // the loop is entered with exactly the loads of one step in flight, the
+    // same as on every later iteration.  (Entered with x still in flight, the
+    // loop's first step would wait for every load on each iteration.)
+    Unit bufs[2][T];
+    {
+        // in the loop's order (scale, then slots, round by round), so the
+        // loop's waits hold on entry as on every later iteration
+        const __amdgpu_buffer_rsrc_t rs0 = rsrc_for(0);
+#pragma unroll
+        for (int tt = 0; tt < T; tt++) {
+            __builtin_amdgcn_sched_barrier(0);
+            load_round(rs0, tt, bufs[0][tt]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    static_assert(2 * T < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * T));  // vmcnt(2T), other counters untouched
     // Windows of S steps (S even, so step t always uses buffer t mod 2); the
     // last window is rounded up to an even count so the loop has a single
     // exit: an extra step falls past the workgroup's rows, loads through an
