@@ -707,7 +707,10 @@ int launch(const GemvArgs &a0, hipStream_t stream)
         pti::set_hip_error(hipGetLastError());
         return PTI_ERR_HIP;
     }
-    const int64_t grid = std::min<int64_t>(cus, (a.rows + kWaves - 1) / kWaves);
+    // Every CU, whatever the row count: with few rows per SIMD the loop is
+    // VALU-bound (four streams), so spreading the rows over more SIMDs is what
+    // shortens it; a workgroup without rows only stages x.
+    const int64_t grid = std::min<int64_t>(cus, a.rows);
     auto kern = gemv_kernel<FMT, NSP, NS, R, ROWS4, kWaves, cfg.prefetch>;
     // The dynamic-LDS limit is a per-device attribute of the kernel: set it once on each device this
     // instance runs on (one bit per device; two threads racing both set it, which is harmless).
