@@ -517,13 +517,16 @@ struct Wave {
             issue(bufs[k]);
     }
 
-    // One step: issue the loads kD steps ahead, then compute this one.
+    // One step: issue the loads kD steps ahead, then compute this one (a
+    // padding step past the segment's last issues its empty loads and skips
+    // the arithmetic).
     template <int K>
-    __device__ __forceinline__ void step()
+    __device__ __forceinline__ void step(int index)
     {
         issue(bufs[(K + kD) % (kD + 1)]);
         __builtin_amdgcn_sched_barrier(0);
-        compute(bufs[K]);
+        if (index < nsteps)  // wave-uniform
+            compute(bufs[K]);
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -544,7 +547,7 @@ struct Wave {
             const int iters = (nsteps + kD) / (kD + 1);
             for (int it = 0; it < iters; it++) {
                 [&]<int... K>(std::integer_sequence<int, K...>) {
-                    (step<K>(), ...);
+                    (step<K>(it * (kD + 1) + K), ...);
                 }(std::make_integer_sequence<int, kD + 1>{});
             }
         } else {
