@@ -2,12 +2,14 @@
 // streams per twin), the Q8 multi-stream GEMV, their grouped forms, and the
 // SSQ GEMV fused with the greedy verify.
 //
-// Kernels.  The per-wave-row kernel below (gemv_kernel) serves Q8 at every
-// stream count and SSQ rows of more than 40 rounds; the row-split kernel
-// further down (gemv_ssq_split_kernel) serves the other SSQ shapes, and with
-// VERIFY also keeps each workgroup's largest output per twin, which
-// verify_keys_kernel then reduces.  Each format's choice depends on the shape
-// alone, never on the stream count.  Both kernels read rows through a segment
+// Kernels.  The per-wave-row kernel below (gemv_kernel) serves Q8 matrices
+// of more than 8192 rows (or of an odd block count, or more than 20 rounds)
+// and SSQ rows of more than 40 rounds; the row-split kernel further down
+// (gemv_ssq_split_kernel) serves the other SSQ shapes, and with VERIFY also
+// keeps each workgroup's largest output per twin, which verify_keys_kernel
+// then reduces; its Q8 form (gemv_q8_split_kernel) serves the other Q8
+// shapes.  Each format's choice depends on the shape alone, never on the
+// stream count.  Both kernels read rows through a segment
 // table (one matrix, or several with the same column count stacked into one
 // row space) and can add a residual to the rows they store.
 //
@@ -1125,11 +1127,212 @@ int launch_ssq_split(const GemvArgs &a, const VerifyOut *vo, hipStream_t stream)
     }
 }
 
+// Q8 form of the row-split kernel, for rows of an even number of blocks (so
+// every row starts on a dword) and at most kQ8SplitMaxQ waves per row.  The
+// same geometry as the SSQ kernel -- workgroup g owns rows g, g + G, ...;
+// the Q waves of a row each take T consecutive rounds; loads run one step
+// ahead, round by round -- with Q8 units: 16 columns per lane, two lanes per
+// 34-byte block, the quants realigned with v_alignbyte.  Each of the NS
+// streams (up to four) keeps its x slice in registers (80 per stream at
+// T = 5), which a bound of four waves per workgroup leaves room for.  A
+// stream's chain (16 products in column order per unit, scaled into the
+// lane's sum per round, the DPP tree, the Q partials in slice order) is the
+// same whatever NS is.
+constexpr int kQ8SplitMaxQ = 4;
+constexpr int64_t kQ8SplitMaxRows = 8192;
+
+template <int T, int NS>
+__global__ __launch_bounds__(64 * 4) void gemv_q8_split_kernel(SplitArgs sa)
+{
+    constexpr int UC = unit_cols<kQ8>();
+    const GemvArgs &a = sa.g;
+    const int P = sa.P, Q = sa.Q, S = sa.S;
+    extern __shared__ float part[];  // [2][S * P][Q][NS]: row partials, double-buffered
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int p = wv / Q, q = wv - (wv / Q) * Q;
+    const int64_t G = gridDim.x, g = blockIdx.x;
+    const int64_t wg_rows = g < a.rows ? (a.rows - g + G - 1) / G : 0;
+    const int steps = (int)((wg_rows + P - 1) / P);
+
+    float xv[T][UC][NS];  // this lane's x (filled below)
+    const LaneOffsets lo = lane_offsets(lane);
+    const int soff = q * T * (int)kRoundBytes;
+    auto rsrc_for = [&](int t) {
+        const int64_t m = (int64_t)t * P + p;
+        const bool in = m < wg_rows;
+        const int n = in ? (int)a.row_bytes : 0;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(row_addr(a, in ? g + m * G : 0)), (short)0, n,
+                                                 0x00020000);
+    };
+    // Loads of round tt: the scale's dword, the 16 quants (4 + 1 dwords).
+    auto load_round = [&](__amdgpu_buffer_rsrc_t rs, int tt, Unit &u) {
+        const int so = soff + tt * (int)kRoundBytes;
+        u.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.q_sc[0], so, 0);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lo.q_d[0], so, 0);
+        u.d[0] = v.x, u.d[1] = v.y, u.d[2] = v.z, u.d[3] = v.w;
+        u.d[4] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.q_h[0], so, 0);
+    };
+
+    auto step = [&](int t, int half, int local, const Unit (&ut)[T], Unit (&nxt)[T]) {
+        const __amdgpu_buffer_rsrc_t rs_next = rsrc_for(t + 1);
+        float acc[NS];
+#pragma unroll
+        for (int tt = 0; tt < T; tt++) {
+            const Unit &u = ut[tt];
+            uint32_t qd[4];
+#pragma unroll
+            for (int k = 0; k < 4; k++)
+                qd[k] = __builtin_amdgcn_alignbyte(u.d[k + 1], u.d[k], lo.q_sh[0]);
+            float bs[NS];
+#pragma unroll
+            for (int c = 0; c < UC; c++) {
+                const float wq = sbyte(qd[c >> 2], c & 3);
+#pragma unroll
+                for (int s = 0; s < NS; s++)
+                    bs[s] = c == 0 ? wq * xv[tt][c][s] : __builtin_fmaf(wq, xv[tt][c][s], bs[s]);
+            }
+            const float d = f16_lo(u.sc >> lo.q_ssh[0]);
+#pragma unroll
+            for (int s = 0; s < NS; s++)
+                acc[s] = tt == 0 ? d * bs[s] : __builtin_fmaf(d, bs[s], acc[s]);
+            __builtin_amdgcn_sched_barrier(0);
+            load_round(rs_next, tt, nxt[tt]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int slot = (half * S + local) * P + p;
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+            const float v = wave_sum(acc[s]);
+            if (lane == 63 && t < steps)
+                part[(slot * Q + q) * NS + s] = v;
+        }
+    };
+
+    auto flush = [&](int t0, int t1, int half) {
+        __syncthreads();
+        const int n = (t1 - t0) * P;
+#pragma unroll
+        for (int s = 0; s < NS; s++)
+            for (int r = tid; r < n; r += 64 * P * Q) {
+                const int64_t m = (int64_t)t0 * P + r;
+                if (m >= wg_rows)
+                    continue;
+                const int slot = half * S * P + r;
+                float acc = part[(slot * Q) * NS + s];
+                for (int j = 1; j < Q; j++)
+                    acc += part[((slot * Q) + j) * NS + s];
+                if (a.res[s])
+                    acc = a.res[s][g + m * G] + acc;
+                a.y[s][g + m * G] = acc;
+            }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): see the SSQ kernel
+    };
+
+    // x first, then the first step's weights in the loop's order, then a wait
+    // for x alone, so the loop is entered as every iteration ends.
+#pragma unroll
+    for (int s = 0; s < NS; s++) {
+        const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(a.x[s]), (short)0, (int)(a.units * UC * 4), 0x00020000);
+#pragma unroll
+        for (int tt = 0; tt < T; tt++) {
+            const int unit = (q * T + tt) * 64 + lane;
+#pragma unroll
+            for (int k = 0; k < UC / 4; k++) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xrs, (unit * UC + 4 * k) * 4, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    xv[tt][4 * k + e][s] = __builtin_bit_cast(float, (uint32_t)v[e]);
+            }
+        }
+    }
+    Unit bufs[2][T];
+    {
+        const __amdgpu_buffer_rsrc_t rs0 = rsrc_for(0);
+#pragma unroll
+        for (int tt = 0; tt < T; tt++) {
+            __builtin_amdgcn_sched_barrier(0);
+            load_round(rs0, tt, bufs[0][tt]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    static_assert(3 * T < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * T));  // vmcnt(3T)
+
+    int half = 0;
+    for (int t0 = 0; t0 < steps; t0 += S, half ^= 1) {
+        const int t1 = t0 + S < steps ? t0 + S : steps;
+        const int iters = (t1 - t0 + 1) / 2;
+        for (int it = 0; it < iters; it++) {
+            const int local = 2 * it, tb = t0 + local;
+            step(tb, half, local, bufs[0], bufs[1]);
+            step(tb + 1, half, local + 1, bufs[1], bufs[0]);
+        }
+        flush(t0, t1, half);
+    }
+}
+
+template <int T, int NS>
+int launch_q8_split(const GemvArgs &a, hipStream_t stream)
+{
+    SplitArgs sa{};
+    sa.Q = (a.rounds + T - 1) / T;
+    if (sa.Q > kQ8SplitMaxQ)
+        return kNotSplit;
+    sa.P = std::max(1, 4 / sa.Q);
+    int S = 64;
+    while (S > 2 && 2 * S * sa.P * sa.Q * NS * 4 > 32 * 1024)
+        S -= 2;
+    sa.S = S;
+    sa.g = a;
+    const int cus = device_cus();
+    if (cus <= 0) {
+        pti::set_hip_error(hipGetLastError());
+        return PTI_ERR_HIP;
+    }
+    const int64_t grid = std::min<int64_t>(std::min(cus, kSplitMaxGrid), a.rows);
+    const size_t lds = (size_t)2 * sa.S * sa.P * sa.Q * NS * sizeof(float);
+    hipLaunchKernelGGL((gemv_q8_split_kernel<T, NS>), dim3((unsigned)grid), dim3((unsigned)(64 * sa.P * sa.Q)), lds,
+                       stream, sa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        pti::set_hip_error(e);
+        return PTI_ERR_HIP;
+    }
+    return PTI_OK;
+}
+
+template <int NS>
+int launch_q8_split(const GemvArgs &a, hipStream_t stream)
+{
+    switch (split_T(a.rounds)) {
+    case 1: return launch_q8_split<1, NS>(a, stream);
+    case 2: return launch_q8_split<2, NS>(a, stream);
+    case 3: return launch_q8_split<3, NS>(a, stream);
+    case 4: return launch_q8_split<4, NS>(a, stream);
+    default: return launch_q8_split<5, NS>(a, stream);
+    }
+}
+
 // Kernel choice of each format: by shape alone, never by the stream count.
 int launch_q8(const GemvArgs &a, int n_streams, hipStream_t st)
 {
     // rows start on dword boundaries when a row holds an even number of blocks
     if ((a.cols / PTI_BLOCK) % 2 == 0) {
+        int rc = kNotSplit;
+        // the row-split form for matrices of up to kQ8SplitMaxRows rows; the
+        // per-wave-row kernel, whose many waves hide more latency, for taller
+        // ones (measured: it is faster there at four streams)
+        if (a.rows <= kQ8SplitMaxRows)
+            switch (n_streams) {
+            case 1: rc = launch_q8_split<1>(a, st); break;
+            case 2: rc = launch_q8_split<2>(a, st); break;
+            case 3: rc = launch_q8_split<3>(a, st); break;
+            default: rc = launch_q8_split<4>(a, st); break;
+            }
+        if (rc != kNotSplit)
+            return rc;
         switch (n_streams) {
         case 1: return launch<kQ8, 1, 1, true>(a, st);
         case 2: return launch<kQ8, 2, 2, true>(a, st);

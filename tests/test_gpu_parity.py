@@ -131,6 +131,8 @@ SHAPES = [
     (65, 5120),
     (64, 5632),
     (40, 17408),  # x split into several LDS chunks at 4 streams
+    (8192, 1024),  # the largest row count of the Q8 row-split form
+    (8193, 1024),  # the smallest above it (per-wave-row kernel)
 ]
 
 
@@ -166,7 +168,10 @@ def test_ssq_vs_oracle_and_split(env, rows, cols):
     assert np.all(np.abs(yb.astype(np.float64) - qb[0]) <= 2 * TOL * tb)
 
 
-@pytest.mark.parametrize("rows,cols", [(129, 1056), (300, 5120)])
+# (129, 1056): odd block count, per-wave-row kernel; (300, 5120), (40, 17408):
+# the row-split form (one and four waves per row); (8193, 1024): above the
+# row-split form's row limit
+@pytest.mark.parametrize("rows,cols", [(129, 1056), (300, 5120), (40, 17408), (8193, 1024)])
 def test_stream_slot_invariance(env, rows, cols):
     d = synth.q8(rows, cols, 4, seed=33)
     single = [run_q8(env, d["Q"], d["S"], d["X"][s:s + 1])[0] for s in range(4)]
