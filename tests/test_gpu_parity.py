@@ -133,6 +133,10 @@ SHAPES = [
     (40, 17408),  # x split into several LDS chunks at 4 streams
     (8192, 1024),  # the largest row count of the Q8 row-split form
     (8193, 1024),  # the smallest above it (per-wave-row kernel)
+    (1, 64),       # two blocks, one row: four of 64 lanes hold weights
+    (2, 1088),     # 34 blocks: two rounds, ragged
+    (5, 20480),    # Q8: 20 rounds, the most the row-split form takes; SSQ: 40
+    (5, 20544),    # one round more (per-wave-row kernel for both formats)
 ]
 
 
