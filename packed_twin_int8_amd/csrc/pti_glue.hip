@@ -372,6 +372,22 @@ __global__ void accept_kernel(const int32_t *__restrict__ tokens_in, const int32
     }
 }
 
+// A pass's inputs written from kernel arguments: the tokens, and the
+// uniforms when sampling (no host-to-device copy on the decode loop's path).
+struct PassInputs {
+    int32_t tok[PTI_MAX_STREAMS];
+    double uni[PTI_MAX_STREAMS];
+};
+
+__global__ void set_inputs_kernel(PassInputs in, int32_t *tok, int n_tok, double *uni, int n_uni)
+{
+    const int i = threadIdx.x;
+    if (i < n_tok)
+        tok[i] = in.tok[i];
+    if (uni && i < n_uni)
+        uni[i] = in.uni[i];
+}
+
 int64_t sv_parts(int64_t vocab) { return (vocab + kSvPart - 1) / kSvPart; }
 
 int launch_status()
@@ -481,6 +497,19 @@ int launch_silu_mul_rows(const float *gu, float *y, int64_t rows, int64_t cols, 
 {
     hipLaunchKernelGGL(silu_mul_rows_kernel, dim3(elementwise_grid(rows * cols)), dim3(256), 0,
                        static_cast<hipStream_t>(stream), gu, y, rows, cols);
+    return launch_status();
+}
+
+int launch_set_inputs(int32_t *tok, const int32_t *tok_host, int n_tok, double *uni, const double *uni_host, int n_uni,
+                      void *stream)
+{
+    PassInputs in{};
+    for (int i = 0; i < n_tok; i++)
+        in.tok[i] = tok_host[i];
+    for (int i = 0; uni_host && i < n_uni; i++)
+        in.uni[i] = uni_host[i];
+    hipLaunchKernelGGL(set_inputs_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), in, tok, n_tok,
+                       uni_host ? uni : nullptr, n_uni);
     return launch_status();
 }
 }  // namespace pti

@@ -48,6 +48,12 @@ int gemv_ssq_res(const void *w, const float *x_a, const float *x_b, float *y_a, 
 // computes it.  Arguments already validated.
 int launch_silu_mul_rows(const float *gu, float *y, int64_t rows, int64_t cols, void *stream);
 
+// tok[i] = tok_host[i] (i < n_tok) and, when uni_host is set, uni[i] =
+// uni_host[i] (i < n_uni), written on the device from kernel arguments (one
+// launch, no host-to-device copy).  n_tok, n_uni <= PTI_MAX_STREAMS.
+int launch_set_inputs(int32_t *tok, const int32_t *tok_host, int n_tok, double *uni, const double *uni_host, int n_uni,
+                      void *stream);
+
 inline bool overlap(Range a, Range b)
 {
     if (a.n == 0 || b.n == 0)

@@ -50,8 +50,8 @@ Layout layout(const pti_toy_model &m, int n)
     L.x = take(N * size_t(m.ffn) * 4);
     L.logits = take(N * size_t(m.vocab) * 4);
     L.tok = take(PTI_MAX_STREAMS * 4);
-    L.out = take(PTI_MAX_STREAMS * 4);
-    L.acc = take(4);
+    L.out = take(PTI_MAX_STREAMS * 4 + 4);  // the drawn tokens, then the accept count: read back in one copy
+    L.acc = L.out + PTI_MAX_STREAMS * 4;
     L.uni = take(PTI_MAX_STREAMS * 8);
     L.sv = take(pti_sample_verify_workspace_bytes(m.vocab, n));  // the sampled verify's part sums
     L.total = off;
@@ -181,29 +181,42 @@ struct Decoder {
     // Draws n tokens from logits rows [row0, row0 + n) with the uniforms of
     // slots slot0 ...; the accept count compares them with the pass inputs
     // already in dev_tok() (read only when n >= 2, i.e. for row0 == 0).
-    int draw(int row0, int n, int step, int slot0, int32_t *out, int32_t *accept)
+    // The pass's inputs: tokens x[0..nx-1] and, when sampling, the uniforms of
+    // the n draws of slots slot0 ..., written by one small kernel.
+    int set_inputs(const int32_t *x, int nx, int step, int slot0, int n)
+    {
+        const double *u = temp == 0.0 ? nullptr : uniforms + (size_t(step) * 2 * N + size_t(slot0));
+        return pti::launch_set_inputs(dev_tok(), x, nx, dev_uni(), u, n, st);
+    }
+
+    // Draws n tokens from logits rows [row0, row0 + n) with the uniforms set
+    // for the pass; the accept count compares them with the pass inputs in
+    // dev_tok() (read only when n >= 2, i.e. for row0 == 0).  The draws and
+    // the accept count come back in one copy.
+    int draw(int row0, int n, int32_t *out, int32_t *accept)
     {
         void *s = st;
         const float *lg = dev_logits() + int64_t(row0) * m.vocab;
-        if (temp == 0.0) {
+        if (temp == 0.0)
             PTI_TRY(pti_verify_argmax(lg, dev_tok(), dev_out(), dev_acc(), m.vocab, n, s));
-        } else {
-            const double *u = uniforms + (size_t(step) * 2 * N + size_t(slot0));
-            PTI_TRY(hip_status(hipMemcpyAsync(dev_uni(), u, size_t(n) * 8, hipMemcpyHostToDevice, st)));
+        else
             PTI_TRY(pti_sample_verify(lg, dev_tok(), dev_uni(), temp, dev_out(), dev_acc(), m.vocab, n, work + L.sv,
                                       pti_sample_verify_workspace_bytes(m.vocab, n), s));
-        }
-        PTI_TRY(hip_status(hipMemcpyAsync(out, dev_out(), size_t(n) * 4, hipMemcpyDeviceToHost, st)));
-        PTI_TRY(hip_status(hipMemcpyAsync(accept, dev_acc(), 4, hipMemcpyDeviceToHost, st)));
-        return hip_status(hipStreamSynchronize(st));
+        int32_t back[PTI_MAX_STREAMS + 1];
+        PTI_TRY(hip_status(hipMemcpyAsync(back, dev_out(), sizeof(back), hipMemcpyDeviceToHost, st)));
+        PTI_TRY(hip_status(hipStreamSynchronize(st)));
+        for (int i = 0; i < n; i++)
+            out[i] = back[i];
+        *accept = back[PTI_MAX_STREAMS];
+        return PTI_OK;
     }
 
     // One pass of every stream on inputs x[0..N-1]: outputs o[], accept count.
     int multi(int step, const int32_t *x, int32_t *o, int32_t *a)
     {
-        PTI_TRY(hip_status(hipMemcpyAsync(dev_tok(), x, size_t(N) * 4, hipMemcpyHostToDevice, st)));
+        PTI_TRY(set_inputs(x, N, step, 0, N));
         PTI_TRY(forward(m, L, work, dev_tok(), dev_logits(), npass, st));
-        PTI_TRY(draw(0, N, step, 0, o, a));
+        PTI_TRY(draw(0, N, o, a));
         for (int s = 0; s < N; s++)
             record(step, s, s, x[s], o[s]);
         return PTI_OK;
@@ -217,10 +230,10 @@ struct Decoder {
         const int32_t in[2] = {t, t};
         const int n = m.format == PTI_FMT_SSQ ? 2 : 1;
         int32_t a;
-        PTI_TRY(hip_status(hipMemcpyAsync(dev_tok(), in, size_t(n) * 4, hipMemcpyHostToDevice, st)));
+        PTI_TRY(set_inputs(in, n, step, slot, 1));
         PTI_TRY(forward(m, L, work, dev_tok(), dev_logits(), n, st));
         const int row = (m.format == PTI_FMT_SSQ && stream >= 1) ? 1 : 0;
-        PTI_TRY(draw(row, 1, step, slot, o, &a));
+        PTI_TRY(draw(row, 1, o, &a));
         record(step, slot, stream, t, *o);
         return PTI_OK;
     }
