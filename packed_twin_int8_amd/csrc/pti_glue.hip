@@ -126,6 +126,52 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const float *__re
         ys[c] = float(double(xs[c]) / r);
 }
 
+// The same arithmetic in the same order for dim <= PER * kNormThreads, with
+// the thread's elements read once, all loads in flight together, and kept in
+// registers for the second pass (a loop with one dependent load per element
+// pays the memory latency once per element).
+template <int PER>
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_reg_kernel(const float *__restrict__ x,
+                                                                   float *__restrict__ y, int64_t dim, double eps)
+{
+    __shared__ double part[kNormThreads / 64];
+    __shared__ double root;
+    const int tid = threadIdx.x;
+    const float *xs = x + blockIdx.x * dim;
+    float *ys = y + blockIdx.x * dim;
+    float v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int64_t c = tid + (int64_t)i * kNormThreads;
+        v[i] = c < dim ? xs[c] : 0.f;
+    }
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 0; i < PER; i++)
+        if (tid + (int64_t)i * kNormThreads < dim) {
+            const double d = v[i];
+            acc += d * d;
+        }
+    acc = wave_sum_f64(acc);
+    if ((tid & 63) == 0)
+        part[tid >> 6] = acc;
+    __syncthreads();
+    if (tid == 0) {
+        double ss = 0.0;
+        for (int i = 0; i < kNormThreads / 64; i++)
+            ss += part[i];
+        root = sqrt(ss / double(dim) + eps);
+    }
+    __syncthreads();
+    const double r = root;
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int64_t c = tid + (int64_t)i * kNormThreads;
+        if (c < dim)
+            ys[c] = float(double(v[i]) / r);
+    }
+}
+
 // ------------------------------------------------------------------ elementwise
 
 __global__ void silu_mul_kernel(const float *g, const float *u, float *y, int64_t n)
@@ -137,14 +183,15 @@ __global__ void silu_mul_kernel(const float *g, const float *u, float *y, int64_
 }
 
 // The same arithmetic on the rows of a stacked gate|up output: g = gu[s][j],
-// u = gu[s][cols + j].
-__global__ void silu_mul_rows_kernel(const float *gu, float *y, int64_t rows, int64_t cols)
+// u = gu[s][cols + j].  Row s = blockIdx.y.
+__global__ void silu_mul_rows_kernel(const float *gu, float *y, int64_t cols)
 {
-    const int64_t n = rows * cols;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t s = i / cols, j = i - s * cols;
-        const double gv = gu[s * 2 * cols + j];
-        y[i] = float(gv / (1.0 + exp(-gv)) * double(gu[s * 2 * cols + cols + j]));
+    const int64_t s = blockIdx.y;
+    const float *g = gu + s * 2 * cols, *u = g + cols;
+    float *ys = y + s * cols;
+    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < cols; j += (int64_t)gridDim.x * blockDim.x) {
+        const double gv = g[j];
+        ys[j] = float(gv / (1.0 + exp(-gv)) * double(u[j]));
     }
 }
 
@@ -457,8 +504,14 @@ extern "C" int pti_rmsnorm(const float *x, float *y, int64_t dim, int n_streams,
     const size_t bytes = size_t(n_streams) * size_t(dim) * 4;
     if (x != y && pti::overlap({x, bytes}, {y, bytes}))
         return PTI_ERR_OVERLAP;
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)n_streams), dim3(kNormThreads), 0,
-                       static_cast<hipStream_t>(stream), x, y, dim, double(eps));
+    const dim3 grid((unsigned)n_streams), block(kNormThreads);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dim <= 8 * kNormThreads)
+        hipLaunchKernelGGL(rmsnorm_reg_kernel<8>, grid, block, 0, st, x, y, dim, double(eps));
+    else if (dim <= 32 * kNormThreads)
+        hipLaunchKernelGGL(rmsnorm_reg_kernel<32>, grid, block, 0, st, x, y, dim, double(eps));
+    else
+        hipLaunchKernelGGL(rmsnorm_kernel, grid, block, 0, st, x, y, dim, double(eps));
     return launch_status();
 }
 
@@ -495,8 +548,8 @@ extern "C" int pti_silu_mul(const float *g, const float *u, float *y, int64_t n,
 namespace pti {
 int launch_silu_mul_rows(const float *gu, float *y, int64_t rows, int64_t cols, void *stream)
 {
-    hipLaunchKernelGGL(silu_mul_rows_kernel, dim3(elementwise_grid(rows * cols)), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), gu, y, rows, cols);
+    hipLaunchKernelGGL(silu_mul_rows_kernel, dim3(elementwise_grid(cols), (unsigned)rows), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), gu, y, cols);
     return launch_status();
 }
 
