@@ -273,7 +273,9 @@ int pti_embed_ssq(const void *w_ssq, const int32_t *tokens, float *x, int64_t vo
 
 /* y[n][c] = x[n][c] / sqrt(mean_c x[n][c]^2 + eps) (no gain), for
  * n < n_streams; x, y: device fp32 [n_streams][dim]; y may equal x (in place)
- * but not overlap it otherwise; eps finite, >= 0; 1 <= dim <= PTI_MAX_ELEMS. */
+ * but not overlap it otherwise; eps finite, >= 0; 1 <= dim <= PTI_MAX_ELEMS.
+ * Sums in fp64, then x times the fp64 reciprocal of the root: each output is
+ * within one fp32 ulp of the formula. */
 int pti_rmsnorm(const float *x, float *y, int64_t dim, int n_streams, float eps, void *stream);
 
 /* y[i] = g[i] / (1 + exp(-g[i])) * u[i] (SiLU gate times up projection), i < n.

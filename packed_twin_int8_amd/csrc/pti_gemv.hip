@@ -67,6 +67,7 @@
 #include <utility>
 
 #include "pti_internal.h"
+#include "pti_norm.h"
 
 // Per-wave-row kernel geometry by format and stream count: waves per
 // workgroup (a multiple of 4), steps of loads in flight, rows per wave.  None
@@ -91,6 +92,11 @@
 
 
 namespace {
+
+// LDS of the per-wave-row kernel: x (dynamic, at most kXLds bytes) and the
+// fused norm's partial sums (static, within the rest of the CU's budget).
+constexpr int kNormLds = 256;
+constexpr int kXLds = PTI_LDS_BUDGET - kNormLds;
 
 constexpr uint32_t kRoundBytes = 1088;  // bytes of a row one round of 64 lanes covers (both formats)
 
@@ -118,6 +124,8 @@ struct GemvArgs {
     int32_t units;         // units per row
     int32_t rounds;        // ceil(units / 64)
     int32_t chunk_rounds;  // rounds of x held in LDS at once
+    int32_t norm;          // per-wave-row kernel, x staged at once: x[s] <- rmsnorm(x[s]) as it is staged
+    double norm_eps;
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -241,6 +249,81 @@ __device__ __forceinline__ void stage_store(float4 *xs, int item0, const float4 
             base[p * 64] = make_float4(o[0], o[1], o[2], o[3]);
         }
     }
+}
+
+// Element (column c, stream s) of x in the LDS layout above (all of x staged).
+template <int UC, int NSP>
+__device__ __forceinline__ float *staged_elem(float4 *xs, int c, int s)
+{
+    constexpr int CG = UC / 4;
+    const int rd = c / (64 * UC), l = (c / UC) % 64, cg = (c % UC) / 4, f = (c % 4) * NSP + s;
+    return reinterpret_cast<float *>(xs + ((rd * CG + cg) * NSP + f / 4) * 64 + l) + f % 4;
+}
+
+// x[s] <- rmsnorm(x[s]) in LDS after all of x was staged and a barrier: the
+// sum of squares by the first 256 threads in pti_rmsnorm's order (so the
+// result has the same bits), then every thread scales the elements of the
+// items it staged.  Ends with a barrier.
+template <int UC, int NSP, int NS, int BATCH, int THREADS>
+__device__ __forceinline__ void norm_staged(const GemvArgs &a, float4 *xs, int tid, int nitems)
+{
+    static_assert(THREADS >= pti_norm::kGroup, "the sum of squares takes 256 threads");
+    __shared__ double part[NS][pti_norm::kGroup / 64];
+    static_assert(sizeof(part) <= kNormLds, "the norm's LDS");
+    if (tid < pti_norm::kGroup) {
+        // B elements of every stream read at once (4 at three or four
+        // streams: 8 would spill), then summed in order
+        constexpr int B = NS >= 3 ? 4 : 8, G = pti_norm::kGroup;
+        double acc[NS];
+#pragma unroll
+        for (int s = 0; s < NS; s++)
+            acc[s] = 0.0;
+        for (int c0 = tid; c0 < a.cols; c0 += B * G) {
+            float v[NS][B];
+#pragma unroll
+            for (int k = 0; k < B; k++)
+#pragma unroll
+                for (int s = 0; s < NS; s++)
+                    v[s][k] = c0 + k * G < a.cols ? *staged_elem<UC, NSP>(xs, c0 + k * G, s) : 0.f;
+#pragma unroll
+            for (int k = 0; k < B; k++)
+                if (c0 + k * G < a.cols)
+#pragma unroll
+                    for (int s = 0; s < NS; s++)
+                        acc[s] = pti_norm::sq_acc(acc[s], v[s][k]);
+        }
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+            const double t = pti_norm::wave_sum_f64(acc[s]);
+            if ((tid & 63) == 0)
+                part[s][tid >> 6] = t;
+        }
+    }
+    __syncthreads();
+    double r[NS];
+#pragma unroll
+    for (int s = 0; s < NS; s++)
+        r[s] = pti_norm::inv_root(part[s], a.cols, a.norm_eps);
+    constexpr int CG = UC / 4;
+#pragma unroll
+    for (int i = 0; i < BATCH; i++) {
+        const int it = i * THREADS + tid;
+        if (it >= nitems)
+            break;
+        const int l = it & 63, cg = (it >> 6) % CG, rd = (it >> 6) / CG;
+        float4 *base = xs + ((rd * CG + cg) * NSP) * 64 + l;
+#pragma unroll
+        for (int p = 0; p < NSP; p++) {
+            float *e = reinterpret_cast<float *>(base + p * 64);
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int st = (4 * p + q) % NSP;
+                if (st < NS)
+                    e[q] = pti_norm::apply(e[q], r[st]);
+            }
+        }
+    }
+    __syncthreads();
 }
 
 // Stage rounds [r0, r0 + nr) of x into LDS rounds 0..nr-1 (nr at most the
@@ -603,7 +686,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemvArgs a)
     // budget holds, so a chunk is staged in one straight-line batch (no loop
     // between the first weight loads and the main loop, which keeps the
     // compiler's count of loads in flight exact).
-    constexpr int kMaxChunkItems = (PTI_LDS_BUDGET / (64 * UC * NSP * 4)) * 64 * (UC / 4);
+    constexpr int kMaxChunkItems = (kXLds / (64 * UC * NSP * 4)) * 64 * (UC / 4);
     constexpr int BATCH = (kMaxChunkItems + kThreads - 1) / kThreads;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -632,6 +715,8 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemvArgs a)
         __builtin_amdgcn_sched_barrier(0);
         stage_store<UC, NSP, BATCH, kThreads>(xs, 0, v, tid, nitems);
         __syncthreads();
+        if (a.norm)  // uniform
+            norm_staged<UC, NSP, NS, BATCH, kThreads>(a, xs, tid, nitems);
         w.begin_group(0);
         w.template loop<true>();
         w.store_group(min(w.npass, w.kGroupPasses));
@@ -705,7 +790,7 @@ int launch(const GemvArgs &a0, hipStream_t stream)
     constexpr int R = cfg.rows, kWaves = cfg.waves, kThreads = 64 * kWaves;
     GemvArgs a = a0;
     const int per_round = 64 * UC * NSP * 4;  // LDS bytes per round of x
-    a.chunk_rounds = max(1, min(a.rounds, PTI_LDS_BUDGET / per_round));
+    a.chunk_rounds = max(1, min(a.rounds, kXLds / per_round));
     const size_t lds = (size_t)a.chunk_rounds * per_round;
     const int cus = device_cus();
     if (cus <= 0) {
@@ -727,7 +812,7 @@ int launch(const GemvArgs &a0, hipStream_t stream)
     }
     if (!(attr_devs.load(std::memory_order_acquire) >> dev & 1)) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, PTI_LDS_BUDGET);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kXLds);
         if (e != hipSuccess) {
             pti::set_hip_error(e);
             return PTI_ERR_HIP;
@@ -1587,6 +1672,35 @@ int gemv_q8_res(const void *w, const float *x, float *y, const float *res, int64
         a.res[s] = res + (size_t)s * rows;
     }
     return launch_q8(a, n, static_cast<hipStream_t>(stream));
+}
+
+int q8_gemv_rmsnorm(const void *const *w, const int64_t *rows, int n_mats, const float *x, float *y, int64_t cols,
+                    int n, float eps, void *stream)
+{
+    GemvArgs a;
+    const int rc = group_args<kQ8>(w, rows, n_mats, cols, nullptr, 0, a);
+    if (rc != PTI_OK)
+        return rc;
+    // the per-wave-row kernel with all of x staged at once, or no fusion
+    const bool even = (a.cols / PTI_BLOCK) % 2 == 0;
+    if (even && a.rows <= kQ8SplitMaxRows && (a.rounds + split_T(a.rounds) - 1) / split_T(a.rounds) <= kQ8SplitMaxQ)
+        return kNormNotFused;
+    const int nsp = n == 1 ? 1 : n == 2 ? 2 : 4;
+    if (a.rounds * 64 * unit_cols<kQ8>() * nsp * 4 > kXLds)
+        return kNormNotFused;
+    for (int s = 0; s < n; s++) {
+        a.x[s] = x + (size_t)s * cols;
+        a.y[s] = y + (size_t)s * a.rows;
+    }
+    a.norm = 1;
+    a.norm_eps = double(eps);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (n) {
+    case 1: return even ? launch<kQ8, 1, 1, true>(a, st) : launch<kQ8, 1, 1, false>(a, st);
+    case 2: return even ? launch<kQ8, 2, 2, true>(a, st) : launch<kQ8, 2, 2, false>(a, st);
+    case 3: return even ? launch<kQ8, 4, 3, true>(a, st) : launch<kQ8, 4, 3, false>(a, st);
+    default: return even ? launch<kQ8, 4, 4, true>(a, st) : launch<kQ8, 4, 4, false>(a, st);
+    }
 }
 
 int gemv_ssq_res(const void *w, const float *x_a, const float *x_b, float *y_a, float *y_b, const float *res_a,

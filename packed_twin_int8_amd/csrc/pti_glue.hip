@@ -13,7 +13,9 @@
 // at the end: the cost is invisible at these sizes and each output is then the
 // correctly rounded value of its formula up to the last fp64 ulp.
 //   * embed: dequantise one matrix row per stream (scale * q is exact in fp32).
-//   * rmsnorm: y = x / sqrt(mean(x^2) + eps), one workgroup per stream.
+//   * rmsnorm: y = x / sqrt(mean(x^2) + eps), one workgroup per stream; x is
+//     multiplied by the fp64 reciprocal of the root, so y is within one fp32
+//     ulp of the formula (the GEMV that fuses the norm gives the same bits).
 //   * silu_mul: y = g / (1 + exp(-g)) * u, elementwise.
 //   * add: y = a + b in fp32, elementwise.
 //   * sample_verify: per stream, weights w_j = exp((l_j - max) / t) in fp64 and
@@ -25,6 +27,7 @@
 #include <cmath>
 
 #include "pti_internal.h"
+#include "pti_norm.h"
 
 namespace {
 
@@ -77,14 +80,6 @@ __global__ void embed_ssq_kernel(const uint8_t *__restrict__ w, const int32_t *_
 
 // ------------------------------------------------------------------ reductions
 
-__device__ __forceinline__ double wave_sum_f64(double v)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v += __shfl_xor(v, off, 64);
-    return v;
-}
-
 __device__ __forceinline__ float wave_max_f32(float v)
 {
 #pragma unroll
@@ -95,35 +90,29 @@ __device__ __forceinline__ float wave_max_f32(float v)
 
 // ------------------------------------------------------------------ rmsnorm
 
-constexpr int kNormThreads = 256;
+constexpr int kNormThreads = pti_norm::kGroup;
 
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const float *__restrict__ x, float *__restrict__ y,
                                                                int64_t dim, double eps)
 {
     __shared__ double part[kNormThreads / 64];
-    __shared__ double root;
+    __shared__ double root;  // 1 / the root
     const int tid = threadIdx.x;
     const float *xs = x + blockIdx.x * dim;
     float *ys = y + blockIdx.x * dim;
     double acc = 0.0;
-    for (int64_t c = tid; c < dim; c += kNormThreads) {
-        const double v = xs[c];
-        acc += v * v;
-    }
-    acc = wave_sum_f64(acc);
+    for (int64_t c = tid; c < dim; c += kNormThreads)
+        acc = pti_norm::sq_acc(acc, xs[c]);
+    acc = pti_norm::wave_sum_f64(acc);
     if ((tid & 63) == 0)
         part[tid >> 6] = acc;
     __syncthreads();
-    if (tid == 0) {
-        double ss = 0.0;
-        for (int i = 0; i < kNormThreads / 64; i++)
-            ss += part[i];
-        root = sqrt(ss / double(dim) + eps);
-    }
+    if (tid == 0)
+        root = pti_norm::inv_root(part, dim, eps);
     __syncthreads();
     const double r = root;
     for (int64_t c = tid; c < dim; c += kNormThreads)
-        ys[c] = float(double(xs[c]) / r);
+        ys[c] = pti_norm::apply(xs[c], r);
 }
 
 // The same arithmetic in the same order for dim <= PER * kNormThreads, with
@@ -135,7 +124,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_reg_kernel(const float *
                                                                    float *__restrict__ y, int64_t dim, double eps)
 {
     __shared__ double part[kNormThreads / 64];
-    __shared__ double root;
+    __shared__ double root;  // 1 / the root
     const int tid = threadIdx.x;
     const float *xs = x + blockIdx.x * dim;
     float *ys = y + blockIdx.x * dim;
@@ -148,27 +137,21 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_reg_kernel(const float *
     double acc = 0.0;
 #pragma unroll
     for (int i = 0; i < PER; i++)
-        if (tid + (int64_t)i * kNormThreads < dim) {
-            const double d = v[i];
-            acc += d * d;
-        }
-    acc = wave_sum_f64(acc);
+        if (tid + (int64_t)i * kNormThreads < dim)
+            acc = pti_norm::sq_acc(acc, v[i]);
+    acc = pti_norm::wave_sum_f64(acc);
     if ((tid & 63) == 0)
         part[tid >> 6] = acc;
     __syncthreads();
-    if (tid == 0) {
-        double ss = 0.0;
-        for (int i = 0; i < kNormThreads / 64; i++)
-            ss += part[i];
-        root = sqrt(ss / double(dim) + eps);
-    }
+    if (tid == 0)
+        root = pti_norm::inv_root(part, dim, eps);
     __syncthreads();
     const double r = root;
 #pragma unroll
     for (int i = 0; i < PER; i++) {
         const int64_t c = tid + (int64_t)i * kNormThreads;
         if (c < dim)
-            ys[c] = float(double(v[i]) / r);
+            ys[c] = pti_norm::apply(v[i], r);
     }
 }
 
@@ -249,7 +232,7 @@ __global__ __launch_bounds__(kSvThreads) void sv_part_kernel(const float *__rest
     if (m > -__builtin_inff())
         for (int i = tid; i < n; i += kSvThreads)
             acc += exp((double(v[i]) - md) / temperature);
-    acc = wave_sum_f64(acc);
+    acc = pti_norm::wave_sum_f64(acc);
     if (lane == 0)
         wsum[wv] = acc;
     __syncthreads();

@@ -46,6 +46,17 @@ int gemv_ssq_res(const void *w, const float *x_a, const float *x_b, float *y_a, 
 // y[s][j] = silu(gu[s][j]) * gu[s][cols + j] for s < rows, j < cols (rows of
 // 2 cols: the stacked output of a grouped gate|up GEMV), as pti_silu_mul
 // computes it.  Arguments already validated.
+// y[s] = W rmsnorm(x[s]) for the Q8 matrices w[0..n_mats) stacked into one
+// row space (as pti_gemv_q8_multi_grouped stacks them), s < n: the
+// per-wave-row GEMV normalises x while staging it, with the bits pti_rmsnorm
+// gives.  Returns kNormNotFused, launching nothing, when the shape takes the
+// row-split kernel or x does not fit in LDS at once (the caller then runs
+// pti_rmsnorm and the plain GEMV).  Arguments already validated, except that
+// the matrices are checked as a grouped launch checks them.
+constexpr int kNormNotFused = 1;
+int q8_gemv_rmsnorm(const void *const *w, const int64_t *rows, int n_mats, const float *x, float *y, int64_t cols,
+                    int n, float eps, void *stream);
+
 int launch_silu_mul_rows(const float *gu, float *y, int64_t rows, int64_t cols, void *stream);
 
 // tok[i] = tok_host[i] (i < n_tok) and, when uni_host is set, uni[i] =

@@ -125,17 +125,31 @@ int forward(const pti_toy_model &m, const Layout &L, char *work, const int32_t *
         PTI_TRY(pti_embed_q8(m.embed, tokens, h, m.vocab, H, n, stream));
     const int64_t rows2[2] = {F, F};
     for (int l = 0; l < m.n_layers; l++) {
-        PTI_TRY(pti_rmsnorm(h, r, H, n, m.eps, stream));
         const void *gate_up[2] = {m.gate[l], m.up[l]};
-        if (ssq)
-            PTI_TRY(pti_gemv_ssq_grouped(gate_up, rows2, 2, r, r + H, gu, gu + 2 * F, H, stream));
-        else
-            PTI_TRY(pti_gemv_q8_multi_grouped(gate_up, rows2, 2, r, gu, H, n, stream));
+        // Q8: the norm inside the gate|up GEMV's staging where that kernel
+        // takes the shape (same bits as the separate norm)
+        const int fused = ssq ? pti::kNormNotFused : pti::q8_gemv_rmsnorm(gate_up, rows2, 2, h, gu, H, n, m.eps, stream);
+        if (fused != pti::kNormNotFused) {
+            PTI_TRY(fused);
+        } else {
+            PTI_TRY(pti_rmsnorm(h, r, H, n, m.eps, stream));
+            if (ssq)
+                PTI_TRY(pti_gemv_ssq_grouped(gate_up, rows2, 2, r, r + H, gu, gu + 2 * F, H, stream));
+            else
+                PTI_TRY(pti_gemv_q8_multi_grouped(gate_up, rows2, 2, r, gu, H, n, stream));
+        }
         PTI_TRY(pti::launch_silu_mul_rows(gu, x, n, F, stream));
         if (ssq)
             PTI_TRY(pti::gemv_ssq_res(m.down[l], x, x + F, h, h + H, h, h + H, H, F, stream));
         else
             PTI_TRY(pti::gemv_q8_res(m.down[l], x, h, h, H, F, n, stream));
+    }
+    if (!ssq) {
+        const void *head[1] = {m.head};
+        const int64_t vrows[1] = {m.vocab};
+        const int fused = pti::q8_gemv_rmsnorm(head, vrows, 1, h, logits, H, n, m.eps, stream);
+        if (fused != pti::kNormNotFused)
+            return fused;
     }
     PTI_TRY(pti_rmsnorm(h, r, H, n, m.eps, stream));
     return gemv(m, m.head, r, logits, m.vocab, H, n, stream);
