@@ -153,10 +153,13 @@ HIT_KERNELS = {
     "gemv_ssq_split_kernel<5, 2, true, 8>": "step: fused SSQ twin GEMV (+ verify keys)",
     "verify_keys_kernel": "step: verify keys",
     "gemv_ssq_split_kernel<5, 2, false, 8>": "SSQ twin GEMV alone",
-    "gemv_kernel<0, 1, 1, 1, true, 12, 4>": "Q8 GEMV, N = 1",
-    "gemv_kernel<0, 2, 2, 1, true, 12, 4>": "Q8 GEMV, N = 2",
+    "gemv_q8_split_kernel<5, 1>": "Q8 GEMV, N = 1",
+    "gemv_q8_split_kernel<5, 2>": "Q8 GEMV, N = 2",
     "gemv_kernel<0, 4, 4, 2, true, 16, 4>": "Q8 GEMV, N = 4",
 }
+# the Q8 kernel of each stream count at 17408 x 5120 (one and two streams take
+# the row-split kernel there, four the per-wave-row kernel)
+Q8_KERNEL = {1: "gemv_q8_split_kernel<5, 1>", 2: "gemv_q8_split_kernel<5, 2>", 4: "gemv_kernel<0, 4, 4, 2, true, 16, 4>"}
 CALIB_BYTES = 64 * 2**20 * 4  # torch.neg over 64 Mi fp32: reads and writes this many bytes
 
 
@@ -796,7 +799,7 @@ def main():
                 "frac_of_hbm_peak": round(algo / (t[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "gemv_per_s": round(1 / (t[n] * 1e-3), 1),
                 "outputs_per_s": round(n * ROWS / (t[n] * 1e-3), 1),
-                "l2_hit_rate": next((v for k, v in (hr or {}).items() if k.startswith(f"gemv_kernel<0, {n}, ")), None),
+                "l2_hit_rate": (hr or {}).get(Q8_KERNEL[n]),
             }
             log(f"q8 n={n}: {t[n] * 1e3:.2f} us, {Pq.nbytes / (t[n] * 1e-3) / 1e9:.1f} GB/s")
         per_kernel["q8_step_cost_n4_over_n1"] = round(t[4] / t[1], 4)

@@ -8,8 +8,9 @@
 // (gemv_ssq_split_kernel) serves the other SSQ shapes, and with VERIFY also
 // keeps each workgroup's largest output per twin, which verify_keys_kernel
 // then reduces; its Q8 form (gemv_q8_split_kernel) serves the other Q8
-// shapes.  Each format's choice depends on the shape alone, never on the
-// stream count.  Both kernels read rows through a segment
+// shapes, and the tall Q8 shapes whose rows take one wave there when one or
+// two streams run (where both kernels give the same bits).  A stream's result
+// never depends on the stream count.  Both kernels read rows through a segment
 // table (one matrix, or several with the same column count stacked into one
 // row space) and can add a residual to the rows they store.
 //
@@ -1278,9 +1279,11 @@ __global__ __launch_bounds__(64 * 4) void gemv_q8_split_kernel(SplitArgs sa)
                     bs[s] = c == 0 ? wq * xv[tt][c][s] : __builtin_fmaf(wq, xv[tt][c][s], bs[s]);
             }
             const float d = f16_lo(u.sc >> lo.q_ssh[0]);
+            // fma into +0 at the first round, as the per-wave-row kernel does
+            // (d * bs would keep a -0 that it turns into +0)
 #pragma unroll
             for (int s = 0; s < NS; s++)
-                acc[s] = tt == 0 ? d * bs[s] : __builtin_fmaf(d, bs[s], acc[s]);
+                acc[s] = __builtin_fmaf(d, bs[s], tt == 0 ? 0.f : acc[s]);
             __builtin_amdgcn_sched_barrier(0);
             load_round(rs_next, tt, nxt[tt]);
             __builtin_amdgcn_sched_barrier(0);
@@ -1400,7 +1403,25 @@ int launch_q8_split(const GemvArgs &a, hipStream_t stream)
     }
 }
 
-// Kernel choice of each format: by shape alone, never by the stream count.
+// Taller Q8 matrices take the per-wave-row kernel, except that with one or
+// two streams a matrix whose rows take one wave of four or five rounds in the
+// row-split kernel takes that kernel (measured faster there: 18.7 against
+// 20.1 us at 17408 x 5120, one stream).  With one wave per row the two
+// kernels do the same operations in the same order -- the lane's 16-column
+// sums, the scale FMAs into +0 then the running sum, round by round, the same
+// 64-lane tree, and no further sum -- so a stream's bits do not depend on
+// which of them ran, and the choice may follow the stream count.
+constexpr int kQ8TallSplitMaxStreams = 2;
+constexpr int kQ8TallSplitMinRounds = 4;  // two rounds measured slower split (32000 x 2048)
+
+bool q8_tall_split(const GemvArgs &a, int n_streams)
+{
+    return n_streams <= kQ8TallSplitMaxStreams && a.rounds >= kQ8TallSplitMinRounds &&
+           split_T(a.rounds) == a.rounds;
+}
+
+// Kernel choice of each format: by shape, and by the stream count only
+// between kernels that give the same bits (above).
 int launch_q8(const GemvArgs &a, int n_streams, hipStream_t st)
 {
     // rows start on dword boundaries when a row holds an even number of blocks
@@ -1409,7 +1430,7 @@ int launch_q8(const GemvArgs &a, int n_streams, hipStream_t st)
         // the row-split form for matrices of up to kQ8SplitMaxRows rows; the
         // per-wave-row kernel, whose many waves hide more latency, for taller
         // ones (measured: it is faster there at four streams)
-        if (a.rows <= kQ8SplitMaxRows)
+        if (a.rows <= kQ8SplitMaxRows || q8_tall_split(a, n_streams))
             switch (n_streams) {
             case 1: rc = launch_q8_split<1>(a, st); break;
             case 2: rc = launch_q8_split<2>(a, st); break;

@@ -50,8 +50,8 @@ int gemv_ssq_res(const void *w, const float *x_a, const float *x_b, float *y_a, 
 // row space (as pti_gemv_q8_multi_grouped stacks them), s < n: the
 // per-wave-row GEMV normalises x while staging it, with the bits pti_rmsnorm
 // gives.  Returns kNormNotFused, launching nothing, when the shape takes the
-// row-split kernel or x does not fit in LDS at once (the caller then runs
-// pti_rmsnorm and the plain GEMV).  Arguments already validated, except that
+// row-split kernel at every stream count or x does not fit in LDS at once (the
+// caller then runs pti_rmsnorm and the plain GEMV).  Arguments already validated, except that
 // the matrices are checked as a grouped launch checks them.
 constexpr int kNormNotFused = 1;
 int q8_gemv_rmsnorm(const void *const *w, const int64_t *rows, int n_mats, const float *x, float *y, int64_t cols,
