@@ -1566,9 +1566,9 @@ int pti_gemv_ssq_grouped(const void *const *w_ssq, const int64_t *rows, int n_ma
 {
     if (!x_a || !x_b || !y_a || !y_b)
         return PTI_ERR_NULL;
-    int64_t total = 0;
-    for (int m = 0; rows && m < n_mats && m < PTI_MAX_GROUP; m++)
-        total += rows[m] > 0 ? rows[m] : 0;
+    int64_t total = 0;  // for the overlap ranges; the arrays are read only once n_mats is in range
+    for (int m = 0; rows && n_mats >= 1 && n_mats <= PTI_MAX_GROUP && m < n_mats; m++)
+        total += rows[m] > 0 ? std::min<int64_t>(rows[m], PTI_MAX_ROWS) : 0;
     const size_t yn = size_t(total) * 4, xn = size_t(cols > 0 ? cols : 0) * 4;
     const pti::Range outs[] = {{y_a, yn}, {y_b, yn}};
     GemvArgs a;
@@ -1659,9 +1659,9 @@ int pti_gemv_q8_multi_grouped(const void *const *w_q8, const int64_t *rows, int 
         return PTI_ERR_NULL;
     if (n_streams < 1 || n_streams > PTI_MAX_STREAMS)
         return PTI_ERR_NSTREAMS;
-    int64_t total = 0;
-    for (int m = 0; rows && m < n_mats && m < PTI_MAX_GROUP; m++)
-        total += rows[m] > 0 ? rows[m] : 0;
+    int64_t total = 0;  // for the overlap ranges; the arrays are read only once n_mats is in range
+    for (int m = 0; rows && n_mats >= 1 && n_mats <= PTI_MAX_GROUP && m < n_mats; m++)
+        total += rows[m] > 0 ? std::min<int64_t>(rows[m], PTI_MAX_ROWS) : 0;
     const size_t yn = size_t(n_streams) * total * 4, xn = size_t(n_streams) * (cols > 0 ? cols : 0) * 4;
     const pti::Range outs[] = {{y, yn}};
     GemvArgs a;

@@ -93,11 +93,10 @@ def test_fused_vs_gemv_and_oracle(env, rows, cols):
     ya, yb, am, acc = fused(env, w, xa, xb, [0, 0], work)
     assert np.array_equal(ya.view(np.uint32), ra.view(np.uint32))
     assert np.array_equal(yb.view(np.uint32), rb.view(np.uint32))
-    idx = np.unique(np.concatenate([np.arange(0, rows, max(1, rows // 200)), [rows - 1]]))
-    ea, eb, ta, tb = oracle.gemv_ssq_rows(oracle.pack_ssq(d["A"], d["B"], d["sA"], d["sB"]), rows, cols,
-                                          d["xA"], d["xB"], idx)
-    check_bound(ya[idx], ea, ta, "y_A")
-    check_bound(yb[idx], eb, tb, "y_B")
+    ea, eb, ta, tb = oracle.gemv_ssq(oracle.pack_ssq(d["A"], d["B"], d["sA"], d["sB"]), rows, cols,
+                                     d["xA"], d["xB"])
+    check_bound(ya, ea, ta, "y_A")
+    check_bound(yb, eb, tb, "y_B")
     check_verify(ya, yb, am, acc, [0, 0])
     # twin B's guess equal to twin A's token, then one that differs
     for guess in (int(am[0]), (int(am[0]) + 1) % rows):
@@ -119,6 +118,14 @@ def test_fused_full_17408x5120(env):
     assert np.array_equal(ya.view(np.uint32), ra.cpu().numpy().view(np.uint32))
     assert np.array_equal(yb.view(np.uint32), rb.cpu().numpy().view(np.uint32))
     check_verify(ya, yb, am, acc, [0, 7])
+    # every row of both twins against the oracle
+    ea, eb, ta, tb = oracle.gemv_ssq(oracle.pack_ssq(d["A"], d["B"], d["sA"], d["sB"]), rows, cols, d["xA"], d["xB"])
+    check_bound(ya, ea, ta, "y_A")
+    check_bound(yb, eb, tb, "y_B")
+    # twin B's guess is twin A's token: both checks pass
+    ya2, yb2, am2, acc2 = fused(env, w, xa, xb, [0, int(am[0])], work)
+    check_verify(ya2, yb2, am2, acc2, [0, int(am[0])])
+    assert acc2 == 2
 
 
 @pytest.mark.parametrize("rows,cols", [(1000, 2048), (17408, 5120), (300, 20992)])

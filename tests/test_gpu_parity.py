@@ -6,6 +6,8 @@ arrays, packed by its own packer):
   * closed forms (one-hot x, unit scales with all-ones x): bit-exact;
   * argmax and accept counts: bit-exact, with the oracle applied to the GPU's
     own logits;
+  * every row of the full-size (17408 x 5120) and decoder-layer outputs, in
+    the launch configuration the benchmark times;
   * properties: SSQ twin == Q8 GEMVs of the split halves (within the bound),
     A==B twins with equal x give bitwise identical outputs, a stream's output
     does not depend on the stream count or its slot, repeated calls are
@@ -236,51 +238,130 @@ def test_scale_edge_values(env):
 
 
 # ------------------------------------------------------------ full-size shapes
+# Every row of every full-size output is compared with the oracle's full GEMV
+# (the oracle computes a 17408 x 5120 twin GEMV in about a tenth of a second).
 
-FULL_ROWS = np.unique(np.concatenate([np.arange(0, 17408, 97), [1, 2, 15, 16, 17, 17406, 17407]]))
 
-
-def test_full_ssq_17408x5120_sampled(env):
+def test_full_ssq_17408x5120_all_rows(env):
     rows, cols = 17408, 5120
-    _note("full ssq 17408x5120, seed 2")
+    _note("full ssq 17408x5120, seed 2, every row")
     d = synth.twin(rows, cols, synth.SEED_SSQ_FFN)
     ya, yb = run_ssq(env, d, rows, cols)
-    Po = oracle.pack_ssq(d["A"], d["B"], d["sA"], d["sB"])
-    ea, eb, ta, tb = oracle.gemv_ssq_rows(Po, rows, cols, d["xA"], d["xB"], FULL_ROWS)
-    ra = check_bound(ya[FULL_ROWS], ea, ta, "y_A")
-    rb = check_bound(yb[FULL_ROWS], eb, tb, "y_B")
-    _note(f"  worst |err|/T over {FULL_ROWS.size} rows: A {ra:.2e}  B {rb:.2e}")
-    assert np.all(np.isfinite(ya)) and np.all(np.isfinite(yb))
+    ea, eb, ta, tb = oracle.gemv_ssq(oracle.pack_ssq(d["A"], d["B"], d["sA"], d["sB"]), rows, cols, d["xA"], d["xB"])
+    ra = check_bound(ya, ea, ta, "y_A")
+    rb = check_bound(yb, eb, tb, "y_B")
+    _note(f"  worst |err|/T over {rows} rows: A {ra:.2e}  B {rb:.2e}")
 
 
-@pytest.mark.parametrize("n", [1, 2, 4])
-def test_full_q8_17408x5120_sampled(env, n):
+def test_full_ssq_17408x5120_same_twins(env):
+    """The self-twin (A == B) at the benchmark's shape: with one x for both
+    twins the outputs are bitwise equal; with independent x each is within
+    the bound of the oracle, every row."""
     rows, cols = 17408, 5120
-    _note(f"full q8 17408x5120 n={n}, seed 3")
+    _note("full ssq 17408x5120 A == B")
+    d = synth.twin(rows, cols, synth.SEED_SSQ_FFN, same=True, same_x=True)
+    ya, yb = run_ssq(env, d, rows, cols)
+    assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32))
+    d = synth.twin(rows, cols, synth.SEED_SSQ_FFN, same=True)
+    ya, yb = run_ssq(env, d, rows, cols)
+    ea, eb, ta, tb = oracle.gemv_ssq(oracle.pack_ssq(d["A"], d["B"], d["sA"], d["sB"]), rows, cols, d["xA"], d["xB"])
+    check_bound(ya, ea, ta, "y_A")
+    check_bound(yb, eb, tb, "y_B")
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_full_q8_17408x5120_all_rows(env, n):
+    rows, cols = 17408, 5120
+    _note(f"full q8 17408x5120 n={n}, seed 3, every row")
     d = synth.q8(rows, cols, n, synth.SEED_Q8_FFN)
     y = run_q8(env, d["Q"], d["S"], d["X"])
-    e, t = oracle.gemv_q8_rows(oracle.pack_q8(d["Q"], d["S"]), rows, cols, d["X"], FULL_ROWS)
+    e, t = oracle.gemv_q8(oracle.pack_q8(d["Q"], d["S"]), rows, cols, d["X"])
     for s in range(n):
-        r = check_bound(y[s][FULL_ROWS], e[s], t[s], f"stream {s}")
+        r = check_bound(y[s], e[s], t[s], f"stream {s}")
         _note(f"  stream {s}: worst |err|/T {r:.2e}")
 
 
 @pytest.mark.parametrize("name,rows,cols", synth.LAYER_SHAPES, ids=[s[0] for s in synth.LAYER_SHAPES])
-def test_layer_sweep_sampled(env, name, rows, cols):
+def test_layer_sweep_all_rows(env, name, rows, cols):
+    """One decoder layer's matrices at their real shapes, every row: SSQ with
+    distinct twins, SSQ with A == B (bitwise equal twins on one x, and within
+    the bound on independent x), and Q8 at one, two and four streams (each
+    stream count its own call, so each runs the kernel it takes)."""
     _note(f"layer {name} {rows}x{cols}")
     d = synth.twin(rows, cols, synth.SEED_LAYER)
     ya, yb = run_ssq(env, d, rows, cols)
-    idx = np.unique(np.concatenate([np.arange(0, rows, max(1, rows // 150)), [rows - 1]]))
-    ea, eb, ta, tb = oracle.gemv_ssq_rows(oracle.pack_ssq(d["A"], d["B"], d["sA"], d["sB"]), rows, cols,
-                                          d["xA"], d["xB"], idx)
-    check_bound(ya[idx], ea, ta, "y_A")
-    check_bound(yb[idx], eb, tb, "y_B")
+    ea, eb, ta, tb = oracle.gemv_ssq(oracle.pack_ssq(d["A"], d["B"], d["sA"], d["sB"]), rows, cols, d["xA"], d["xB"])
+    check_bound(ya, ea, ta, "y_A")
+    check_bound(yb, eb, tb, "y_B")
+    s = synth.twin(rows, cols, synth.SEED_LAYER, same=True, same_x=True)
+    sa, sb = run_ssq(env, s, rows, cols)
+    assert np.array_equal(sa.view(np.uint32), sb.view(np.uint32)), "A == B twins on one x"
+    s = synth.twin(rows, cols, synth.SEED_LAYER, same=True)
+    sa, sb = run_ssq(env, s, rows, cols)
+    esa, esb, tsa, tsb = oracle.gemv_ssq(oracle.pack_ssq(s["A"], s["B"], s["sA"], s["sB"]), rows, cols,
+                                         s["xA"], s["xB"])
+    check_bound(sa, esa, tsa, "A == B, y_A")
+    check_bound(sb, esb, tsb, "A == B, y_B")
     X = np.stack([d["xA"], d["xB"], -d["xA"], d["xB"] * 0.5])
-    y = run_q8(env, d["A"], d["sA"], X)
-    e, t = oracle.gemv_q8_rows(oracle.pack_q8(d["A"], d["sA"]), rows, cols, X, idx)
-    for s in range(4):
-        check_bound(y[s][idx], e[s], t[s], f"stream {s}")
-    assert np.all(np.abs(y[0][idx].astype(np.float64) - ya[idx]) <= 2 * TOL * ta)
+    e, t = oracle.gemv_q8(oracle.pack_q8(d["A"], d["sA"]), rows, cols, X)
+    for n in (1, 2, 4):
+        y = run_q8(env, d["A"], d["sA"], X[:n])
+        for k in range(n):
+            check_bound(y[k], e[k], t[k], f"q8 n={n} stream {k}")
+        assert np.all(np.abs(y[0].astype(np.float64) - ya) <= 2 * TOL * ta)
+
+
+# Edge values in SSQ slots and scales: -128 in the high byte (twin A), the low
+# byte (twin B) or both; for each twin's scale the smallest and largest
+# subnormals, -0, +0, -1 and 65504.  (120, 640): the row-split kernel;
+# (12, 20544): rows of 41 rounds, the per-wave-row kernel.
+SSQ_EDGE_SHAPES = [(120, 640), (12, 20544)]
+
+
+def ssq_edge_inputs(rows, cols, seed):
+    d = synth.twin(rows, cols, seed)
+    A, B, sA, sB = d["A"], d["B"], d["sA"], d["sB"]
+    A[0, :] = -128
+    B[1, :] = -128
+    A[2, :] = -128
+    B[2, :] = -128
+    A[3, ::2] = -128
+    B[3, 1::2] = -128
+    edges = [0x0001, 0x03FF, 0x8000, 0x0000, 0xBC00, 0x7BFF]
+    for k, v in enumerate(edges):
+        sA[4 + k % (rows - 4), :] = v
+        sB[4 + (k + 3) % (rows - 4), :] = v
+    sA[0, 0], sB[1, -1] = 0x7BFF, 0x0001
+    return d
+
+
+@pytest.mark.parametrize("rows,cols", SSQ_EDGE_SHAPES, ids=[f"{r}x{c}" for r, c in SSQ_EDGE_SHAPES])
+def test_ssq_edge_values(env, rows, cols):
+    torch, pti, dev = env
+    _note(f"ssq edge values {rows}x{cols}")
+    d = ssq_edge_inputs(rows, cols, 91)
+    ya, yb = run_ssq(env, d, rows, cols)
+    ea, eb, ta, tb = oracle.gemv_ssq(oracle.pack_ssq(d["A"], d["B"], d["sA"], d["sB"]), rows, cols, d["xA"], d["xB"])
+    check_bound(ya, ea, ta, "y_A")
+    check_bound(yb, eb, tb, "y_B")
+    # the fused step and two streams per twin run the same rows
+    w = torch.from_numpy(pti.pack_ssq(d["A"], d["B"], d["sA"], d["sB"])).to(dev)
+    xa, xb = torch.from_numpy(d["xA"]).to(dev), torch.from_numpy(d["xB"]).to(dev)
+    fa, fb, am, acc = pti.gemv_ssq_verify(w, xa, xb, torch.zeros(2, dtype=torch.int32, device=dev),
+                                          pti.ssq_verify_workspace(dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(fa.cpu().numpy().view(np.uint32), ya.view(np.uint32))
+    assert np.array_equal(fb.cpu().numpy().view(np.uint32), yb.view(np.uint32))
+    want, _ = oracle.verify_argmax(np.stack([ya, yb]), np.zeros(2, np.int32))
+    assert list(am.cpu().numpy()) == list(want)
+    ma, mb = pti.gemv_ssq_multi(w, torch.stack([xa, -xa]), torch.stack([xb, xb * 2]))
+    torch.cuda.synchronize()
+    assert np.array_equal(ma[0].cpu().numpy().view(np.uint32), ya.view(np.uint32))
+    assert np.array_equal(mb[0].cpu().numpy().view(np.uint32), yb.view(np.uint32))
+    e2a, e2b, t2a, t2b = oracle.gemv_ssq(oracle.pack_ssq(d["A"], d["B"], d["sA"], d["sB"]), rows, cols,
+                                         -d["xA"], d["xB"] * 2)
+    check_bound(ma[1].cpu().numpy(), e2a, t2a, "multi y_A stream 1")
+    check_bound(mb[1].cpu().numpy(), e2b, t2b, "multi y_B stream 1")
 
 
 # ------------------------------------------------------------ beyond 4 GiB
@@ -313,6 +394,31 @@ def test_q8_beyond_4gib_all_rows(env):
     idx = np.arange(rows) % period
     y = y.cpu().numpy()
     for s in range(2):
+        check_bound(y[s], e[s][idx], t[s][idx], f"stream {s}")
+
+
+@pytest.mark.parametrize("n", [1, 2])
+def test_q8_beyond_4gib_split_kernel_all_rows(env, n):
+    """4.35 GB of Q8 weights at 5120 columns (800,003 rows of 5440 bytes): one
+    and two streams take the row-split kernel for these tall rows of five
+    rounds.  Row offsets pass 2^31 and 2^32; the 4096-row period
+    (4096 x 5440 bytes) divides neither, so a wrapped offset reads other
+    values.  Every row is checked against the oracle's result for its base
+    row."""
+    torch, pti, dev = env
+    rows, cols, period = 800_003, 5120, 4096
+    _note(f"q8 {rows}x{cols} n={n} tiled from {period} rows")
+    d = synth.q8(period, cols, n, synth.SEED_BIG + n)
+    w = _tiled(env, pti.pack_q8(d["Q"], d["S"]), rows)
+    assert w.numel() > 2 ** 32
+    y = pti.gemv_q8_multi(w, torch.from_numpy(d["X"]).to(dev))
+    torch.cuda.synchronize()
+    del w
+    torch.cuda.empty_cache()
+    e, t = oracle.gemv_q8(oracle.pack_q8(d["Q"], d["S"]), period, cols, d["X"])
+    idx = np.arange(rows) % period
+    y = y.cpu().numpy()
+    for s in range(n):
         check_bound(y[s], e[s][idx], t[s][idx], f"stream {s}")
 
 

@@ -451,6 +451,31 @@ def check_draws(stack, passes, temp=0.0, uniforms=None, N=None):
     return n_amb
 
 
+AMBIG = 2e-5  # a greedy step is ambiguous when the oracle's top-2 gap is <= AMBIG * max_v T_v
+
+
+def greedy_chain_checks(chain, first, model, what):
+    """The GPU's greedy chain against the fp64 oracle, transition by transition
+    (teacher-forced on the GPU's previous token): every transition whose
+    argmax differs from the oracle's must be ambiguous, i.e. the oracle's
+    top-2 gap is at most AMBIG * max T, with T_v = sum_c |head[v][c] r[c]|
+    the scale of logit v's fp32 rounding error.  With no ambiguous step the
+    chain equals the oracle's own free-running greedy chain."""
+    prev = [first] + list(chain[:-1])
+    want = model.logits(prev)
+    T = model.head_abs_terms(prev)
+    srt = np.sort(want, axis=1)
+    gap = srt[:, -1] - srt[:, -2]
+    amb = gap <= AMBIG * T.max(axis=1)
+    mism = np.array([toy.argmax_first(w) != t for w, t in zip(want, chain)])
+    print(f"{what}: {int((~mism).sum())}/{len(chain)} transitions equal the fp64 oracle's argmax, "
+          f"{int(amb.sum())} ambiguous, smallest gap / (2e-5 max T) {float((gap / (AMBIG * T.max(axis=1))).min()):.3g}")
+    assert not (mism & ~amb).any(), f"{what}: disagreement at a clear argmax, steps {np.nonzero(mism & ~amb)[0]}"
+    if not amb.any():
+        assert list(chain) == toy.greedy_chain(model, first, len(chain)), f"{what}: oracle greedy chain"
+    return int(amb.sum())
+
+
 def test_decode_greedy_q8_four_streams(full_q8, full_oracle):
     steps = 64
     c4, a4, p4 = full_q8.gpu.decode(1, 4, steps)
@@ -460,24 +485,18 @@ def test_decode_greedy_q8_four_streams(full_q8, full_oracle):
     rc, ra = replay(p4, 1, 4, steps)
     assert rc == c4.tolist() and ra == a4.tolist()
     check_draws(full_q8, p4)
-    # the chain against the fp64 oracle's own greedy decisions, transition by transition
-    prev = [1] + c4.tolist()[:-1]
-    want = full_oracle.logits(prev)
-    agree = sum(int(np.argmax(w)) == t for w, t in zip(want, c4.tolist()))
-    srt = np.sort(want, axis=1)
-    near_tie = int(np.sum(srt[:, -1] - srt[:, -2] < 1e-3 * want.std()))
-    print(f"greedy chain: {agree}/{steps} transitions equal the fp64 oracle's argmax, {near_tie} near-ties")
-    assert agree + near_tie >= steps
+    greedy_chain_checks(c4.tolist(), 1, full_oracle, "q8 greedy chain")
 
 
-def test_decode_greedy_ssq_self_twin(full_ssq):
+def test_decode_greedy_ssq_self_twin(full_ssq, full_oracle):
     st = full_ssq
-    steps = 32
+    steps = 64
     c, a, p = st.gpu.decode(1, 2, steps)
     assert a.tolist() == [2] * steps
     rc, ra = replay(p, 1, 2, steps)
     assert rc == c.tolist()
     check_draws(st, p)
+    greedy_chain_checks(c.tolist(), 1, full_oracle, "ssq self-twin greedy chain")
 
 
 def test_decode_greedy_ssq_distinct_twins_rejects_and_redraws(small_raw):
@@ -510,18 +529,22 @@ def test_decode_greedy_small_q8_all_stream_counts(small_raw):
         check_draws(st, p)
 
 
-def test_decode_sampled_q8_four_streams_statistics():
-    """T = 0.7 on the stack with a flatter head (scales / 4, mean sum p^2 ~ 0.5)."""
+def sampled_statistics(raw, steps, what):
+    """T = 0.7, four Q8 streams: the loop's control is replayed through the
+    oracle's loop, every draw equals the oracle's inverse-CDF draw on the
+    GPU's logits (boundary cases flagged), and the checks' pass count is
+    z-tested against the collision probability sum p^2 and against the
+    probability of the guess, both from the oracle's own fp64 logits.
+    Returns the mean sum p^2 over the checks."""
     pti = _pti()
-    raw = synth.toy_weights(synth.SEED_TOY, lm_scale_div=4.0)
     st = Stack(raw, pti.FMT_Q8)
-    N, steps = 4, 160
+    N = 4
     u = np.random.default_rng(synth.SEED_TOY).random((steps + 1) * 2 * N)
     c, a, p = st.gpu.decode(1, N, steps, temperature=TEMP, uniforms=u)
     rc, ra = replay(p, 1, N, steps)
     assert rc == c.tolist() and ra == a.tolist()
     n_amb = check_draws(st, p, TEMP, u, N)
-    print(f"sampled run: accept histogram {np.bincount(a, minlength=N + 1)[1:]}, {n_amb} boundary draws")
+    print(f"{what}: accept histogram {np.bincount(a, minlength=N + 1)[1:]}, {n_amb} boundary draws")
     # checks evaluated at each step: i = 1 .. min(a, N-1); check i passes iff i < a
     inputs = {}
     for k, s, i, inp, out in p:
@@ -544,9 +567,25 @@ def test_decode_sampled_q8_four_streams_statistics():
     ind = np.array(ind)
     coll = np.array([float((P[c] ** 2).sum()) for c in ctx])
     cond = np.array([float(P[c][gs]) for c, gs in zip(ctx, guess)])
-    z_coll = (ind.sum() - coll.sum()) / math.sqrt((coll * (1 - coll)).sum())
+    z_coll = (ind.sum() - coll.sum()) / math.sqrt(max((coll * (1 - coll)).sum(), 1e-12))
     z_cond = (ind.sum() - cond.sum()) / math.sqrt(max((cond * (1 - cond)).sum(), 1e-12))
-    print(f"{len(ind)} checks: passed {ind.sum():.0f}, expected sum p^2 {coll.sum():.1f} (z {z_coll:.2f}), "
-          f"expected p(guess) {cond.sum():.1f} (z {z_cond:.2f})")
+    print(f"{what}: {len(ind)} checks: passed {ind.sum():.0f}, expected sum p^2 {coll.sum():.1f} (z {z_coll:.2f}), "
+          f"expected p(guess) {cond.sum():.1f} (z {z_cond:.2f}), mean sum p^2 {coll.mean():.3f}")
     assert abs(z_coll) <= 4 and abs(z_cond) <= 4
-    assert 0.2 < coll.mean() < 0.95  # the statistics are informative
+    return float(coll.mean())
+
+
+def test_decode_sampled_q8_four_streams_statistics():
+    """The toy stack exactly as specified (seed 1), T = 0.7, 160 steps.  Its
+    logits are spread widely (mean sum p^2 near 0.9), so most checks pass;
+    the z-tests still compare the pass count with sum p^2."""
+    mean = sampled_statistics(synth.toy_weights(synth.SEED_TOY), 160, "sampled, seed-1 stack")
+    assert mean > 0.5
+
+
+def test_decode_sampled_q8_flat_head_statistics():
+    """The labelled second run: the same stack with the LM-head scales divided
+    by 4 (mean sum p^2 ~ 0.5), where a pass is close to a coin flip and the
+    z-tests have the most power."""
+    mean = sampled_statistics(synth.toy_weights(synth.SEED_TOY, lm_scale_div=4.0), 160, "sampled, head / 4")
+    assert 0.2 < mean < 0.95  # the statistics are informative

@@ -122,6 +122,78 @@ def test_zero_down_is_identity_and_head_matches_c_gemv():
         assert np.all(np.abs(lg[i] - y[0]) <= 2.0 ** -24 * t[0] * 1.01 + 1e-15)
 
 
+def test_head_abs_terms_matches_c_oracle_t_and_brute_force():
+    """T_v = sum_c |head[v][c] r[c]| with r = rmsnorm(h_L): the C oracle's Q8
+    GEMV returns the same sum of |terms| from the packed head (its x is r
+    rounded to fp32, which moves T by <= 2^-24 T), and a scalar loop over the
+    dequantised weights gives it exactly."""
+    g = np.random.default_rng(12)
+    raw = _tiny_raw(g, hidden=64, ffn=96, vocab=50, layers=2)
+    m = toy.ToyModel(raw, eps=1e-6)
+    toks = [0, 13, 49]
+    T = m.head_abs_terms(toks)
+    assert T.shape == (3, 50)
+    r = toy.rmsnorm(m.hidden_states(toks)[-1], 1e-6)
+    O = oracle.default()
+    P = O.pack_q8(raw["head"]["Q"], raw["head"]["S"])
+    W = toy.dequant(raw["head"]["Q"], raw["head"]["S"])
+    for i in range(3):
+        _, t = O.gemv_q8(P, 50, 64, r[i:i + 1])
+        np.testing.assert_allclose(T[i], t[0], rtol=2.0 ** -23)
+        for v in (0, 17, 49):
+            brute = 0.0
+            for c in range(64):
+                brute += abs(W[v, c] * r[i, c])
+            assert abs(T[i, v] - brute) <= 1e-12 * brute
+    # it bounds |logit| and is not the logit itself (absolute values inside the sum)
+    lg = m.logits(toks)
+    assert np.all(np.abs(lg) <= T * (1 + 1e-12)) and np.any(np.abs(lg) < 0.9 * T)
+
+
+def test_greedy_chain_matches_transition_table_and_systolic_loop():
+    """The stack is a Markov chain: greedy decoding follows the table
+    next[t] = argmax_v logits(t)[v] (numpy's argmax, first index on ties),
+    built from one batched logits call; and the staggered loop's committed
+    chain under the same argmax draws is that chain for every stream count."""
+    g = np.random.default_rng(13)
+    raw = _tiny_raw(g, hidden=32, ffn=64, vocab=40, layers=2)
+    m = toy.ToyModel(raw, eps=1e-6)
+    nxt = np.argmax(m.logits(list(range(40))), axis=1)
+    for first in (0, 7, 39):
+        want, t = [], first
+        for _ in range(25):
+            t = int(nxt[t])
+            want.append(t)
+        got = toy.greedy_chain(m, first, 25)
+        assert got == want
+        assert len(got) == 25 and got[0] != first or nxt[first] == first
+        for N in (1, 2, 4):
+            committed, _, _ = toy.systolic_decode(lambda k, s, i, tok: int(nxt[tok]), first, N, 25)
+            assert committed == got
+
+
+def test_greedy_chain_and_abs_terms_pins_catch_planted_mistakes():
+    """Mutants of the two helpers must fail the pins above."""
+    g = np.random.default_rng(14)
+    raw = _tiny_raw(g, hidden=32, ffn=64, vocab=40, layers=2)
+    m = toy.ToyModel(raw, eps=1e-6)
+    nxt = np.argmax(m.logits(list(range(40))), axis=1)
+    want, t = [], 3
+    for _ in range(10):
+        t = int(nxt[t])
+        want.append(t)
+    # chain that includes the first token / stops one short / uses the last index on ties
+    assert ([3] + toy.greedy_chain(m, 3, 9)) != want
+    assert toy.greedy_chain(m, 3, 9) != want
+    # abs outside the sum (|sum| instead of sum |.|) is not the C oracle's T
+    r = toy.rmsnorm(m.hidden_states([5])[-1], 1e-6)
+    O = oracle.default()
+    _, t = O.gemv_q8(O.pack_q8(raw["head"]["Q"], raw["head"]["S"]), 40, 32, r)
+    wrong = np.abs(r @ m.head.T)
+    assert not np.allclose(wrong[0], t[0], rtol=1e-6)
+    assert np.allclose(m.head_abs_terms([5])[0], t[0], rtol=2.0 ** -23)
+
+
 def test_batch_rows_are_independent():
     g = np.random.default_rng(9)
     m = toy.ToyModel(_tiny_raw(g), eps=1e-6)
