@@ -253,6 +253,25 @@ int pti_sample_verify(const float *logits, const int32_t *tokens_in, const doubl
                       int32_t *tokens_out, int32_t *accept_out, int64_t vocab, int n_streams, void *work,
                       size_t work_bytes, void *stream);
 
+/* pti_sample_verify without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The part sums go to a scratch array the
+ * library keeps in device memory: PTI_STATIC_SCRATCH_BYTES per GPU, held from
+ * the first call on that GPU until the process ends; the call itself
+ * allocates nothing.  Arguments, results and errors as pti_sample_verify,
+ * plus PTI_ERR_SHAPE when pti_sample_verify_workspace_bytes(vocab,
+ * n_streams) exceeds PTI_STATIC_SCRATCH_BYTES (at most 4096 parts of 2048
+ * logits over all streams: vocab up to 2,097,152 at four streams), and
+ * PTI_ERR_HIP if the scratch's device address cannot be obtained.  Every call
+ * on one GPU shares that GPU's scratch: calls that overlap in time on one GPU
+ * (on different streams or host threads) race and give wrong draws; calls
+ * enqueued on one stream are ordered and safe.  Nothing needs to start at
+ * zero: each call writes every part sum before reading it. */
+#define PTI_STATIC_SCRATCH_BYTES 65536
+int pti_sample_verify_static(const float *logits, const int32_t *tokens_in, const double *uniforms,
+                             double temperature, int32_t *tokens_out, int32_t *accept_out, int64_t vocab,
+                             int n_streams, void *stream);
+
 /* ------------------------------------------------------------------------- */
 /* Decoder-stack glue [Digest, implementation architecture: the forward pass in
  * which one weight load serves every stream].  Device calls, conventions as

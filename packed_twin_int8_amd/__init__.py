@@ -25,6 +25,7 @@ from .build import LIB as LIB_PATH
 __all__ = [
     "PtiError", "lib", "ssq_bytes", "q8_bytes", "pack_ssq", "unpack_ssq", "pack_q8", "unpack_q8",
     "ssq_split", "ssq_join", "gemv_ssq", "gemv_q8_multi", "verify_argmax", "status_str", "sample_verify", "sample_verify_workspace",
+    "sample_verify_static",
     "embed_q8", "embed_ssq", "rmsnorm", "silu_mul", "add", "ToyStack", "FMT_Q8", "FMT_SSQ",
 ]
 
@@ -40,7 +41,8 @@ EXPORTS = (
     "pti_status_str", "pti_last_hip_error", "pti_abi_version", "pti_ssq_bytes", "pti_q8_bytes", "pti_pack_ssq",
     "pti_unpack_ssq", "pti_pack_q8", "pti_unpack_q8", "pti_ssq_split", "pti_ssq_join", "pti_gemv_ssq",
     "pti_gemv_ssq_verify", "pti_gemv_q8_multi", "pti_gemv_ssq_grouped", "pti_gemv_q8_multi_grouped",
-    "pti_gemv_ssq_multi", "pti_attn_workspace_bytes", "pti_attn_decode", "pti_verify_argmax", "pti_sample_verify", "pti_sample_verify_workspace_bytes", "pti_embed_q8", "pti_embed_ssq", "pti_rmsnorm",
+    "pti_gemv_ssq_multi", "pti_attn_workspace_bytes", "pti_attn_decode", "pti_verify_argmax", "pti_sample_verify", "pti_sample_verify_workspace_bytes",
+    "pti_sample_verify_static", "pti_embed_q8", "pti_embed_ssq", "pti_rmsnorm",
     "pti_silu_mul", "pti_add", "pti_toy_workspace_bytes", "pti_toy_forward", "pti_toy_decode",
     "pti_toy_forward_graph", "pti_graph_launch", "pti_graph_destroy",
 )
@@ -103,6 +105,7 @@ def lib() -> ctypes.CDLL:
         L.pti_gemv_q8_multi_grouped.argtypes = [_P, _P, _INT, _P, _P, _I64, _INT, _P]
         L.pti_verify_argmax.argtypes = [_P, _P, _P, _P, _I64, _INT, _P]
         L.pti_sample_verify.argtypes = [_P, _P, _P, ctypes.c_double, _P, _P, _I64, _INT, _P, ctypes.c_size_t, _P]
+        L.pti_sample_verify_static.argtypes = [_P, _P, _P, ctypes.c_double, _P, _P, _I64, _INT, _P]
         L.pti_sample_verify_workspace_bytes.argtypes = [_I64, _INT]
         L.pti_sample_verify_workspace_bytes.restype = ctypes.c_size_t
         L.pti_embed_q8.argtypes = [_P, _P, _P, _I64, _I64, _INT, _P]
@@ -480,6 +483,28 @@ def sample_verify(logits, tokens_in, uniforms, temperature: float, tokens_out=No
                                                         float(temperature), tokens_out.data_ptr(),
                                                         accept_out.data_ptr(), vocab, n, work.data_ptr(),
                                                         work.numel() * work.element_size(), _stream(stream)))
+    return tokens_out, accept_out
+
+
+STATIC_SCRATCH_BYTES = 65536  # PTI_STATIC_SCRATCH_BYTES
+
+
+def sample_verify_static(logits, tokens_in, uniforms, temperature: float, tokens_out, accept_out, stream=None):
+    """sample_verify with the part sums in the library's own scratch (the call
+    allocates nothing; outputs must be given).  Calls overlapping in time on
+    one GPU share that scratch and race."""
+    torch = _torch()
+    _dev(logits, "logits", torch.float32), _dev(tokens_in, "tokens_in", torch.int32)
+    _dev(uniforms, "uniforms", torch.float64)
+    _dev(tokens_out, "tokens_out", torch.int32), _dev(accept_out, "accept_out", torch.int32)
+    if logits.dim() == 1:
+        logits = logits.unsqueeze(0)
+    n, vocab = logits.shape
+    if tokens_in.numel() != n or uniforms.numel() != n or tokens_out.numel() != n or accept_out.numel() < 1:
+        raise ValueError("sample_verify_static: one token, uniform and output per stream, one accept count")
+    _check("pti_sample_verify_static", lib().pti_sample_verify_static(
+        logits.data_ptr(), tokens_in.data_ptr(), uniforms.data_ptr(), float(temperature), tokens_out.data_ptr(),
+        accept_out.data_ptr(), vocab, n, _stream(stream)))
     return tokens_out, accept_out
 
 

@@ -23,6 +23,7 @@
 //     the accept count of the drawn tokens.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cmath>
 
@@ -573,31 +574,39 @@ extern "C" size_t pti_sample_verify_workspace_bytes(int64_t vocab, int n_streams
     return size_t(n_streams) * size_t(sv_parts(vocab)) * sizeof(SvPart);
 }
 
-extern "C" int pti_sample_verify(const float *logits, const int32_t *tokens_in, const double *uniforms,
-                                 double temperature, int32_t *tokens_out, int32_t *accept_out, int64_t vocab,
-                                 int n_streams, void *work, size_t work_bytes, void *stream)
+namespace {
+
+// Checks every argument of the sampled verify except the workspace, which
+// each entry point checks its own way.
+int sample_verify_args(const float *logits, const int32_t *tokens_in, const double *uniforms, double temperature,
+                       const int32_t *tokens_out, const int32_t *accept_out, int64_t vocab, int n_streams)
 {
-    if (!logits || !tokens_in || !uniforms || !tokens_out || !accept_out || !work)
+    if (!logits || !tokens_in || !uniforms || !tokens_out || !accept_out)
         return PTI_ERR_NULL;
     if (vocab < 1 || vocab > PTI_MAX_VOCAB || !(temperature > 0.0) || !std::isfinite(temperature))
         return PTI_ERR_SHAPE;
     if (n_streams < 1 || n_streams > PTI_MAX_STREAMS)
         return PTI_ERR_NSTREAMS;
-    if (work_bytes < pti_sample_verify_workspace_bytes(vocab, n_streams))
-        return PTI_ERR_SHAPE;
     if (!pti::aligned(logits, 4) || !pti::aligned(tokens_in, 4) || !pti::aligned(uniforms, 8) ||
-        !pti::aligned(tokens_out, 4) || !pti::aligned(accept_out, 4) || !pti::aligned(work, 16))
+        !pti::aligned(tokens_out, 4) || !pti::aligned(accept_out, 4))
         return PTI_ERR_ALIGN;
     const size_t ns = size_t(n_streams);
     const pti::Range L{logits, ns * size_t(vocab) * 4}, T{tokens_in, ns * 4}, U{uniforms, ns * 8},
-        O{tokens_out, ns * 4}, C{accept_out, 4}, W{work, pti_sample_verify_workspace_bytes(vocab, n_streams)};
-    for (const pti::Range &out : {O, C, W})
+        O{tokens_out, ns * 4}, C{accept_out, 4};
+    for (const pti::Range &out : {O, C})
         if (pti::overlap(out, L) || pti::overlap(out, T) || pti::overlap(out, U))
             return PTI_ERR_OVERLAP;
-    if (pti::overlap(O, C) || pti::overlap(O, W) || pti::overlap(C, W))
+    if (pti::overlap(O, C))
         return PTI_ERR_OVERLAP;
+    return PTI_OK;
+}
+
+// The three kernels of a sampled verify, with the part sums in `parts`.
+int launch_sample_verify(const float *logits, const int32_t *tokens_in, const double *uniforms, double temperature,
+                         int32_t *tokens_out, int32_t *accept_out, int64_t vocab, int n_streams, SvPart *parts,
+                         void *stream)
+{
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    SvPart *parts = static_cast<SvPart *>(work);
     const int64_t np = sv_parts(vocab);
     hipLaunchKernelGGL(sv_part_kernel, dim3((unsigned)np, (unsigned)n_streams), dim3(kSvThreads), 0, st, logits,
                        temperature, parts, vocab, np);
@@ -605,4 +614,79 @@ extern "C" int pti_sample_verify(const float *logits, const int32_t *tokens_in, 
                        temperature, parts, tokens_out, vocab, np);
     hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, st, tokens_in, tokens_out, accept_out, n_streams);
     return launch_status();
+}
+
+// Scratch of the allocation-free sampled verify: the part sums, in device
+// memory that the library owns.  Each GPU the library runs on holds its own
+// copy until the process ends; host code reaches it only through the
+// per-device address from hipGetSymbolAddress (the array's name is a host-side
+// stand-in, not a device address).  Every call on a GPU shares that GPU's copy.
+constexpr size_t kStaticScratchBytes = PTI_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch, looked up once per device
+// (with that device current) and kept; nullptr with the HIP error recorded if
+// the lookup fails.
+void *scratch_ptr()
+{
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        pti::set_hip_error(e != hipSuccess ? e : hipErrorInvalidDevice);
+        return nullptr;
+    }
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // two threads racing both look it up and store the same address
+        if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess || !p) {
+            pti::set_hip_error(e != hipSuccess ? e : hipErrorInvalidSymbol);
+            return nullptr;
+        }
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+}  // namespace
+
+extern "C" int pti_sample_verify_static(const float *logits, const int32_t *tokens_in, const double *uniforms,
+                                        double temperature, int32_t *tokens_out, int32_t *accept_out, int64_t vocab,
+                                        int n_streams, void *stream)
+{
+    if (const int rc = sample_verify_args(logits, tokens_in, uniforms, temperature, tokens_out, accept_out, vocab,
+                                          n_streams);
+        rc != PTI_OK)
+        return rc;
+    if (pti_sample_verify_workspace_bytes(vocab, n_streams) > kStaticScratchBytes)
+        return PTI_ERR_SHAPE;  // more part sums than the library's scratch holds
+    void *p = scratch_ptr();
+    if (!p)
+        return PTI_ERR_HIP;
+    return launch_sample_verify(logits, tokens_in, uniforms, temperature, tokens_out, accept_out, vocab, n_streams,
+                                static_cast<SvPart *>(p), stream);
+}
+
+extern "C" int pti_sample_verify(const float *logits, const int32_t *tokens_in, const double *uniforms,
+                                 double temperature, int32_t *tokens_out, int32_t *accept_out, int64_t vocab,
+                                 int n_streams, void *work, size_t work_bytes, void *stream)
+{
+    if (!work)
+        return PTI_ERR_NULL;
+    if (const int rc = sample_verify_args(logits, tokens_in, uniforms, temperature, tokens_out, accept_out, vocab,
+                                          n_streams);
+        rc != PTI_OK)
+        return rc;
+    if (work_bytes < pti_sample_verify_workspace_bytes(vocab, n_streams))
+        return PTI_ERR_SHAPE;
+    if (!pti::aligned(work, 16))
+        return PTI_ERR_ALIGN;
+    const size_t ns = size_t(n_streams);
+    const pti::Range L{logits, ns * size_t(vocab) * 4}, T{tokens_in, ns * 4}, U{uniforms, ns * 8},
+        O{tokens_out, ns * 4}, C{accept_out, 4}, W{work, pti_sample_verify_workspace_bytes(vocab, n_streams)};
+    if (pti::overlap(W, L) || pti::overlap(W, T) || pti::overlap(W, U) || pti::overlap(W, O) || pti::overlap(W, C))
+        return PTI_ERR_OVERLAP;
+    return launch_sample_verify(logits, tokens_in, uniforms, temperature, tokens_out, accept_out, vocab, n_streams,
+                                static_cast<SvPart *>(work), stream);
 }

@@ -311,6 +311,33 @@ def test_sample_verify_errors():
     assert call(a8=_fake(A4 - 16)) == OVERLAP  # workspace over accept_out
 
 
+def test_sample_verify_static_errors():
+    """The allocation-free form: the workspace form's argument checks, and
+    PTI_ERR_SHAPE (before any HIP call) when the part sums would not fit the
+    library's scratch."""
+    L = pti.lib()
+    f = L.pti_sample_verify_static
+    ok = (_fake(A0), _fake(A1), _fake(A2), 0.7, _fake(A3), _fake(A4), 100, 2, None)
+
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return f(*a)
+
+    assert call(a0=None) == NULL and call(a2=None) == NULL
+    assert call(a3=0.0) == SHAPE and call(a3=float("nan")) == SHAPE and call(a6=0) == SHAPE
+    assert call(a7=0) == NSTREAMS and call(a7=5) == NSTREAMS
+    assert call(a2=_fake(A2 + 4)) == ALIGN
+    assert call(a4=_fake(A2 + 8)) == OVERLAP
+    # the scratch holds 4096 part sums of 2048 logits: 4 streams x 2,097,152 fit, one more logit does not
+    assert pti.STATIC_SCRATCH_BYTES == 65536
+    assert L.pti_sample_verify_workspace_bytes(2048 * 1024, 4) == pti.STATIC_SCRATCH_BYTES
+    assert call(a6=2048 * 1024 + 1, a7=4, a1=_fake(0x70000000), a2=_fake(0x71000000), a3=0.7,
+                a4=_fake(0x72000000), a5=_fake(0x73000000)) == SHAPE
+    assert call(a6=4 * 2048 * 1024 + 1, a7=1) == SHAPE
+
+
 def test_glue_errors():
     L = pti.lib()
     assert L.pti_embed_q8(None, _fake(A1), _fake(A2), 100, 64, 1, None) == NULL
