@@ -51,6 +51,12 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# GPU outputs of each configuration, kept on the host for the CPU-baseline leg,
+# which computes the oracle's results on the same inputs, times them, and
+# reports the largest |y_gpu - y_oracle| / T (T = sum |scale q x| per output).
+GPU_OUT = {}
+
+
 def copies_for(nbytes: int) -> int:
     """Copies of a buffer to rotate through so the set is >= 2x the Infinity Cache."""
     return max(2, -(-2 * MALL_BYTES // nbytes))
@@ -130,36 +136,14 @@ def _cpu_model() -> str:
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "gemv_ssq_verify_17408x5120_pmc.txt")
-KT_FILE = os.path.join(HERE, "profiles", "gemv_ssq_q8_17408x5120_kernel_stats.md")
-# the step's kernels, as rocprofv3 names them (template arguments kept)
-STEP_KERNELS = ("gemv_ssq_split_kernel<5, 2, true, 8>", "verify_keys_kernel")
+KT_FILE = os.path.join(HERE, "profiles", "bench_default_17408x5120_kernel_stats.md")
+# the kernel of the headline step (the fused SSQ twin GEMV; verify_keys_kernel follows it)
+STEP_KERNEL = "gemv_ssq_split_kernel<5, 2, true, 8>"
 KERNEL_SOURCES = ("packed_twin_int8_amd/csrc/pti_gemv.hip", "packed_twin_int8_amd/build.py")
-PROFILE_CMDS = {
-    "kt": "rocprofv3 --kernel-trace --stats -f csv -d rocprof_out/kt -o kt -- python3 bench.py --no-cpu",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d rocprof_out/fetch -o fetch -- "
-             "python3 bench.py --only-main --no-cpu --steps 10 --warmup 2 --copy-calibration",
-    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d rocprof_out/write -o write -- "
-             "python3 bench.py --only-main --no-cpu --steps 10 --warmup 2 --copy-calibration",
-    "summary": "python3 bench.py --summarize-profiles rocprof_out/kt rocprof_out/fetch "
-               "rocprof_out/write --profiles-out profiles",
-    "tcc": "rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum -f csv -d rocprof_out/tcc -o tcc -- "
-           "python3 bench.py --cache-profile --no-cpu",
-    "tcc_summary": "python3 bench.py --summarize-hit-rate rocprof_out/tcc --profiles-out profiles",
+KT_CMDS = {
+    "kt": "rocprofv3 --kernel-trace --stats -f csv -d rocprof_out/bench -o bench -- python3 bench.py --no-cpu",
+    "summary": "python3 bench.py --summarize-kt rocprof_out/bench",
 }
-HIT_FILE = os.path.join(HERE, "profiles", "gemv_l2_hit_rate_17408x5120_pmc.txt")
-# kernels of the cache-profile run, as rocprofv3 names them, and what each one is there
-HIT_KERNELS = {
-    "gemv_ssq_split_kernel<5, 2, true, 8>": "step: fused SSQ twin GEMV (+ verify keys)",
-    "verify_keys_kernel": "step: verify keys",
-    "gemv_ssq_split_kernel<5, 2, false, 8>": "SSQ twin GEMV alone",
-    "gemv_q8_split_kernel<5, 1>": "Q8 GEMV, N = 1",
-    "gemv_q8_split_kernel<5, 2>": "Q8 GEMV, N = 2",
-    "gemv_kernel<0, 4, 4, 2, true, 16, 4>": "Q8 GEMV, N = 4",
-}
-# the Q8 kernel of each stream count at 17408 x 5120 (one and two streams take
-# the row-split kernel there, four the per-wave-row kernel)
-Q8_KERNEL = {1: "gemv_q8_split_kernel<5, 1>", 2: "gemv_q8_split_kernel<5, 2>", 4: "gemv_kernel<0, 4, 4, 2, true, 16, 4>"}
 CALIB_BYTES = 64 * 2**20 * 4  # torch.neg over 64 Mi fp32: reads and writes this many bytes
 
 
@@ -176,45 +160,6 @@ def kernel_source_hash() -> str:
         with open(os.path.join(HERE, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
-
-
-def read_traffic():
-    """HBM bytes per SSQ GEMV launch from the committed PMC summary, or None if
-    there is none or the kernel source changed since the counters were taken."""
-    try:
-        kv = {}
-        with open(TRAFFIC_FILE) as f:
-            for line in f:
-                if ":" in line and not line.startswith((" ", "#", "|")):
-                    k, v = line.split(":", 1)
-                    kv[k.strip()] = v.strip()
-        if kv.get("kernel_source_sha256") != kernel_source_hash():
-            return None
-        return {"bytes": int(kv["traffic_bytes_per_launch"]), "fetch_bytes": int(kv["fetch_bytes_per_launch"]),
-                "write_bytes": int(kv["write_bytes_per_launch"]), "source": os.path.relpath(TRAFFIC_FILE, HERE)}
-    except (OSError, KeyError, ValueError):
-        return None
-
-
-def read_kernel_avgs():
-    """rocprofv3 average duration (us) of each step kernel from the committed
-    kernel-trace summary, or None if it is missing or the source changed."""
-    try:
-        avgs, src = {}, None
-        with open(KT_FILE) as f:
-            for line in f:
-                if line.startswith("kernel_source_sha256:"):
-                    src = line.split(":", 1)[1].strip()
-                elif line.startswith("| "):
-                    cells = [c.strip() for c in line.strip().strip("|").split("|")]
-                    for k in STEP_KERNELS:
-                        if cells[0].endswith(k):
-                            avgs[k] = float(cells[2])
-        if src != kernel_source_hash() or len(avgs) != len(STEP_KERNELS):
-            return None
-        return avgs
-    except (OSError, ValueError, IndexError):
-        return None
 
 
 def _csv_rows(d, suffix):
@@ -241,18 +186,16 @@ def _short(name: str) -> str:
     return name
 
 
-def summarize_profiles(kt_dir, fetch_dir, write_dir, out_dir):
-    """Turn rocprofv3 CSV output into the text summaries kept under profiles/."""
-    src_hash = kernel_source_hash()
+def summarize_kt(kt_dir, out_dir):
+    """The kernel-trace statistics of the default bench run (every kernel it
+    launches, mixed shapes per kernel name) as a text table under profiles/."""
     kt = _csv_rows(kt_dir, "kernel_stats.csv")
-    lines = ["# rocprofv3 kernel-trace statistics: bench.py default run on one MI355X: the fused SSQ twin GEMV",
-             "# 17408x5120 + verify (the step), the unfused GEMV and verify, SSQ with two streams per twin, Q8",
-             "# multi-stream GEMV 17408x5120 at N=1,2,4, a decoder layer's GEMVs (separate, grouped, graph), the",
-             "# toy decoder forward pass, and twin-KV attention at 4K and 32K positions.  A kernel's row mixes",
-             "# every shape it ran; the step's kernels (gemv_ssq_split_kernel<5, 2, true, 8>, verify_keys_kernel)",
-             "# run only in the step.",
-             "", "command: " + PROFILE_CMDS["kt"], "summary: " + PROFILE_CMDS["summary"],
-             "kernel_source_sha256: " + src_hash, "",
+    lines = ["# rocprofv3 kernel-trace statistics of the default bench.py run on one MI355X.  A kernel's row",
+             "# mixes every shape that kernel ran; the headline step's GEMV (" + STEP_KERNEL + ") and",
+             "# verify_keys_kernel run only in the step.  Per-call figures of single kernels are in the",
+             "# gemv_*_isolated.txt profiles.",
+             "", "command: " + KT_CMDS["kt"], "summary: " + KT_CMDS["summary"],
+             "kernel_source_sha256: " + kernel_source_hash(), "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in kt:
         name = _short(r["Name"])
@@ -260,148 +203,400 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, out_dir):
         lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
                      f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.2f} |")
     os.makedirs(out_dir, exist_ok=True)
-    with open(os.path.join(out_dir, "gemv_ssq_q8_17408x5120_kernel_stats.md"), "w") as f:
-        f.write("\n".join(lines) + "\n")
-
-    def per_kernel(d, counter):
-        acc = {}
-        for r in _csv_rows(d, "counter_collection.csv"):
-            if r["Counter_Name"] != counter:
-                continue
-            acc.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
-        return acc
-
-    def pick(acc, key):
-        ks = [k for k in acc if key(k)]
-        if len(ks) != 1:
-            raise SystemExit(f"expected one kernel, found {ks}")
-        v = acc[ks[0]]
-        return ks[0], sum(v) / len(v), len(v)
-
-    out = {}
-    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        acc = per_kernel(d, counter)
-        # the PMC runs launch only the step's kernels (and the calibration copy)
-        steps = [pick(acc, lambda k, sk=sk: k.endswith(sk)) for sk in STEP_KERNELS]
-        cname, c_kib, c_n = pick(acc, lambda k: "neg_kernel" in k or "neg" in k.lower())
-        factor = CALIB_BYTES / 1024.0 / c_kib
-        g_kib = sum(k for _, k, _ in steps)
-        out[counter] = dict(steps=steps, g_kib=g_kib, cname=cname, c_kib=c_kib, c_n=c_n, factor=factor,
-                            bytes=int(round(g_kib * 1024 * factor)))
-    algo = step_algo_bytes()
-    fb, wb = out["FETCH_SIZE"]["bytes"], out["WRITE_SIZE"]["bytes"]
-    lines = ["# HBM traffic of the fused SSQ twin GEMV + verify (17408x5120; both kernels of one call),",
-             "# rocprofv3 PMC counters, one MI355X",
-             "# Each counter is scaled by the ratio of known bytes to the counter's reading for torch.neg",
-             "# over 256 MiB (reads 256 MiB, writes 256 MiB) in the same run.",
-             "", "command_fetch: " + PROFILE_CMDS["fetch"], "command_write: " + PROFILE_CMDS["write"],
-             "summary: " + PROFILE_CMDS["summary"], ""]
-    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-        o = out[counter]
-        lines += [f"| {counter} | kernel | dispatches | avg KiB/dispatch |", "|---|---|---|---|"]
-        lines += [f"| | {n} | {cnt} | {kib:.1f} |" for n, kib, cnt in o["steps"]]
-        lines += [f"| | step total | | {o['g_kib']:.1f} |",
-                  f"| | {o['cname'][:90]} (calibration, {CALIB_BYTES} B) | {o['c_n']} | {o['c_kib']:.1f} |",
-                  f"calibration factor {counter}: {o['factor']:.4f}", ""]
-    lines += [f"algorithmic_bytes_per_launch: {algo}",
-              f"fetch_bytes_per_launch: {fb}", f"write_bytes_per_launch: {wb}",
-              f"traffic_bytes_per_launch: {fb + wb}",
-              f"traffic_over_algorithmic: {(fb + wb) / algo:.4f}",
-              "kernel_source_sha256: " + src_hash]
-    with open(os.path.join(out_dir, os.path.basename(TRAFFIC_FILE)), "w") as f:
+    with open(os.path.join(out_dir, os.path.basename(KT_FILE)), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def summarize_hit_rate(tcc_dir, out_dir):
-    """L2 (TCC) hit rate per kernel of the cache-profile run, from rocprofv3's
-    TCC_HIT_sum and TCC_MISS_sum: the share of L2 requests served without a
-    fetch from the Infinity Fabric (x re-reads hit; streamed weights miss)."""
-    acc = {}
-    for r in _csv_rows(tcc_dir, "counter_collection.csv"):
-        k = _short(r["Kernel_Name"])
-        acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-    lines = ["# L2 (TCC) hit rate per kernel: the fused SSQ step, the SSQ GEMV alone and the Q8 GEMV at",
-             "# N = 1, 2, 4 streams over 17408x5120 (weights rotated over copies larger than the Infinity Cache),",
-             "# rocprofv3 PMC counters TCC_HIT_sum and TCC_MISS_sum, one MI355X.  hit rate = hits / (hits + misses).",
-             "", "command: " + PROFILE_CMDS["tcc"], "summary: " + PROFILE_CMDS["tcc_summary"],
-             "kernel_source_sha256: " + kernel_source_hash(), "",
-             "| kernel | what | dispatches | avg hits | avg misses | hit rate |", "|---|---|---|---|---|---|"]
-    found = 0
-    for name, what in HIT_KERNELS.items():
-        ks = [k for k in acc if k.endswith(name)]
-        if len(ks) != 1:
-            raise SystemExit(f"expected one kernel named {name}, found {ks}")
-        c = acc[ks[0]]
-        h, m = c.get("TCC_HIT_sum", []), c.get("TCC_MISS_sum", [])
-        if not h or len(h) != len(m):
-            raise SystemExit(f"{name}: missing TCC counters")
-        hh, mm = sum(h) / len(h), sum(m) / len(m)
-        lines.append(f"| {name} | {what} | {len(h)} | {hh:.0f} | {mm:.0f} | {hh / max(hh + mm, 1):.4f} |")
-        found += 1
-    os.makedirs(out_dir, exist_ok=True)
-    with open(os.path.join(out_dir, os.path.basename(HIT_FILE)), "w") as f:
-        f.write("\n".join(lines) + "\n")
-    print("\n".join(lines))
-
-
-def read_hit_rates():
-    """{kernel: L2 hit rate} from the committed summary, or None if it is
-    missing or the kernel source changed since the counters were taken."""
+def read_kt_avg(kernel):
+    """Average duration (us) of `kernel` in the committed default-run kernel-trace
+    summary, or None if it is missing or the kernel source changed."""
     try:
-        rates, src = {}, None
-        with open(HIT_FILE) as f:
+        avg, src = None, None
+        with open(KT_FILE) as f:
             for line in f:
                 if line.startswith("kernel_source_sha256:"):
                     src = line.split(":", 1)[1].strip()
-                elif line.startswith("| ") and not line.startswith("| kernel"):
+                elif line.startswith("| "):
                     cells = [c.strip() for c in line.strip().strip("|").split("|")]
-                    rates[cells[0]] = float(cells[5])
-        if src != kernel_source_hash() or set(rates) != set(HIT_KERNELS):
-            return None
-        return rates
+                    if cells[0].endswith(kernel):
+                        avg = float(cells[2])
+        return avg if src == kernel_source_hash() else None
     except (OSError, ValueError, IndexError):
         return None
 
 
-def cache_profile_run(torch, pti, dev, stream):
-    """The kernels of the L2 hit-rate profile, a few launches each: the fused
-    step, the SSQ GEMV alone, and the Q8 GEMV at N = 1, 2, 4 (17408x5120,
-    weights rotated over copies)."""
+# Calls that can be launched alone for a per-kernel profile: name -> (what,
+# kernel name as rocprofv3 reports it, format, streams).  At 17408 x 5120 one
+# and two Q8 streams take the row-split kernel, four the per-wave-row kernel.
+ISOLATED = {
+    "ssq": ("SSQ twin GEMV alone (pti_gemv_ssq)", "gemv_ssq_split_kernel<5, 2, false, 8>", "ssq", 2),
+    "step": ("fused SSQ twin GEMV + greedy verify (pti_gemv_ssq_verify)", "gemv_ssq_split_kernel<5, 2, true, 8>",
+             "ssq", 2),
+    "q8n1": ("Q8 GEMV, N = 1 (pti_gemv_q8_multi)", "gemv_q8_split_kernel<5, 1>", "q8", 1),
+    "q8n2": ("Q8 GEMV, N = 2 (pti_gemv_q8_multi)", "gemv_q8_split_kernel<5, 2>", "q8", 2),
+    "q8n4": ("Q8 GEMV, N = 4 (pti_gemv_q8_multi)", "gemv_kernel<0, 4, 4, 2, true, 16, 4>", "q8", 4),
+}
+ISOLATED_CALLS = 60
+SQ_COUNTERS = ("SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU",
+               "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT")
+
+
+def isolated_cmds(name):
+    base = f"python3 bench.py --only {name} --no-cpu --copy-calibration"
+    d = f"rocprof_out/{name}"
+    return {
+        "kt": f"rocprofv3 --kernel-trace --stats -f csv -d {d}/kt -o kt -- {base}",
+        "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/fetch -o fetch -- {base}",
+        "write": f"rocprofv3 --pmc WRITE_SIZE TCC_HIT_sum TCC_MISS_sum -f csv -d {d}/write -o write -- {base}",
+        "sq": f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} GRBM_GUI_ACTIVE -f csv -d {d}/sq -o sq -- {base}",
+        "summary": f"python3 bench.py --summarize-isolated {name} {d}/kt {d}/fetch {d}/write {d}/write {d}/sq",
+    }
+
+
+def isolated_profile_path(name):
+    return os.path.join(HERE, "profiles", f"gemv_{name}_17408x5120_isolated.txt")
+
+
+def isolated_run(torch, pti, dev, stream, name, calibrate):
+    """ISOLATED_CALLS launches of one call over 17408 x 5120 (weights rotated over
+    copies past the Infinity Cache), after the calibration copies if asked."""
     import synth
     L, sp = pti.lib(), pti._stream(stream)
-    d = synth.twin(ROWS, COLS, synth.SEED_SSQ_FFN)
-    P = pti.pack_ssq(d["A"], d["B"], d["sA"], d["sB"])
-    n = copies_for(P.nbytes)
+    what, kernel, fmt, n = ISOLATED[name]
+    if calibrate:
+        src = torch.ones(64 * 2**20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    if fmt == "ssq":
+        d = synth.twin(ROWS, COLS, synth.SEED_SSQ_FFN)
+        P = pti.pack_ssq(d["A"], d["B"], d["sA"], d["sB"])
+        X = np.stack([d["xA"], d["xB"]])
+    else:
+        d = synth.q8(ROWS, COLS, n, synth.SEED_Q8_FFN)
+        P = pti.pack_q8(d["Q"], d["S"])
+        X = d["X"]
+    nc = copies_for(P.nbytes)
     w0 = torch.from_numpy(P).to(dev)
-    ws = [w0] + [w0.clone() for _ in range(n - 1)]
-    xa, xb = torch.from_numpy(d["xA"]).to(dev), torch.from_numpy(d["xB"]).to(dev)
-    y2 = torch.empty((2, ROWS), dtype=torch.float32, device=dev)
+    ws = [w0] + [w0.clone() for _ in range(nc - 1)]
+    x = torch.from_numpy(np.ascontiguousarray(X)).to(dev)
+    y = torch.empty((max(n, 2), ROWS), dtype=torch.float32, device=dev)
     tok = torch.zeros(2, dtype=torch.int32, device=dev)
     am = torch.empty(2, dtype=torch.int32, device=dev)
     acc = torch.empty(1, dtype=torch.int32, device=dev)
     work = pti.ssq_verify_workspace(dev)
-    for i in range(12):
-        pti._check("pti_gemv_ssq_verify", L.pti_gemv_ssq_verify(
-            ws[i % n].data_ptr(), xa.data_ptr(), xb.data_ptr(), y2[0].data_ptr(), y2[1].data_ptr(), ROWS, COLS,
-            tok.data_ptr(), am.data_ptr(), acc.data_ptr(), work.data_ptr(), work.numel(), sp))
-        pti._check("pti_gemv_ssq", L.pti_gemv_ssq(ws[i % n].data_ptr(), xa.data_ptr(), xb.data_ptr(),
-                                                  y2[0].data_ptr(), y2[1].data_ptr(), ROWS, COLS, sp))
+    for i in range(ISOLATED_CALLS):
+        w = ws[i % nc].data_ptr()
+        if name == "ssq":
+            st = L.pti_gemv_ssq(w, x[0].data_ptr(), x[1].data_ptr(), y[0].data_ptr(), y[1].data_ptr(), ROWS, COLS, sp)
+        elif name == "step":
+            st = L.pti_gemv_ssq_verify(w, x[0].data_ptr(), x[1].data_ptr(), y[0].data_ptr(), y[1].data_ptr(), ROWS,
+                                       COLS, tok.data_ptr(), am.data_ptr(), acc.data_ptr(), work.data_ptr(),
+                                       work.numel(), sp)
+        else:
+            st = L.pti_gemv_q8_multi(w, x.data_ptr(), y.data_ptr(), ROWS, COLS, n, sp)
+        pti._check(name, st)
     torch.cuda.synchronize()
-    del ws, w0
-    q = synth.q8(ROWS, COLS, 4, synth.SEED_Q8_FFN)
-    Pq = pti.pack_q8(q["Q"], q["S"])
-    nq = copies_for(Pq.nbytes)
-    wq0 = torch.from_numpy(Pq).to(dev)
-    wqs = [wq0] + [wq0.clone() for _ in range(nq - 1)]
-    X = torch.from_numpy(q["X"]).to(dev)
-    Y = torch.empty((4, ROWS), dtype=torch.float32, device=dev)
-    for ns in (1, 2, 4):
-        for i in range(12):
-            pti._check("pti_gemv_q8_multi", L.pti_gemv_q8_multi(wqs[i % nq].data_ptr(), X.data_ptr(), Y.data_ptr(),
-                                                                 ROWS, COLS, ns, sp))
+    log(f"isolated {name}: {ISOLATED_CALLS} launches of {what}, {nc} weight copies of {P.nbytes} B")
+
+
+def isolated_algo_bytes(name):
+    _, _, fmt, n = ISOLATED[name]
+    w = ROWS * (COLS // 32) * (68 if fmt == "ssq" else 34)
+    extra = 20 if name == "step" else 0  # guess tokens, argmaxes, accept count
+    return w + n * (COLS + ROWS) * 4 + extra
+
+
+def summarize_isolated(name, kt_dir, fetch_dir, write_dir, tcc_dir, sq_dir, out_dir):
+    """One call's profile from its --only runs: per-launch kernel time from the
+    trace (for the fused step, also the span from the GEMV's start to the
+    verify kernel's end), HBM traffic (FETCH_SIZE, WRITE_SIZE scaled by the
+    counters' reading for torch.neg over 256 MiB in the same run), the L2 hit
+    rate, and SQ counters."""
+    what, kernel, fmt, n = ISOLATED[name]
+    cmds = isolated_cmds(name)
+    trace = _csv_rows(kt_dir, "kernel_trace.csv")
+    disp = [r for r in trace if _short(r["Kernel_Name"]).endswith(kernel)]
+    if len(disp) != ISOLATED_CALLS:
+        raise SystemExit(f"{name}: expected {ISOLATED_CALLS} dispatches of {kernel}, found {len(disp)}")
+    dur = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in disp[10:])
+    med = dur[len(dur) // 2]
+    avg = sum(dur) / len(dur)
+    span = None
+    if name == "step":
+        # the call: the GEMV's start to the verify kernel's end, dispatch by dispatch
+        rows = sorted(trace, key=lambda r: int(r["Start_Timestamp"]))
+        spans = []
+        for i, r in enumerate(rows):
+            if _short(r["Kernel_Name"]).endswith(kernel) and i + 1 < len(rows) and \
+                    _short(rows[i + 1]["Kernel_Name"]).endswith("verify_keys_kernel"):
+                spans.append((int(rows[i + 1]["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        spans = sorted(spans[10:])
+        span = (spans[len(spans) // 2], sum(spans) / len(spans))
+
+    def per_kernel(d, counter):
+        acc = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] == counter:
+                acc.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return acc
+
+    def kern_avg(acc, key):
+        ks = [k for k in acc if key(k)]
+        if len(ks) != 1:
+            raise SystemExit(f"{name}: expected one kernel, found {ks}")
+        v = acc[ks[0]]
+        return sum(v) / len(v), len(v)
+
+    algo = isolated_algo_bytes(name)
+    traffic = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        acc = per_kernel(d, counter)
+        k_kib, k_n = kern_avg(acc, lambda k: k.endswith(kernel))
+        c_kib, _ = kern_avg(acc, lambda k: "neg" in k.lower())
+        factor = CALIB_BYTES / 1024.0 / c_kib
+        traffic[counter] = (k_kib, k_n, factor, int(round(k_kib * 1024 * factor)))
+    hits = per_kernel(tcc_dir, "TCC_HIT_sum")
+    miss = per_kernel(tcc_dir, "TCC_MISS_sum")
+    h, _ = kern_avg(hits, lambda k: k.endswith(kernel))
+    m, _ = kern_avg(miss, lambda k: k.endswith(kernel))
+    sq = {}
+    for c in SQ_COUNTERS + ("GRBM_GUI_ACTIVE",):
+        sq[c] = kern_avg(per_kernel(sq_dir, c), lambda k: k.endswith(kernel))[0]
+    fb, wb = traffic["FETCH_SIZE"][3], traffic["WRITE_SIZE"][3]
+    lines = [f"# Isolated profile: {what}, 17408x5120, one MI355X.",
+             f"# {ISOLATED_CALLS} launches, weights rotated over copies past the 256 MB Infinity Cache; durations",
+             "# are per dispatch from the kernel trace (the first 10 dispatches left out); FETCH_SIZE and WRITE_SIZE",
+             "# are scaled by their reading for torch.neg over 256 MiB (reads and writes 256 MiB) in the same run.",
+             ""] + [f"command_{k}: {v}" for k, v in cmds.items()] + [
+             "kernel_source_sha256: " + kernel_source_hash(), "",
+             f"kernel: {kernel}",
+             f"dispatches: {len(disp)}",
+             f"duration_us_median: {med:.3f}", f"duration_us_mean: {avg:.3f}",
+             f"duration_us_min: {dur[0]:.3f}", f"duration_us_max: {dur[-1]:.3f}"]
+    if span:
+        lines += [f"call_span_us_median: {span[0]:.3f}  (GEMV start to verify_keys_kernel end)",
+                  f"call_span_us_mean: {span[1]:.3f}"]
+    lines += [f"algorithmic_bytes_per_launch: {algo}",
+              f"algorithmic_GBps_at_median: {algo / (med * 1e-6) / 1e9:.1f}",
+              f"frac_of_8TBps_at_median: {algo / (med * 1e-6) / 1e9 / HBM_PEAK_GBS:.4f}"]
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        k_kib, k_n, factor, b = traffic[counter]
+        lines.append(f"{counter.lower()}_kib_per_dispatch: {k_kib:.1f} (x {factor:.4f} calibration = {b} B)")
+    lines += [f"fetch_bytes_per_launch: {fb}", f"write_bytes_per_launch: {wb}",
+              f"traffic_bytes_per_launch: {fb + wb}", f"traffic_over_algorithmic: {(fb + wb) / algo:.4f}",
+              f"l2_hits: {h:.0f}", f"l2_misses: {m:.0f}", f"l2_hit_rate: {h / max(h + m, 1):.4f}"]
+    for c, v in sq.items():
+        lines.append(f"{c.lower()}: {v:.0f}")
+    # derived.  A wave64 VALU instruction occupies its SIMD for 4 cycles; the
+    # chip has 256 CUs x 4 SIMDs at 2.4 GHz (nominal).  Per weight: lane
+    # operations over the weights one launch reads.
+    weights = ROWS * COLS * (2 if fmt == "ssq" else 1)
+    simd_cycles = 1024 * med * 1e-6 * 2.4e9
+    lines += [f"valu_lane_ops_per_weight: {sq['SQ_INSTS_VALU'] * 64 / weights:.3f}",
+              f"valu_busy_frac: {sq['SQ_INSTS_VALU'] * 4 / simd_cycles:.4f}  (VALU issue cycles / SIMD cycles at "
+              f"the median duration and 2.4 GHz)",
+              f"lds_busy_frac: {sq['SQ_INSTS_LDS'] * 64 * 16 / (256 * 128 * med * 1e-6 * 2.4e9):.4f}  (upper bound: "
+              f"16 B per lane per LDS instruction at 128 B per CU-cycle)",
+              f"lds_insts_per_valu_inst: {sq['SQ_INSTS_LDS'] / max(sq['SQ_INSTS_VALU'], 1):.4f}"]
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, os.path.basename(isolated_profile_path(name)))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def read_isolated(name):
+    """{field: value} of a committed isolated profile, or None if it is missing
+    or the kernel source changed since it was taken."""
+    try:
+        kv = {}
+        with open(isolated_profile_path(name)) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        return kv
+    except OSError:
+        return None
+
+
+def isolated_roofline(name, algo_bytes, us):
+    """roofline block of a per-kernel entry: this run's time against 8 TB/s, with
+    the kernel's trace duration, HBM traffic and L2 hit rate from its committed
+    isolated profile (null when that profile is missing or stale)."""
+    kv = read_isolated(name) or {}
+    out = {"bound": "hbm", "achieved": round(algo_bytes / (us * 1e-6) / 1e9, 2), "peak": HBM_PEAK_GBS,
+           "unit": "GB/s", "frac": round(algo_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "algorithmic_bytes_per_launch": algo_bytes,
+           "traffic": int(kv["traffic_bytes_per_launch"]) if kv else None,
+           "fetch_bytes": int(kv["fetch_bytes_per_launch"]) if kv else None,
+           "rocprof_median_us": float(kv["duration_us_median"]) if kv else None,
+           "l2_hit_rate": float(kv["l2_hit_rate"]) if kv else None,
+           "profile": os.path.relpath(isolated_profile_path(name), HERE)}
+    if kv:
+        out["valu_busy_frac"] = float(kv["valu_busy_frac"].split()[0])
+        out["valu_lane_ops_per_weight"] = float(kv["valu_lane_ops_per_weight"])
+    return out
+
+
+def tiny_twin(torch, pti, dev, stream):
+    """The tiny SSQ twin workload (256 x 512, seed 0): latency-bound, timed for
+    completeness; its outputs go to the parity check of the CPU leg."""
+    import synth
+    d = synth.twin(256, 512, synth.SEED_TINY)
+    w = torch.from_numpy(pti.pack_ssq(d["A"], d["B"], d["sA"], d["sB"])).to(dev)
+    xa, xb = torch.from_numpy(d["xA"]).to(dev), torch.from_numpy(d["xB"]).to(dev)
+    y = torch.empty((2, 256), device=dev)
+    L, sp = pti.lib(), pti._stream(stream)
+    st = timed_stats(torch, lambda i: pti._check("pti_gemv_ssq", L.pti_gemv_ssq(
+        w.data_ptr(), xa.data_ptr(), xb.data_ptr(), y[0].data_ptr(), y[1].data_ptr(), 256, 512, sp)), stream,
+        reps=5, per_rep=200)
     torch.cuda.synchronize()
-    log("cache profile: 12 launches of each kernel")
+    GPU_OUT["config1"] = (y[0].cpu().numpy().copy(), y[1].cpu().numpy().copy())
+    return {"ssq_twin_256x512": {**st, "weight_bytes": int(w.numel())}}
+
+
+def layer_sweep(torch, pti, dev, stream):
+    """Every decoder-layer matrix (q, k, v, o 5120 wide; gate, up 17408 x 5120;
+    down 5120 x 17408) from the seeded generator (seed 4): SSQ with distinct
+    twins, SSQ with A == B, and Q8 (twin A's matrix) at N = 1, 2, 4 streams.
+    Each matrix rotates over copies totalling at least 512 MB, so every launch
+    reads its weights from HBM."""
+    import synth
+    L, sp = pti.lib(), pti._stream(stream)
+    out = {}
+    for name, rows, cols in synth.LAYER_SHAPES:
+        twins = {"ssq": synth.twin(rows, cols, synth.SEED_LAYER),
+                 "ssq_same": synth.twin(rows, cols, synth.SEED_LAYER, same=True)}
+        twins["q8"] = twins["ssq"]  # Q8 runs twin A's matrix
+        for variant in ("ssq", "ssq_same", "q8"):
+            d = twins[variant]
+            if variant == "q8":
+                P = pti.pack_q8(d["A"], d["sA"])
+                X = np.stack([d["xA"], d["xB"], -d["xA"], 0.5 * d["xB"]])
+            else:
+                P = pti.pack_ssq(d["A"], d["B"], d["sA"], d["sB"])
+                X = np.stack([d["xA"], d["xB"]])
+            nc = copies_for(P.nbytes)
+            w0 = torch.from_numpy(P).to(dev)
+            ws = [w0] + [w0.clone() for _ in range(nc - 1)]
+            x = torch.from_numpy(np.ascontiguousarray(X)).to(dev)
+            y = torch.empty((4, rows), device=dev)
+            for n in ((2,) if variant != "q8" else (1, 2, 4)):
+                if variant == "q8":
+                    fn = lambda i, n=n: pti._check("pti_gemv_q8_multi", L.pti_gemv_q8_multi(
+                        ws[i % nc].data_ptr(), x.data_ptr(), y.data_ptr(), rows, cols, n, sp))
+                else:
+                    fn = lambda i: pti._check("pti_gemv_ssq", L.pti_gemv_ssq(
+                        ws[i % nc].data_ptr(), x[0].data_ptr(), x[1].data_ptr(), y[0].data_ptr(), y[1].data_ptr(),
+                        rows, cols, sp))
+                st = timed_stats(torch, fn, stream, reps=5, per_rep=100, warmup=20)
+                torch.cuda.synchronize()
+                key = f"layer_{name}_{variant}" + (f"_n{n}" if variant == "q8" else "")
+                GPU_OUT[key] = y[:n].cpu().numpy().copy()
+                us = st["median_us"]
+                algo = P.nbytes + n * (rows + cols) * 4
+                out[key] = {**st, "rows": rows, "cols": cols, "weight_bytes": int(P.nbytes), "rotated_copies": nc,
+                            "weight_GBps": round(P.nbytes / (us * 1e-6) / 1e9, 1),
+                            "frac_of_hbm_peak": round(algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                            "outputs_per_s": round(n * rows / (us * 1e-6), 1)}
+            del ws, w0
+            torch.cuda.empty_cache()
+        log(f"layer {name}: " + ", ".join(f"{k[len('layer_' + name) + 1:]} {v['median_us']} us"
+                                          for k, v in out.items() if k.startswith(f"layer_{name}_")))
+    return out
+
+
+def _median_time(fn, reps=3):
+    ts = []
+    res = None
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        res = fn()
+        ts.append(time.perf_counter() - t0)
+    return sorted(ts)[len(ts) // 2], res
+
+
+def _ratio(got, want, t):
+    got = np.asarray(got, np.float64)
+    return float(np.max(np.abs(got - want) / np.maximum(t, 1e-300)))
+
+
+def oracle_per_config():
+    """The oracle (scalar C, one host thread) on each configuration the GPU ran,
+    the median of 3 runs (one run of the toy decode loop), with the largest
+    |y_gpu - y_oracle| / T over every output the GPU produced for it."""
+    import oracle
+    import synth
+    from oracle import scalar, toy
+    res = {}
+    if "config1" in GPU_OUT:
+        d = synth.twin(256, 512, synth.SEED_TINY)
+        P = oracle.pack_ssq(d["A"], d["B"], d["sA"], d["sB"])
+        t, (ya, yb, ta, tb) = _median_time(lambda: oracle.gemv_ssq(P, 256, 512, d["xA"], d["xB"]))
+        tp, _ = _median_time(lambda: scalar.gemv_ssq(P.tobytes(), 256, 512, d["xA"], d["xB"]))
+        ga, gb = GPU_OUT["config1"]
+        res["config1_ssq_twin_256x512"] = {"oracle_s": round(t, 5), "pure_python_s": round(tp, 3),
+                                           "parity_max_err_over_T": max(_ratio(ga, ya, ta), _ratio(gb, yb, tb))}
+    if "config2" in GPU_OUT:
+        d = synth.twin(ROWS, COLS, synth.SEED_SSQ_FFN)
+        P = oracle.pack_ssq(d["A"], d["B"], d["sA"], d["sB"])
+        t, (ya, yb, ta, tb) = _median_time(lambda: oracle.gemv_ssq(P, ROWS, COLS, d["xA"], d["xB"]))
+        ga, gb = GPU_OUT["config2"]
+        res["config2_ssq_twin_17408x5120"] = {"oracle_s": round(t, 4),
+                                              "parity_max_err_over_T": max(_ratio(ga, ya, ta), _ratio(gb, yb, tb))}
+    if "config3_n4" in GPU_OUT:
+        q = synth.q8(ROWS, COLS, 4, synth.SEED_Q8_FFN)
+        P = oracle.pack_q8(q["Q"], q["S"])
+        for n in (1, 2, 4):
+            t, (y, tt) = _median_time(lambda n=n: oracle.gemv_q8(P, ROWS, COLS, q["X"][:n]))
+            res[f"config3_q8_17408x5120_n{n}"] = {"oracle_s": round(t, 4), "parity_max_err_over_T": max(
+                _ratio(GPU_OUT[f"config3_n{n}"][s], y[s], tt[s]) for s in range(n))}
+    for name, rows, cols in synth.LAYER_SHAPES:
+        if f"layer_{name}_ssq" not in GPU_OUT:
+            continue
+        entry = {}
+        twins = {"ssq": synth.twin(rows, cols, synth.SEED_LAYER),
+                 "ssq_same": synth.twin(rows, cols, synth.SEED_LAYER, same=True)}
+        twins["q8"] = twins["ssq"]
+        for variant in ("ssq", "ssq_same", "q8"):
+            d = twins[variant]
+            if variant == "q8":
+                P = oracle.pack_q8(d["A"], d["sA"])
+                X = np.stack([d["xA"], d["xB"], -d["xA"], 0.5 * d["xB"]])
+                t, (y, tt) = _median_time(lambda: oracle.gemv_q8(P, rows, cols, X))
+                r = max(_ratio(GPU_OUT[f"layer_{name}_q8_n{n}"][s], y[s], tt[s]) for n in (1, 2, 4) for s in range(n))
+            else:
+                P = oracle.pack_ssq(d["A"], d["B"], d["sA"], d["sB"])
+                t, (ya, yb, ta, tb) = _median_time(lambda: oracle.gemv_ssq(P, rows, cols, d["xA"], d["xB"]))
+                g = GPU_OUT[f"layer_{name}_{variant}"]
+                r = max(_ratio(g[0], ya, ta), _ratio(g[1], yb, tb))
+            entry[variant] = {"oracle_s": round(t, 4), "parity_max_err_over_T": r}
+        res[f"config4_layer_{name}_{rows}x{cols}"] = {
+            **entry, "parity_max_err_over_T": max(v["parity_max_err_over_T"] for v in entry.values())}
+    if "config5_n4" in GPU_OUT:
+        raw = synth.toy_weights(synth.SEED_TOY)
+        t0 = time.perf_counter()
+        model = toy.ToyModel(raw, 1e-6)
+        t_build = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        committed, accepts, passes = toy.systolic_decode(
+            lambda k, s, i, tok: toy.argmax_first(model.logits([tok])[0]), 1, 4, 64)
+        t_loop = time.perf_counter() - t0
+        gpu = GPU_OUT["config5_n4"].tolist()
+        agree = sum(int(a == b) for a, b in zip(gpu, committed))
+        res["config5_toy_decode_q8_n4_64steps"] = {
+            "oracle_model_build_s": round(t_build, 2), "oracle_loop_s": round(t_loop, 2),
+            "oracle_passes": len(passes), "oracle_mean_accept": round(float(np.mean(accepts)), 3),
+            "committed_tokens_equal_to_gpu": f"{agree}/{len(committed)}", "parity_max_err_over_T": None}
+    log(f"oracle per config: {json.dumps(res)}")
+    return res
 
 
 def layer_and_graph(torch, pti, dev, stream):
@@ -509,6 +704,7 @@ def layer_and_graph(torch, pti, dev, stream):
         # passes rows are (step, slot, stream, input, output): an N-stream pass
         # has slots 0..N-1, a single-stream (ramp-up or redraw) pass a slot >= N
         fwd = 64 + int((passes[:, 1] >= n).sum()) if n > 1 else 64
+        GPU_OUT[f"config5_n{n}"] = np.asarray(committed).copy()
         out[f"toy_decode_q8_n{n}_64steps"] = {
             "ms": round(t * 1e3, 3), "forward_passes": fwd, "us_per_step": round(t / 64 * 1e6, 2),
             "us_per_forward_pass": round(t / fwd * 1e6, 2),
@@ -599,22 +795,25 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-main", action="store_true",
-                    help="time the fused SSQ step only, no other kernels (profiling runs)")
+                    help="time the fused SSQ step only, no other kernels")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run 3 elementwise copies of 256 MiB (reference kernel for HBM byte counters)")
-    ap.add_argument("--summarize-profiles", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="write the profiles/ summaries from rocprofv3 CSV output (CPU only) and exit")
-    ap.add_argument("--cache-profile", action="store_true",
-                    help="run only the kernels of the L2 hit-rate profile (a few launches each) and exit")
-    ap.add_argument("--summarize-hit-rate", metavar="TCC_DIR",
-                    help="write the L2 hit-rate summary from rocprofv3 CSV output (CPU only) and exit")
+                    help="with --only: first run 3 elementwise copies of 256 MiB (reference kernel for HBM byte "
+                         "counters)")
+    ap.add_argument("--summarize-kt", metavar="KT_DIR",
+                    help="write the default run's kernel-trace summary from rocprofv3 CSV output (CPU only) and exit")
     ap.add_argument("--profiles-out", default=os.path.join(HERE, "profiles"))
+    ap.add_argument("--only", choices=sorted(ISOLATED),
+                    help="launch only this call (a few times, weights rotated) and exit: the runs behind the "
+                         "per-kernel profiles")
+    ap.add_argument("--summarize-isolated", nargs=6, metavar=("NAME", "KT_DIR", "FETCH_DIR", "WRITE_DIR", "TCC_DIR",
+                                                              "SQ_DIR"),
+                    help="write profiles/<summary of NAME> from the rocprofv3 output of its --only runs (CPU only)")
     args = ap.parse_args()
-    if args.summarize_profiles:
-        summarize_profiles(*args.summarize_profiles, args.profiles_out)
+    if args.summarize_isolated:
+        summarize_isolated(*args.summarize_isolated, args.profiles_out)
         return
-    if args.summarize_hit_rate:
-        summarize_hit_rate(args.summarize_hit_rate, args.profiles_out)
+    if args.summarize_kt:
+        summarize_kt(args.summarize_kt, args.profiles_out)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; run with --gpus 1", file=sys.stderr)
@@ -628,8 +827,8 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     log(f"device {torch.cuda.get_device_name(0)}")
-    if args.cache_profile:
-        cache_profile_run(torch, pti, dev, stream)
+    if args.only:
+        isolated_run(torch, pti, dev, stream, args.only, args.copy_calibration)
         return
 
     # ---------------- inputs: SSQ twin workload, seed 2
@@ -670,15 +869,6 @@ def main():
         if st:
             pti._check("pti_gemv_ssq_verify", st)
 
-    if args.copy_calibration:
-        # torch.neg: an elementwise kernel that reads and writes 256 MiB each
-        src = torch.ones(64 * 2**20, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        log(f"copy calibration: 3 x torch.neg over {src.numel() * 4} bytes")
-        del src, dst
     log(f"ssq twin {ROWS}x{COLS}: {w_bytes} weight bytes, {n_copies} copies rotated")
     for i in range(args.warmup):
         step(i)
@@ -691,6 +881,8 @@ def main():
     st_fused = timed_stats(torch, step, stream)
     ms_fused = st_fused["median_us"] * 1e-3
     log(f"fused gemv+verify: {st_fused}")
+    torch.cuda.synchronize()
+    GPU_OUT["config2"] = (ya.cpu().numpy().copy(), yb.cpu().numpy().copy())
     per_kernel = {}
     copy_GBps = None
     if not args.only_main:
@@ -698,10 +890,10 @@ def main():
         st_verify = timed_stats(torch, verify, stream)
         ms_gemv = st_gemv["median_us"] * 1e-3
         log(f"unfused: ssq gemv alone {st_gemv}; verify alone {st_verify}")
-        hr = read_hit_rates()
         per_kernel["ssq_twin_gemv_unfused"] = {**st_gemv,
                                                "weight_GBps": round(w_bytes / (ms_gemv * 1e-3) / 1e9, 2),
-                                               "l2_hit_rate": hr["gemv_ssq_split_kernel<5, 2, false, 8>"] if hr else None}
+                                               "roofline": isolated_roofline("ssq", isolated_algo_bytes("ssq"),
+                                                                             st_gemv["median_us"])}
         per_kernel["verify_n2_v17408_unfused"] = st_verify
         # two streams per twin: four activation vectors per weight read
         xa2 = torch.randn((2, COLS), device=dev)
@@ -728,8 +920,7 @@ def main():
         del dsts
         log(f"copy {w_bytes} B: {st_copy}, {copy_GBps:.0f} GB/s read+write")
 
-    traffic = read_traffic()
-    hit_rates = read_hit_rates()
+    prof = read_isolated("step") or {}
     result = {
         "metric": METRIC,
         "value": round(w_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -758,16 +949,20 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(algo_bytes / (ms_fused * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": traffic["bytes"] if traffic else None,
+            "traffic": int(prof["traffic_bytes_per_launch"]) if prof else None,
             "algorithmic_bytes_per_launch": algo_bytes,
             "avg_launch_us": round(ms_fused * 1e3, 3),
             "launch_us_stats": st_fused,
-            "traffic_source": traffic["source"] if traffic else None,
             "vs_copy": round(algo_bytes / (ms_fused * 1e-3) / 1e9 / copy_GBps, 4) if copy_GBps else None,
-            "rocprof_avg_us": read_kernel_avgs(),
-            "rocprof_source": os.path.relpath(KT_FILE, HERE),
-            "l2_hit_rate": ({k: hit_rates[k] for k in STEP_KERNELS} if hit_rates else None),
-            "l2_hit_rate_source": os.path.relpath(HIT_FILE, HERE),
+            # from the committed isolated profile of this call (null if missing or stale): the GEMV
+            # kernel's trace duration, and the call's span from the GEMV's start to the verify
+            # kernel's end, per dispatch, medians
+            "rocprof_gemv_kernel_us": float(prof["duration_us_median"]) if prof else None,
+            "rocprof_call_span_us": float(prof["call_span_us_median"].split()[0]) if prof else None,
+            "rocprof_default_run_gemv_avg_us": read_kt_avg(STEP_KERNEL),
+            "l2_hit_rate": float(prof["l2_hit_rate"]) if prof else None,
+            "profile": os.path.relpath(isolated_profile_path("step"), HERE),
+            "kernel_stats": os.path.relpath(KT_FILE, HERE),
         },
     }
     if copy_GBps:
@@ -793,18 +988,22 @@ def main():
             stn = timed_stats(torch, qgemv, stream)
             t[n] = stn["median_us"] * 1e-3
             algo = Pq.nbytes + n * (COLS + ROWS) * 4
+            torch.cuda.synchronize()
+            GPU_OUT[f"config3_n{n}"] = Y[:n].cpu().numpy().copy()
             per_kernel[f"q8_gemv_n{n}"] = {
                 "us": round(t[n] * 1e3, 3), **stn,
                 "weight_GBps": round(Pq.nbytes / (t[n] * 1e-3) / 1e9, 2),
                 "frac_of_hbm_peak": round(algo / (t[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "gemv_per_s": round(1 / (t[n] * 1e-3), 1),
                 "outputs_per_s": round(n * ROWS / (t[n] * 1e-3), 1),
-                "l2_hit_rate": (hr or {}).get(Q8_KERNEL[n]),
+                "roofline": isolated_roofline(f"q8n{n}", algo, t[n] * 1e3),
             }
             log(f"q8 n={n}: {t[n] * 1e3:.2f} us, {Pq.nbytes / (t[n] * 1e-3) / 1e9:.1f} GB/s")
         per_kernel["q8_step_cost_n4_over_n1"] = round(t[4] / t[1], 4)
         del wqs, wq0
         torch.cuda.empty_cache()
+        per_kernel.update(tiny_twin(torch, pti, dev, stream))
+        per_kernel.update(layer_sweep(torch, pti, dev, stream))
         per_kernel.update(layer_and_graph(torch, pti, dev, stream))
         per_kernel.update(attention(torch, pti, dev, stream))
         per_kernel.update(verify_and_pack(torch, pti, dev, stream, d))
@@ -813,6 +1012,11 @@ def main():
     if not args.no_cpu:
         log("cpu baseline (oracle)...")
         result["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
+        if not args.only_main:
+            result["cpu_baseline"]["per_config"] = oracle_per_config()
+            result["parity_max_err_over_T"] = max(
+                v["parity_max_err_over_T"] for v in result["cpu_baseline"]["per_config"].values()
+                if v.get("parity_max_err_over_T") is not None)
     print(json.dumps(result), flush=True)
 
 

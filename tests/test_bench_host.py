@@ -1,5 +1,6 @@
 """Host-side checks of bench.py: the one-GPU guard and the rocprofv3 summary
-parsing (fake CSV output in the layout rocprofv3 writes)."""
+parsing (fake CSV output in the layout rocprofv3 writes), and the staleness
+rule that drops a profile taken from other kernel sources."""
 
 import csv
 import os
@@ -34,72 +35,84 @@ KEYS = "void (anonymous namespace)::verify_keys_kernel(unsigned long long const*
 NEG = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>(int, float*)"
 
 
-def test_summarize_profiles(tmp_path, monkeypatch):
-    kt, fe, wr, out = (str(tmp_path / n) for n in ("kt", "fetch", "write", "out"))
+def _isolated_dirs(tmp_path, name, kernel, dur_ns, fetch_kib, write_kib, hits, misses, valu):
+    kt, fe, wr, sq = (str(tmp_path / name / n) for n in ("kt", "fetch", "write", "sq"))
+    tr_hdr = ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+    rows, t = [], 1000
+    for _ in range(bench.ISOLATED_CALLS):
+        rows.append(["KERNEL_DISPATCH", kernel, t, t + dur_ns])
+        if name == "step":
+            rows.append(["KERNEL_DISPATCH", KEYS, t + dur_ns + 500, t + dur_ns + 2500])
+        t += 100000
+    _write_csv(os.path.join(kt, "box", "kt_kernel_trace.csv"), tr_hdr, rows)
+    hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    calib_kib = bench.CALIB_BYTES / 1024 / 2.0  # the counter reads half the true bytes
+    _write_csv(os.path.join(fe, "box", "f_counter_collection.csv"), hdr,
+               [[kernel, "FETCH_SIZE", fetch_kib], [kernel, "FETCH_SIZE", fetch_kib + 2], [NEG, "FETCH_SIZE", calib_kib]])
+    _write_csv(os.path.join(wr, "box", "w_counter_collection.csv"), hdr,
+               [[kernel, "WRITE_SIZE", write_kib], [NEG, "WRITE_SIZE", calib_kib],
+                [kernel, "TCC_HIT_sum", hits], [kernel, "TCC_MISS_sum", misses]])
+    _write_csv(os.path.join(sq, "box", "s_counter_collection.csv"), hdr,
+               [[kernel, c, valu if c == "SQ_INSTS_VALU" else 1000.0]
+                for c in bench.SQ_COUNTERS + ("GRBM_GUI_ACTIVE",)])
+    return kt, fe, wr, sq
+
+
+@pytest.mark.parametrize("name", ["q8n1", "step"])
+def test_summarize_isolated(tmp_path, monkeypatch, name):
+    kernel = "void (anonymous namespace)::" + bench.ISOLATED[name][1] + "(SplitArgs)"
+    kt, fe, wr, sq = _isolated_dirs(tmp_path, name, kernel, 20000, 1000.0, 100.0, 25.0, 75.0, 3.2e6)
+    out = str(tmp_path / "out")
+    bench.summarize_isolated(name, kt, fe, wr, wr, sq, out)
+    monkeypatch.setattr(bench, "isolated_profile_path", lambda n: os.path.join(out, f"gemv_{n}_17408x5120_isolated.txt"))
+    kv = bench.read_isolated(name)
+    assert kv is not None
+    assert float(kv["duration_us_median"]) == 20.0
+    # (1000 + 1002) / 2 KiB fetched, 100 KiB written, each times the calibration factor 2
+    assert int(kv["fetch_bytes_per_launch"]) == round(1001.0 * 1024 * 2)
+    assert int(kv["write_bytes_per_launch"]) == round(100.0 * 1024 * 2)
+    assert float(kv["l2_hit_rate"]) == 0.25
+    weights = bench.ROWS * bench.COLS * (2 if name == "step" else 1)
+    assert abs(float(kv["valu_lane_ops_per_weight"]) - 3.2e6 * 64 / weights) < 1e-3
+    if name == "step":  # GEMV start to verify end: 20 + 0.5 + 2 us
+        assert float(kv["call_span_us_median"].split()[0]) == 22.5
+    r = bench.isolated_roofline(name, bench.isolated_algo_bytes(name), 25.0)
+    assert r["traffic"] == int(kv["traffic_bytes_per_launch"]) and r["rocprof_median_us"] == 20.0
+    # a profile taken from other kernel sources is not used
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
+    assert bench.read_isolated(name) is None and bench.isolated_roofline(name, 1, 1.0)["traffic"] is None
+
+
+def test_summarize_isolated_requires_every_dispatch(tmp_path):
+    kernel = "void (anonymous namespace)::" + bench.ISOLATED["q8n4"][1] + "(GemvArgs)"
+    kt, fe, wr, sq = _isolated_dirs(tmp_path, "q8n4", kernel, 20000, 1.0, 1.0, 1.0, 1.0, 1.0)
+    other = "void (anonymous namespace)::" + bench.ISOLATED["q8n1"][1] + "(SplitArgs)"
+    with pytest.raises(SystemExit):
+        bench.summarize_isolated("q8n1", kt, fe, wr, wr, sq, str(tmp_path / "out"))  # kernel name mismatch
+    assert other != kernel
+
+
+def test_summarize_kt(tmp_path, monkeypatch):
+    kt, out = str(tmp_path / "kt"), str(tmp_path / "out")
     _write_csv(os.path.join(kt, "box", "kt_kernel_stats.csv"),
                ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"],
                [[SPLIT, 10, 336000, 33600, 90.0, 33000, 34000], [KEYS, 10, 10000, 1000, 2.7, 900, 1100]])
-    hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
-    calib_kib = bench.CALIB_BYTES / 1024 / 2.0  # counter reads half the true bytes
-    _write_csv(os.path.join(fe, "box", "f_counter_collection.csv"), hdr,
-               [[SPLIT, "FETCH_SIZE", 1000.0], [SPLIT, "FETCH_SIZE", 1002.0], [KEYS, "FETCH_SIZE", 4.0],
-                [NEG, "FETCH_SIZE", calib_kib]])
-    _write_csv(os.path.join(wr, "box", "w_counter_collection.csv"), hdr,
-               [[SPLIT, "WRITE_SIZE", 100.0], [KEYS, "WRITE_SIZE", 2.0], [NEG, "WRITE_SIZE", calib_kib]])
-    bench.summarize_profiles(kt, fe, wr, out)
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", os.path.join(out, os.path.basename(bench.TRAFFIC_FILE)))
+    bench.summarize_kt(kt, out)
     monkeypatch.setattr(bench, "KT_FILE", os.path.join(out, os.path.basename(bench.KT_FILE)))
-    t = bench.read_traffic()
-    assert t is not None
-    # (1001 + 4) KiB and (100 + 2) KiB per call, times the calibration factor 2
-    assert t["fetch_bytes"] == round(1005.0 * 1024 * 2) and t["write_bytes"] == round(102.0 * 1024 * 2)
-    assert t["bytes"] == t["fetch_bytes"] + t["write_bytes"]
-    assert bench.read_kernel_avgs() == {"gemv_ssq_split_kernel<5, 2, true, 8>": 33.6, "verify_keys_kernel": 1.0}
-    # a summary taken from other sources is not used
+    assert bench.read_kt_avg(bench.STEP_KERNEL) == 33.6
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
-    assert bench.read_traffic() is None and bench.read_kernel_avgs() is None
-
-
-def test_summarize_requires_each_step_kernel(tmp_path):
-    kt, fe, wr, out = (str(tmp_path / n) for n in ("kt", "fetch", "write", "out"))
-    _write_csv(os.path.join(kt, "k_kernel_stats.csv"),
-               ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"],
-               [[SPLIT, 1, 1, 1, 100, 1, 1]])
-    hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
-    for d, c in ((fe, "FETCH_SIZE"), (wr, "WRITE_SIZE")):
-        _write_csv(os.path.join(d, "c_counter_collection.csv"), hdr, [[SPLIT, c, 1.0], [NEG, c, 1.0]])
-    with pytest.raises(SystemExit):
-        bench.summarize_profiles(kt, fe, wr, out)
+    assert bench.read_kt_avg(bench.STEP_KERNEL) is None
 
 
 def test_step_algorithmic_bytes():
     rows, cols = bench.ROWS, bench.COLS
     assert bench.step_algo_bytes() == rows * cols // 32 * 68 + 8 * cols + 8 * rows + 20
+    assert bench.isolated_algo_bytes("step") == bench.step_algo_bytes()
+    assert bench.isolated_algo_bytes("q8n4") == rows * cols // 32 * 34 + 4 * (rows + cols) * 4
 
 
-def test_summarize_hit_rate(tmp_path, monkeypatch):
-    d, out = str(tmp_path / "tcc"), str(tmp_path / "out")
-    rows = []
-    for i, k in enumerate(bench.HIT_KERNELS):
-        for _ in range(2):
-            rows += [[f"void (anonymous namespace)::{k}(Args)", "TCC_HIT_sum", 10.0 * (i + 1)],
-                     [f"void (anonymous namespace)::{k}(Args)", "TCC_MISS_sum", 90.0]]
-    _write_csv(os.path.join(d, "box", "tcc_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"],
-               rows)
-    bench.summarize_hit_rate(d, out)
-    monkeypatch.setattr(bench, "HIT_FILE", os.path.join(out, os.path.basename(bench.HIT_FILE)))
-    r = bench.read_hit_rates()
-    assert r is not None and set(r) == set(bench.HIT_KERNELS)
-    for i, k in enumerate(bench.HIT_KERNELS):
-        assert r[k] == round(10.0 * (i + 1) / (10.0 * (i + 1) + 90.0), 4)
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
-    assert bench.read_hit_rates() is None
-
-
-def test_summarize_hit_rate_requires_each_kernel(tmp_path):
-    d = str(tmp_path / "tcc")
-    k = next(iter(bench.HIT_KERNELS))
-    _write_csv(os.path.join(d, "c_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"],
-               [[k, "TCC_HIT_sum", 1.0], [k, "TCC_MISS_sum", 1.0]])
-    with pytest.raises(SystemExit):
-        bench.summarize_hit_rate(d, str(tmp_path / "out"))
+def test_isolated_commands_run_committed_files():
+    for name in bench.ISOLATED:
+        cmds = bench.isolated_cmds(name)
+        assert all("bench.py" in c for c in cmds.values())
+        assert f"--only {name}" in cmds["kt"] and "--copy-calibration" in cmds["fetch"]
