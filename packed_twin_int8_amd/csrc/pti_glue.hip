@@ -203,6 +203,7 @@ __global__ void add_kernel(const float *a, const float *b, float *y, int64_t n)
 constexpr int kSvPart = 2048;
 constexpr int kSvThreads = 256;
 constexpr int kSvWaves = kSvThreads / 64;
+constexpr int kSvRun = kSvPart / kSvThreads;  // a thread's run of indices within a part
 
 struct SvPart {
     double m, s;  // the part's max logit and its exp-sum relative to that max
@@ -254,11 +255,24 @@ __device__ __forceinline__ double block_prefix(double loc, double *loc_s, double
     loc_s[tid] = loc;
     __syncthreads();
     if (lane == 0) {
-        double run = 0.0;
-        for (int i = 0; i < 64; i++) {
-            pre_s[tid + i] = run;
-            run += loc_s[tid + i];
+        // the wave's 64 values into registers, the sequential prefix there,
+        // then back (LDS round trips pipelined instead of one per element)
+        double v[64];
+#pragma unroll
+        for (int i = 0; i < 64; i += 2) {
+            const double2 t = *reinterpret_cast<const double2 *>(&loc_s[tid + i]);
+            v[i] = t.x, v[i + 1] = t.y;
         }
+        double run = 0.0;
+#pragma unroll
+        for (int i = 0; i < 64; i++) {
+            const double t = v[i];
+            v[i] = run;
+            run += t;
+        }
+#pragma unroll
+        for (int i = 0; i < 64; i += 2)
+            *reinterpret_cast<double2 *>(&pre_s[tid + i]) = make_double2(v[i], v[i + 1]);
         wbase[wv + 1] = run;
     }
     __syncthreads();
@@ -282,8 +296,8 @@ __global__ __launch_bounds__(kSvThreads) void sv_draw_kernel(const float *__rest
                                                              int32_t *__restrict__ tokens_out, int64_t vocab,
                                                              int64_t nparts)
 {
-    __shared__ double loc_s[kSvThreads];
-    __shared__ double pre_s[kSvThreads];
+    __shared__ __attribute__((aligned(16))) double loc_s[kSvThreads];
+    __shared__ __attribute__((aligned(16))) double pre_s[kSvThreads];
     __shared__ double wbase[kSvWaves + 1];
     __shared__ float wmax[kSvWaves];
     __shared__ int owner;
@@ -351,11 +365,15 @@ __global__ __launch_bounds__(kSvThreads) void sv_draw_kernel(const float *__rest
     const int n = (int)min<int64_t>(kSvPart, vocab - j0);
     const float *v = logits + s * vocab + j0;
     const double mb = ps[b].m, fb = factor(mb);
-    const int cq = (n + kSvThreads - 1) / kSvThreads;
+    const int cq = (n + kSvThreads - 1) / kSvThreads;  // at most kSvRun
     const int q0 = min(n, tid * cq), q1 = min(n, q0 + cq);
+    double e[kSvRun];  // this thread's weights, kept for the owner's scan
     double loc2 = 0.0;
-    for (int q = q0; q < q1; q++)
-        loc2 += exp((double(v[q]) - mb) / temperature) * fb;
+#pragma unroll
+    for (int k = 0; k < kSvRun; k++) {
+        e[k] = q0 + k < q1 ? exp((double(v[q0 + k]) - mb) / temperature) * fb : 0.0;
+        loc2 += e[k];
+    }
     if (tid == 0)
         owner = -1;
     double Zp;
@@ -372,15 +390,13 @@ __global__ __launch_bounds__(kSvThreads) void sv_draw_kernel(const float *__rest
     if (tid == own2) {
         double run = excl2;
         int pick = -1, last = -1;
-        for (int q = q0; q < q1; q++) {
-            const double e = exp((double(v[q]) - mb) / temperature) * fb;
-            if (e > 0.0) {
-                last = q;
-                run += e;
-                if (run > target) {
-                    pick = q;
-                    break;
-                }
+#pragma unroll
+        for (int k = 0; k < kSvRun; k++) {
+            if (pick < 0 && e[k] > 0.0) {  // entries past q1 are 0
+                last = q0 + k;
+                run += e[k];
+                if (run > target)
+                    pick = q0 + k;
             }
         }
         tokens_out[s] = (int32_t)(j0 + (pick >= 0 ? pick : last));
