@@ -18,28 +18,33 @@
 // Mapped onto CDNA4 as a split-K "flash decode" with both products on the
 // matrix cores (v_mfma_f32_16x16x32_f16):
 //   * Pass 1, one workgroup of 256 threads per (key chunk of 128, kv head,
-//     stream).  Cache rows are read whole: d/8 lanes cover a row with 16-byte
-//     loads, so a load instruction of a wave reads 64 / (d/8) consecutive rows
-//     as one contiguous span, and all of a wave's K loads (then all its V
-//     loads) are in flight together.  The rows go to LDS; the new entry,
-//     rounded as it is stored, replaces the row at pos_s there.
-//     Scores: each wave multiplies its 32 keys (16 per MFMA row block) by the
+//     stream); each of its four waves owns 32 consecutive keys.  Cache rows
+//     are read whole: d/8 lanes cover a row with 16-byte loads, so a load
+//     instruction of a wave reads 64 / (d/8) consecutive rows as one
+//     contiguous span, and all of a wave's K loads are in flight together
+//     (its V loads follow once the scores are issued).  A wave's rows go to
+//     its own LDS rows; the new entry, rounded as it is stored, replaces the
+//     row at pos_s there.
+//     Scores: the wave multiplies its 32 keys (16 per MFMA row block) by the
 //     group's queries.  q is split exactly enough for fp32: per head it is
 //     scaled by a power of two so that max |q| lies in [2^14, 2^15), then
-//     written as a high binary16 part plus a low one (22 bits in all); the
-//     16 MFMA columns hold the high parts of up to 8 heads and their low
-//     parts, and a DPP rotate adds each head's two columns.  Products of
+//     written as a high binary16 part plus a low one (22 bits in all);
+//     MFMA column 2h holds head h's high part and column 2h + 1 its low
+//     part, and a DPP swap of neighbouring lanes adds the two.  Products of
 //     binary16 values are exact in fp32, so the only roundings are the
 //     accumulation's.  A key is read once for all heads that share it.
-//     Softmax: the chunk's max and exp-sum per head (DPP trees and LDS); the
-//     weights are kept in units of 2^-15 (exact) so both of their binary16
-//     parts stay normal.
-//     Weighted V: rows = head parts (weights split the same way), k = keys,
-//     columns = 16 dimensions read transposed from the V rows in LDS
-//     (ds_read_b64_tr_b16); each wave owns d/4 dimensions over all 128 keys,
-//     and a lane swap adds each head's two rows.  The chunk's (max, exp-sum,
-//     weighted V) per head go to the workspace.  The chunk holding pos_s
-//     stores the new entry.
+//     Softmax: the wave's max per head in registers, the chunk's max over
+//     the four waves through LDS (the first barrier); the weights, in units
+//     of 2^-15 (exact, so both of their binary16 parts stay normal), stay in
+//     the lanes that computed them, which are already where the next
+//     product's A operand needs them.
+//     Weighted V: rows = head parts (row 2h high, 2h + 1 low), k = the
+//     wave's 32 keys, columns = 16 dimensions read transposed from the
+//     wave's V rows in LDS (ds_read_b64_tr_b16); each head's two rows sit in
+//     one lane and are added there.  The four waves' weighted V meet in LDS
+//     (the second barrier) and are added in wave order; the chunk's (max,
+//     exp-sum, weighted V) per head go to the workspace.  The chunk holding
+//     pos_s stores the new entry.
 //   * Pass 2, one workgroup per (head, stream, 32 dimensions): the chunks up
 //     to pos_s combine, rescaled by exp(m_c - M), in a fixed grouping of
 //     chunks.
@@ -104,18 +109,6 @@ __device__ __forceinline__ float wave_max(float v)
     return v;
 }
 
-// Sum over the 64 lanes, in lane 63, by the same tree.
-__device__ __forceinline__ float wave_add(float v)
-{
-    v = v + dpp_or<0x111, 0xf>(v, 0.f);
-    v = v + dpp_or<0x112, 0xf>(v, 0.f);
-    v = v + dpp_or<0x114, 0xf>(v, 0.f);
-    v = v + dpp_or<0x118, 0xf>(v, 0.f);
-    v = v + dpp_or<0x142, 0xa>(v, 0.f);
-    v = v + dpp_or<0x143, 0xc>(v, 0.f);
-    return v;
-}
-
 // Position of stream s, or -1 when outside the cache (the pass then writes
 // NaN outputs and touches no cache memory).
 __device__ __forceinline__ int64_t stream_pos(const AttnArgs &a, int s)
@@ -124,66 +117,54 @@ __device__ __forceinline__ int64_t stream_pos(const AttnArgs &a, int s)
     return (p >= 0 && p < a.max_len) ? p : -1;
 }
 
-// v + the value DPP moves into each lane (row_shr by CTRL - 0x110 lanes with
-// bound_ctrl, so lanes with no source within the 16-lane row add 0).
-template <int CTRL>
-__device__ __forceinline__ float add_shr(float v)
+// 8 consecutive fp32 values (two float4) rounded to binary16, packed as they
+// are stored.
+__device__ __forceinline__ u32x4 pack8(float4 a, float4 b)
 {
-    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf,
-                                                                     true));
+    return u32x4{(uint32_t)f2h(a.x) | ((uint32_t)f2h(a.y) << 16), (uint32_t)f2h(a.z) | ((uint32_t)f2h(a.w) << 16),
+                 (uint32_t)f2h(b.x) | ((uint32_t)f2h(b.y) << 16), (uint32_t)f2h(b.z) | ((uint32_t)f2h(b.w) << 16)};
 }
 
-// Sum over each aligned group of N lanes (N = 8 or 16) of a 16-lane row; the
-// group's last lane holds it.  A fixed tree of row shifts.
-template <int N>
-__device__ __forceinline__ float group_sum(float v)
+// c ? a : b by bit masks, so the compiler cannot move b's load into a branch
+// (which would reorder the loads and make the first wait cover all of them).
+__device__ __forceinline__ u32x4 pick(bool c, u32x4 a, u32x4 b)
 {
-    static_assert(N == 8 || N == 16, "group size");
-    v = add_shr<0x111>(v);
-    v = add_shr<0x112>(v);
-    v = add_shr<0x114>(v);
-    if constexpr (N == 16)
-        v = add_shr<0x118>(v);
-    return v;
-}
-
-// 8 consecutive fp32 values rounded to binary16, packed as they are stored.
-__device__ __forceinline__ u32x4 pack8(const float *x)
-{
-    u32x4 w;
-#pragma unroll
-    for (int e = 0; e < 4; e++)
-        w[e] = (uint32_t)f2h(x[2 * e]) | ((uint32_t)f2h(x[2 * e + 1]) << 16);
-    return w;
+    const uint32_t m = c ? 0xFFFFFFFFu : 0u;
+    return (a & m) | (b & ~m);
 }
 
 // Max over the four 16-lane rows of a wave, per column (lane % 16), in every
-// lane (once per workgroup).
+// lane.
 __device__ __forceinline__ float col_max(float v)
 {
     v = fmaxf(v, __shfl_xor(v, 16, 64));
     return fmaxf(v, __shfl_xor(v, 32, 64));
 }
 
-// For lanes l < 32: lane l's value plus lane l + 32's.
-__device__ __forceinline__ float half_sum(float v) { return v + __shfl_xor(v, 32, 64); }
-
+// Pass 1.  Each wave owns 32 consecutive keys of the chunk and takes them
+// through scores, softmax numerators and the weighted V on its own; the
+// workgroup meets twice: for the chunk max of each head, and to add the four
+// waves' weighted V.  The V rows are loaded once the scores are issued: with
+// them in flight from the start the K rows arrived later (every chunk's K
+// and V compete for HBM at once) and the registers allowed three waves per
+// SIMD instead of four; both were slower, at 4K and at 32K positions.
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void attn_partial_kernel(AttnArgs a)
 {
     static_assert(G >= 1 && G <= 8, "the high and low parts of at most 8 heads fill the 16 MFMA columns");
     constexpr int LPR = D / 8;                  // lanes per cache row: 16 bytes (8 halves) each
     constexpr int RPI = 64 / LPR;               // rows one load instruction of a wave covers
     constexpr int NW = kThreads / 64;
-    constexpr int KPW = kChunk / NW;            // keys per wave (scores)
+    constexpr int KPW = kChunk / NW;            // keys per wave
     constexpr int IT = KPW / RPI;               // loads per wave per tile
     constexpr int KSTEPS = D / 32;              // MFMA steps over the dimensions (scores)
-    constexpr int NBW = D / 16 / NW;            // 16-dimension output blocks per wave (weighted V)
-    constexpr int PITCH = 2 * D + 16;           // LDS row pitch of the K and V tiles, bytes
-    static_assert(KPW == 32 && NBW >= 1, "tile shape");
-    __shared__ __attribute__((aligned(16))) uint8_t tile[kChunk * PITCH];  // K rows, then V rows
-    __shared__ __attribute__((aligned(16))) float ps[G][kChunk];            // scores, then weights
-    __shared__ float red[G][NW];
+    constexpr int NB = D / 16;                  // 16-dimension output blocks (weighted V)
+    constexpr int PITCH = 2 * D + 16;           // LDS row pitch of the K and V rows, bytes
+    static_assert(KPW == 32, "tile shape");
+    static_assert(G * D * 4 <= KPW * PITCH, "a wave's weighted V fits its own rows' LDS");
+    // per wave: its 32 K rows, then its 32 V rows, then its weighted V [G][D]
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kChunk * PITCH];
+    __shared__ float wred[2][NW][8];  // per wave and head: max, then exp-sum
     const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t pos = stream_pos(a, s);
@@ -198,45 +179,59 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a)
     const float *vn = a.v_new + ((size_t)s * a.Hkv + g) * D;
     const int r = lane / LPR, seg = lane % LPR;  // row within a load, 8-dimension segment
     const int n = lane & 15, kg = lane >> 4;     // MFMA column / row (lane % 16) and k group (lane / 16)
+    uint8_t *rows = tile + wv * KPW * PITCH;     // this wave's rows
 
-    // ---- K and V rows are read whole and in order (LPR lanes x 16 bytes),
-    // every load of the wave in flight at once, through buffer resources over
-    // the chunk's valid rows (rows past them read 0 without a branch).  The
-    // new entry (rounded as it is stored) replaces the row at pos when the
-    // rows are written to LDS.
+    // ---- loads.  A wave's loads return in order, so the order they are
+    // issued in sets what each step waits for: the new entry's and q's few
+    // bytes first (no branch: every workgroup's k_new, v_new and q rows
+    // exist), then the wave's K rows (its V rows follow the scores).  Rows are read
+    // whole and in order (LPR lanes x 16 bytes) through buffer resources over
+    // the chunk's valid rows (rows past them read 0 without a branch).
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(K + (size_t)j0 * D), (short)0, nk * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(V + (size_t)j0 * D), (short)0, nk * D * 2, 0x00020000);
     const int newkey = has_new ? (int)(pos - j0) : -1;  // chunk index of the new entry
-    u32x4 kn8 = {0, 0, 0, 0}, vn8 = {0, 0, 0, 0};
-    if (has_new)  // uniform
-        kn8 = pack8(kn + 8 * seg), vn8 = pack8(vn + 8 * seg);
-    u32x4 kt[IT];
+    const float4 *knp = reinterpret_cast<const float4 *>(kn + 8 * seg);
+    const float4 *vnp = reinterpret_cast<const float4 *>(vn + 8 * seg);
+    const float4 kn0 = knp[0], kn1 = knp[1], vn0 = vnp[0], vn1 = vnp[1];
+    const int hq = n >> 1;  // the head of MFMA column (and row) n; n & 1 picks its part
+    const float4 *qrow = reinterpret_cast<const float4 *>(
+        a.q + ((size_t)s * a.H + (size_t)g * G + (hq < G ? hq : 0)) * D + 8 * kg);
+    float4 qv[KSTEPS][2];
 #pragma unroll
-    for (int it = 0; it < IT; it++) {
-        const int key = wv * KPW + it * RPI + r;
-        kt[it] = __builtin_amdgcn_raw_buffer_load_b128(krs, (key * D + 8 * seg) * 2, 0, 0);
-    }
+    for (int ks = 0; ks < KSTEPS; ks++)
+#pragma unroll
+        for (int e4 = 0; e4 < 2; e4++)
+            qv[ks][e4] = qrow[8 * ks + e4];
+    u32x4 kt[IT], vt[IT];
+#pragma unroll
+    for (int it = 0; it < IT; it++)
+        kt[it] = __builtin_amdgcn_raw_buffer_load_b128(krs, ((wv * KPW + it * RPI + r) * D + 8 * seg) * 2, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads above issued first, in this order
+    const u32x4 kn8 = pack8(kn0, kn1), vn8 = pack8(vn0, vn1);  // used only where has_new
 
-    // ---- q as the MFMA's B operand: column n < 8 holds the high binary16
-    // part of head n, column n + 8 the low part (q' - high), for the k
-    // group's 8 dimensions per step.  q' = q 2^sh with sh chosen per head so
-    // that max |q'| lies in [2^14, 2^15): both parts stay normal (or exactly
+    // ---- q as the MFMA's B operand: column 2h holds the high binary16 part
+    // of head h, column 2h + 1 the low part (q' - high), for the k group's 8
+    // dimensions per step.  q' = q 2^sh with sh chosen per head so that
+    // max |q'| lies in [2^14, 2^15): both parts stay normal (or exactly
     // representable) and high + low carries 22 bits of each element.
-    const int hq = n & 7;
+    // Columns past the group's heads get zeros (a mask, not a branch).
+    const uint32_t keep = hq < G ? 0xFFFFFFFFu : 0u;
     float qf[KSTEPS][8];
     float qmax = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ks++)
 #pragma unroll
         for (int e4 = 0; e4 < 2; e4++) {
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (hq < G)
-                v = *reinterpret_cast<const float4 *>(a.q + ((size_t)s * a.H + (size_t)g * G + hq) * D + 32 * ks +
-                                                      8 * kg + 4 * e4);
-            qf[ks][4 * e4] = v.x, qf[ks][4 * e4 + 1] = v.y, qf[ks][4 * e4 + 2] = v.z, qf[ks][4 * e4 + 3] = v.w;
-            qmax = fmaxf(qmax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            const float4 t = qv[ks][e4];
+            const float e[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const float x = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, e[j]) & keep);
+                qf[ks][4 * e4 + j] = x;
+                qmax = fmaxf(qmax, fabsf(x));
+            }
         }
     qmax = col_max(qmax);  // over the four k groups: the head's max |q|
     const int sh = qmax > 0.f ? 15 - __builtin_amdgcn_frexp_expf(qmax) : 0;
@@ -247,17 +242,16 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a)
         for (int e = 0; e < 8; e++) {
             const float x = ldexpf(qf[ks][e], sh);
             const _Float16 hi = (_Float16)x;
-            qb[ks][e] = n < 8 ? hi : (_Float16)(x - (float)hi);
+            qb[ks][e] = (n & 1) ? (_Float16)(x - (float)hi) : hi;
         }
 
-    // ---- this wave's 32 K rows to its own LDS rows, then the scores on the
-    // matrix cores: rows = keys (A, 16 per block), columns = head parts (B)
-    uint8_t *kw = tile + wv * KPW * PITCH;
+    // ---- the wave's 32 K rows to its LDS rows (the new entry, rounded as it
+    // is stored, replaces the row at pos), then the scores on the matrix
+    // cores: rows = keys (A, 16 per block), columns = head parts (B)
 #pragma unroll
     for (int it = 0; it < IT; it++) {
         const int kk = it * RPI + r;
-        const u32x4 row = (wv * KPW + kk == newkey) ? kn8 : kt[it];
-        *reinterpret_cast<u32x4 *>(kw + kk * PITCH + 16 * seg) = row;
+        *reinterpret_cast<u32x4 *>(rows + kk * PITCH + 16 * seg) = pick(wv * KPW + kk == newkey, kn8, kt[it]);
     }
     // the wave reads rows other lanes wrote: LDS serves a wave's accesses in
     // order, and the fence keeps the compiler from moving reads above writes
@@ -269,131 +263,130 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a)
         sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ks++) {
-            const f16x8 ka = *reinterpret_cast<const f16x8 *>(kw + (16 * kb + n) * PITCH + 64 * ks + 16 * kg);
+            const f16x8 ka = *reinterpret_cast<const f16x8 *>(rows + (16 * kb + n) * PITCH + 64 * ks + 16 * kg);
             sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[ks], sacc[kb], 0, 0, 0);
         }
     }
-    // lane (n, kg) holds keys 16 kb + 4 kg + i of column n: a head's score is
-    // its high column plus its low column (8 lanes over, same 16-lane row)
+    // V rows now: their latency overlaps the softmax
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
-        f32x4 sc;
+    for (int it = 0; it < IT; it++)
+        vt[it] = __builtin_amdgcn_raw_buffer_load_b128(vrs, ((wv * KPW + it * RPI + r) * D + 8 * seg) * 2, 0, 0);
+
+    // ---- scores of the lane's 8 keys (wave key 16 kb + 4 kg + i) for head
+    // n / 2: its column plus the partner column n ^ 1 (the other part of the
+    // same head; both lanes of a pair get the same sum); keys past the
+    // chunk's last get -inf.  Then the wave's max per head (over its 8
+    // values, then the four k groups).
+    float sc[8];
+    float m = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             // (a copy first: a bit cast of a vector element itself reads element 0)
-            const float hi = sacc[kb][i];
-            const float lo = __builtin_bit_cast(
-                float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, hi), 0x128, 0xf, 0xf, false));
-            sc[i] = ldexpf(hi + lo, -sh) * a.scale;
+            const float own = sacc[kb][i];
+            const float other = __builtin_bit_cast(
+                float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, own), 0xB1, 0xf, 0xf, false));
+            const float v = ldexpf((n & 1) ? other + own : own + other, -sh) * a.scale;  // high + low
+            sc[4 * kb + i] = wv * KPW + 16 * kb + 4 * kg + i < nk ? v : -INFINITY;
+            m = fmaxf(m, sc[4 * kb + i]);
         }
-        if (n < G)
-            *reinterpret_cast<f32x4 *>(&ps[n][wv * KPW + 16 * kb + 4 * kg]) = sc;
-    }
+    m = col_max(m);
+    if (kg == 0 && (n & 1) == 0 && hq < G)
+        wred[0][wv][hq] = m;
+    __syncthreads();  // (1) every wave's max
+    m = wred[0][0][hq & 7];
+#pragma unroll
+    for (int w = 1; w < NW; w++)
+        m = fmaxf(m, wred[0][w][hq & 7]);
 
-    // ---- V rows: issued now so the loads overlap the softmax
-    u32x4 vt[IT];
+    // ---- weights in units of 2^-15 (exact; both binary16 parts below stay
+    // normal), 0 for keys past the chunk and for columns past the heads; the
+    // wave's exp-sum per head (its 8 values in order, then the k groups)
+    float pw[8];
+    float l = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        pw[e] = hq < G ? expf(sc[e] - m) * 32768.f : 0.f;
+        l += pw[e];
+    }
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (kg == 0 && (n & 1) == 0 && hq < G)
+        wred[1][wv][hq] = l;
+
+    // ---- the wave's V rows over its K rows (the scores have read them)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int it = 0; it < IT; it++) {
-        const int key = wv * KPW + it * RPI + r;
-        vt[it] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (key * D + 8 * seg) * 2, 0, 0);
+        const int kk = it * RPI + r;
+        *reinterpret_cast<u32x4 *>(rows + kk * PITCH + 16 * seg) = pick(wv * KPW + kk == newkey, vn8, vt[it]);
     }
-    __syncthreads();  // scores complete; every wave is done with its K rows
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 
-    // ---- chunk max and exp-sum per head (thread tid: key tid, if any)
-    float sc[G], m[G];
+    // ---- weighted V of the wave's 32 keys on the matrix cores: rows = head
+    // parts (A: row 2h the high binary16 part of head h's weights, row
+    // 2h + 1 the low part -- lane n holds head n / 2's weights already),
+    // k = the 32 keys in the scores' order (k group kg holds keys
+    // 4 kg .. 4 kg + 3 and 16 + 4 kg .. 16 + 4 kg + 3), columns = 16
+    // dimensions (B, read transposed from the V rows)
+    f16x8 pa;
 #pragma unroll
-    for (int h = 0; h < G; h++) {
-        sc[h] = tid < nk ? ps[h][tid] : -INFINITY;  // nk <= kChunk
-        const float wm = wave_max(sc[h]);
-        if (lane == 63)
-            red[h][wv] = wm;
+    for (int e = 0; e < 8; e++) {
+        const _Float16 hi = (_Float16)pw[e];
+        pa[e] = (n & 1) ? (_Float16)(pw[e] - (float)hi) : hi;
     }
-    __syncthreads();
+    // A product's lane (column n, row group kg) holds rows 4 kg .. 4 kg + 3:
+    // heads 2 kg and 2 kg + 1, high part then low part; each head's sum is
+    // the wave's weighted V, parked over the wave's rows once every product
+    // has read them
+    float ov[NB][2];
 #pragma unroll
-    for (int h = 0; h < G; h++) {
-        float v = red[h][0];
-#pragma unroll
-        for (int w = 1; w < NW; w++)
-            v = fmaxf(v, red[h][w]);
-        m[h] = v;
+    for (int j = 0; j < NB; j++) {
+        const int col = 2 * (16 * j + 4 * (n & 3));  // byte offset of 4 dimensions
+        const uint8_t *t0 = rows + (4 * kg + (n >> 2)) * PITCH + col;
+        const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t0));
+        const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t0 + 16 * PITCH));
+        const f16x8 vb = __builtin_bit_cast(f16x8, s16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]});
+        const f32x4 o = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const float o0 = o[0], o1 = o[1], o2 = o[2], o3 = o[3];  // (copies first, as above)
+        ov[j][0] = o0 + o1;
+        ov[j][1] = o2 + o3;
     }
-    __syncthreads();  // red is reused below
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    float *ow = reinterpret_cast<float *>(rows);  // [G][D]
 #pragma unroll
-    for (int h = 0; h < G; h++) {
-        // weights in units of 2^-15 (exact): the binary16 parts below stay normal
-        const float p = tid < nk ? expf(sc[h] - m[h]) * 32768.f : 0.f;
-        if (tid < kChunk)
-            ps[h][tid] = p;  // only this thread reads or writes index tid
-        const float ws = wave_add(p);
-        if (lane == 63)
-            red[h][wv] = ws;
-    }
-    // V rows to LDS (over the K rows, which no wave reads any more)
+    for (int j = 0; j < NB; j++)
 #pragma unroll
-    for (int it = 0; it < IT; it++) {
-        const int key = wv * KPW + it * RPI + r;
-        const u32x4 row = (key == newkey) ? vn8 : vt[it];
-        *reinterpret_cast<u32x4 *>(tile + key * PITCH + 16 * seg) = row;
-    }
-    __syncthreads();
+        for (int u = 0; u < 2; u++) {
+            const int h = 2 * kg + u;
+            if (h < G)
+                ow[h * D + 16 * j + n] = ov[j][u];
+        }
+    __syncthreads();  // (2) every wave's weighted V and exp-sums
 
-    // ---- weighted V on the matrix cores: rows = head parts (A: row n < 8
-    // the high binary16 part of head n's weights (units of 2^-15), n + 8 the low part),
-    // k = keys, columns = 16 dimensions (B, read transposed from the V rows).
-    // Within each 32-key step, k group kg holds keys 4 kg .. 4 kg + 3 and
-    // 16 + 4 kg .. 16 + 4 kg + 3 in both operands.
-    f32x4 oacc[NBW];
+    // ---- chunk partials: the four waves' weighted V added in wave order,
+    // the max and exp-sum per head, all in units of 2^-15 (the combine
+    // divides one by the other)
+    for (int o = tid; o < G * D; o += kThreads) {
+        const int h = o / D, dd = o % D;
+        float v = 0.f;
 #pragma unroll
-    for (int j = 0; j < NBW; j++)
-        oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kq = 0; kq < kChunk / 32; kq++) {
-        float4 p0 = make_float4(0.f, 0.f, 0.f, 0.f), p1 = p0;
-        if (hq < G) {
-            p0 = *reinterpret_cast<const float4 *>(&ps[hq][32 * kq + 4 * kg]);
-            p1 = *reinterpret_cast<const float4 *>(&ps[hq][32 * kq + 16 + 4 * kg]);
-        }
-        const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-        f16x8 pa;
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            const _Float16 hi = (_Float16)pv[e];
-            pa[e] = n < 8 ? hi : (_Float16)(pv[e] - (float)hi);
-        }
-#pragma unroll
-        for (int j = 0; j < NBW; j++) {
-            const int col = 2 * (16 * (wv * NBW + j) + 4 * (n & 3));  // byte offset of 4 dimensions
-            const uint8_t *t0 = tile + (32 * kq + 4 * kg + (n >> 2)) * PITCH + col;
-            const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t0));
-            const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t0 + 16 * PITCH));
-            const f16x8 vb = __builtin_bit_cast(f16x8, s16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]});
-            oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, oacc[j], 0, 0, 0);
-        }
-    }
-
-    // ---- chunk partials: weighted V (high + low parts), max, sum, both in
-    // units of 2^-15 (the combine divides one by the other).
-    // Lane l < 32 holds rows 4 (l / 16) + i (heads), column n; lane l + 32
-    // holds the low parts of the same heads.
-#pragma unroll
-    for (int j = 0; j < NBW; j++) {
-        const int d0 = 16 * (wv * NBW + j) + n;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const float v = half_sum(oacc[j][i]);
-            const int h = 4 * kg + i;
-            if (kg < 2 && h < G)
-                a.part[(((size_t)s * a.H + (size_t)g * G + h) * a.n_chunks + c) * D + d0] = v;
-        }
+        for (int w = 0; w < NW; w++)
+            v += reinterpret_cast<const float *>(tile + w * KPW * PITCH)[o];
+        a.part[(((size_t)s * a.H + (size_t)g * G + h) * a.n_chunks + c) * D + dd] = v;
     }
     if (tid < G) {
-        float l = red[tid][0];
+        float mm = wred[0][0][tid], ll = wred[1][0][tid];
 #pragma unroll
         for (int w = 1; w < NW; w++)
-            l += red[tid][w];
+            mm = fmaxf(mm, wred[0][w][tid]), ll += wred[1][w][tid];
         float *pp = a.ml + (((size_t)s * a.H + (size_t)g * G + tid) * a.n_chunks + c) * 2;
-        pp[0] = m[tid];
-        pp[1] = l;
+        pp[0] = mm;
+        pp[1] = ll;
     }
 
     // ---- store the new entry (the chunk that holds pos; every reader of
