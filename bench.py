@@ -86,6 +86,38 @@ def timed_stats(torch, fn, stream, reps=10, per_rep=200, warmup=50):
     return {"median_us": round(q(0.5), 3), "p10_us": round(q(0.1), 3), "p90_us": round(q(0.9), 3)}
 
 
+def graph_us(torch, pti, make, calls=50, reps=10):
+    """GPU time per call with the host's launch cost taken out: `calls` calls,
+    made by make(stream_handle)(i), captured on a side stream into one graph
+    and replayed back to back; the median over `reps` replays, in
+    microseconds.  (A call of a few microseconds timed in a Python loop is
+    bound by the loop, not by the GPU.)"""
+    s = torch.cuda.Stream()
+    fn = make(pti._stream(s))
+    torch.cuda.synchronize()
+    fn(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(calls):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    t = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(cur)
+        g.replay()
+        b.record(cur)
+        b.synchronize()
+        t.append(a.elapsed_time(b) * 1e3 / calls)
+    del g
+    t.sort()
+    return round(t[len(t) // 2], 3)
+
+
 def cpu_baseline(d, budget_s: float):
     """The oracle (scalar fp64 C, one thread) on the same SSQ GEMV, repeated
     until budget_s seconds have passed (at least once)."""
@@ -454,10 +486,11 @@ def tiny_twin(torch, pti, dev, stream):
     w = torch.from_numpy(pti.pack_ssq(d["A"], d["B"], d["sA"], d["sB"])).to(dev)
     xa, xb = torch.from_numpy(d["xA"]).to(dev), torch.from_numpy(d["xB"]).to(dev)
     y = torch.empty((2, 256), device=dev)
-    L, sp = pti.lib(), pti._stream(stream)
-    st = timed_stats(torch, lambda i: pti._check("pti_gemv_ssq", L.pti_gemv_ssq(
-        w.data_ptr(), xa.data_ptr(), xb.data_ptr(), y[0].data_ptr(), y[1].data_ptr(), 256, 512, sp)), stream,
-        reps=5, per_rep=200)
+    L = pti.lib()
+    make = lambda sp: lambda i: pti._check("pti_gemv_ssq", L.pti_gemv_ssq(
+        w.data_ptr(), xa.data_ptr(), xb.data_ptr(), y[0].data_ptr(), y[1].data_ptr(), 256, 512, sp))
+    st = timed_stats(torch, make(pti._stream(stream)), stream, reps=5, per_rep=200)
+    st["graph_us"] = graph_us(torch, pti, make)
     torch.cuda.synchronize()
     GPU_OUT["config1"] = (y[0].cpu().numpy().copy(), y[1].cpu().numpy().copy())
     return {"ssq_twin_256x512": {**st, "weight_bytes": int(w.numel())}}
@@ -491,21 +524,24 @@ def layer_sweep(torch, pti, dev, stream):
             y = torch.empty((4, rows), device=dev)
             for n in ((2,) if variant != "q8" else (1, 2, 4)):
                 if variant == "q8":
-                    fn = lambda i, n=n: pti._check("pti_gemv_q8_multi", L.pti_gemv_q8_multi(
+                    make = lambda sp, n=n: lambda i: pti._check("pti_gemv_q8_multi", L.pti_gemv_q8_multi(
                         ws[i % nc].data_ptr(), x.data_ptr(), y.data_ptr(), rows, cols, n, sp))
                 else:
-                    fn = lambda i: pti._check("pti_gemv_ssq", L.pti_gemv_ssq(
+                    make = lambda sp: lambda i: pti._check("pti_gemv_ssq", L.pti_gemv_ssq(
                         ws[i % nc].data_ptr(), x[0].data_ptr(), x[1].data_ptr(), y[0].data_ptr(), y[1].data_ptr(),
                         rows, cols, sp))
-                st = timed_stats(torch, fn, stream, reps=5, per_rep=100, warmup=20)
+                st = timed_stats(torch, make(sp), stream, reps=5, per_rep=100, warmup=20)
+                st["graph_us"] = graph_us(torch, pti, make)
                 torch.cuda.synchronize()
                 key = f"layer_{name}_{variant}" + (f"_n{n}" if variant == "q8" else "")
                 GPU_OUT[key] = y[:n].cpu().numpy().copy()
                 us = st["median_us"]
                 algo = P.nbytes + n * (rows + cols) * 4
+                gus = st["graph_us"]
                 out[key] = {**st, "rows": rows, "cols": cols, "weight_bytes": int(P.nbytes), "rotated_copies": nc,
                             "weight_GBps": round(P.nbytes / (us * 1e-6) / 1e9, 1),
                             "frac_of_hbm_peak": round(algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                            "graph_frac_of_hbm_peak": round(algo / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                             "outputs_per_s": round(n * rows / (us * 1e-6), 1)}
             del ws, w0
             torch.cuda.empty_cache()
@@ -727,16 +763,18 @@ def verify_and_pack(torch, pti, dev, stream, d):
         tok = torch.zeros(n, dtype=torch.int32, device=dev)
         am = torch.empty(n, dtype=torch.int32, device=dev)
         acc = torch.empty(1, dtype=torch.int32, device=dev)
-        st = timed_stats(torch, lambda i: L.pti_verify_argmax(logits.data_ptr(), tok.data_ptr(), am.data_ptr(),
-                                                              acc.data_ptr(), 32000, n, sp),
-                         stream, reps=5, per_rep=50, warmup=10)
+        make = lambda sp: lambda i: L.pti_verify_argmax(logits.data_ptr(), tok.data_ptr(), am.data_ptr(),
+                                                        acc.data_ptr(), 32000, n, sp)
+        st = timed_stats(torch, make(sp), stream, reps=5, per_rep=50, warmup=10)
+        st["graph_us"] = graph_us(torch, pti, make)
         out[f"verify_greedy_n{n}_v32000"] = st
         u = torch.rand(n, dtype=torch.float64, generator=g).to(dev)
         sw = pti.sample_verify_workspace(32000, n, dev)
-        st = timed_stats(torch, lambda i: L.pti_sample_verify(logits.data_ptr(), tok.data_ptr(), u.data_ptr(), 0.7,
-                                                              am.data_ptr(), acc.data_ptr(), 32000, n,
-                                                              sw.data_ptr(), sw.numel(), sp),
-                         stream, reps=5, per_rep=50, warmup=10)
+        make = lambda sp: lambda i: L.pti_sample_verify(logits.data_ptr(), tok.data_ptr(), u.data_ptr(), 0.7,
+                                                        am.data_ptr(), acc.data_ptr(), 32000, n, sw.data_ptr(),
+                                                        sw.numel(), sp)
+        st = timed_stats(torch, make(sp), stream, reps=5, per_rep=50, warmup=10)
+        st["graph_us"] = graph_us(torch, pti, make)
         out[f"verify_sampled_n{n}_v32000_t0.7"] = st
         log(f"verify n={n}: {out[f'verify_greedy_n{n}_v32000']}")
     ts = []
@@ -782,18 +820,22 @@ def attention(torch, pti, dev, stream):
         args = (q.data_ptr(), kn.data_ptr(), vn.data_ptr(), pos.data_ptr(), o.data_ptr(), work.data_ptr(),
                 work.numel())
 
-        def call(i, a=args):
-            kp, vp = ptrs[i % n_sets]
-            st = lib.pti_attn_decode(a[0], a[1], a[2], kp, vp, a[3], a[4], S, H, Hkv, d, L, a[5], a[6], sp)
-            if st:
-                pti._check("pti_attn_decode", st)
-        st = timed_stats(torch, call, stream, reps=5, per_rep=50, warmup=10)
+        def make(sp, a=args):
+            def call(i):
+                kp, vp = ptrs[i % n_sets]
+                st = lib.pti_attn_decode(a[0], a[1], a[2], kp, vp, a[3], a[4], S, H, Hkv, d, L, a[5], a[6], sp)
+                if st:
+                    pti._check("pti_attn_decode", st)
+            return call
+        st = timed_stats(torch, make(sp), stream, reps=5, per_rep=50, warmup=10)
+        st["graph_us"] = graph_us(torch, pti, make)
         kv_bytes = 2 * Hkv * d * 2 * ((L - 1) + L)  # K and V rows 0..pos of both streams
         algo = kv_bytes + 2 * S * H * d * 4 + 2 * S * Hkv * d * 4
         out[f"attn_twin_h40_kv8_d128_ctx{L}"] = {
             **st, "kv_bytes": kv_bytes, "algorithmic_bytes": algo, "cache_sets": n_sets,
             "GBps": round(algo / (st["median_us"] * 1e-6) / 1e9, 1),
-            "frac_of_hbm_peak": round(algo / (st["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            "frac_of_hbm_peak": round(algo / (st["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "graph_frac_of_hbm_peak": round(algo / (st["graph_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"attention ctx {L}: {out[f'attn_twin_h40_kv8_d128_ctx{L}']}")
         del kc, vc, work
         torch.cuda.empty_cache()
