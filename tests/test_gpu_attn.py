@@ -15,8 +15,9 @@ Bars:
     element, the 128-term fp32 accumulation of exact products costs
     d u, the sum of the two parts, the scaling by 2^-sh and the product with
     the fp32 1/sqrt(d) one rounding each.  The weights (in units of 2^-15)
-    are split the same way, so a chunk's weighted V carries 128 u of
-    accumulation, 4 u of split and one rounding for the two parts' sum, plus
+    are split the same way, so a chunk's weighted V carries at most 128 u of
+    accumulation (32 keys per wave, then the four waves' sum: 35 u), 4 u of
+    split and one rounding for the two parts' sum, plus
     2^-40 |v_j| per key from the low part's binary16 spacing.  The score
     error passes through exp into the weights (4 eps_s); the factor 2 covers
     the numerator and the exp-sum of the normalisation, n_chunks the chunk
