@@ -173,6 +173,7 @@ KT_FILE = os.path.join(HERE, "profiles", "bench_default_17408x5120_kernel_stats.
 # the kernel of the headline step (the fused SSQ twin GEMV; verify_keys_kernel follows it)
 STEP_KERNEL = "gemv_ssq_split_kernel<5, 2, true, 8>"
 KERNEL_SOURCES = ("packed_twin_int8_amd/csrc/pti_gemv.hip", "packed_twin_int8_amd/build.py")
+ATTN_SOURCES = ("packed_twin_int8_amd/csrc/pti_attn.hip", "packed_twin_int8_amd/build.py")
 KT_CMDS = {
     "kt": "rocprofv3 --kernel-trace --stats -f csv -d rocprof_out/bench -o bench -- python3 bench.py --no-cpu",
     "summary": "python3 bench.py --summarize-kt rocprof_out/bench",
@@ -186,10 +187,10 @@ def step_algo_bytes() -> int:
     return ROWS * (COLS // 32) * 68 + 2 * COLS * 4 + 2 * ROWS * 4 + 2 * 4 + 2 * 4 + 4
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(HERE, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -269,7 +270,15 @@ ISOLATED = {
     "q8n1": ("Q8 GEMV, N = 1 (pti_gemv_q8_multi)", "gemv_q8_split_kernel<5, 1>", "q8", 1),
     "q8n2": ("Q8 GEMV, N = 2 (pti_gemv_q8_multi)", "gemv_q8_split_kernel<5, 2>", "q8", 2),
     "q8n4": ("Q8 GEMV, N = 4 (pti_gemv_q8_multi)", "gemv_kernel<0, 4, 4, 2, true, 16, 4>", "q8", 4),
+    # attention: format "attn", the last field the context length
+    "attn4k": ("twin-KV decode attention (pti_attn_decode), 2 streams, 40 query heads over 8 kv heads of 128, "
+               "4096 positions", "attn_partial_kernel<128, 5>", "attn", 4096),
+    "attn32k": ("twin-KV decode attention (pti_attn_decode), 2 streams, 40 query heads over 8 kv heads of 128, "
+                "32768 positions", "attn_partial_kernel<128, 5>", "attn", 32768),
 }
+ATTN_SHAPE = (2, 40, 8, 128)  # streams, query heads, kv heads, head dim
+ATTN_COMBINE = "attn_combine_kernel<128>"
+
 ISOLATED_CALLS = 60
 SQ_COUNTERS = ("SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU",
                "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT")
@@ -288,7 +297,14 @@ def isolated_cmds(name):
 
 
 def isolated_profile_path(name):
+    _, _, fmt, n = ISOLATED[name]
+    if fmt == "attn":
+        return os.path.join(HERE, "profiles", f"attn_twin_h40_kv8_d128_ctx{n}_isolated.txt")
     return os.path.join(HERE, "profiles", f"gemv_{name}_17408x5120_isolated.txt")
+
+
+def isolated_sources(name):
+    return ATTN_SOURCES if ISOLATED[name][2] == "attn" else KERNEL_SOURCES
 
 
 def isolated_run(torch, pti, dev, stream, name, calibrate):
@@ -304,6 +320,9 @@ def isolated_run(torch, pti, dev, stream, name, calibrate):
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    if fmt == "attn":
+        attn_isolated_run(torch, pti, dev, stream, name)
+        return
     if fmt == "ssq":
         d = synth.twin(ROWS, COLS, synth.SEED_SSQ_FFN)
         P = pti.pack_ssq(d["A"], d["B"], d["sA"], d["sB"])
@@ -336,8 +355,45 @@ def isolated_run(torch, pti, dev, stream, name, calibrate):
     log(f"isolated {name}: {ISOLATED_CALLS} launches of {what}, {nc} weight copies of {P.nbytes} B")
 
 
+def attn_algo_bytes(L):
+    """Algorithmic bytes of one attention call at the benchmark's shape with
+    positions L - 2 and L - 1: the K and V rows 0..pos of both streams, q,
+    k_new, v_new and out."""
+    S, H, Hkv, d = ATTN_SHAPE
+    kv_bytes = 2 * Hkv * d * 2 * ((L - 1) + L)
+    return kv_bytes + 2 * S * H * d * 4 + 2 * S * Hkv * d * 4
+
+
+def attn_isolated_run(torch, pti, dev, stream, name):
+    """ISOLATED_CALLS attention calls at the benchmark's shape through the C
+    entry point, caches rotated over sets of at least 640 MB in all."""
+    what, _, _, L = ISOLATED[name]
+    S, H, Hkv, d = ATTN_SHAPE
+    set_bytes = 2 * S * Hkv * L * d * 2
+    n_sets = max(2, -(-640 * 2**20 // set_bytes))
+    kc = [[torch.randn((Hkv, L, d), device=dev).half() for _ in range(S)] for _ in range(n_sets)]
+    vc = [[torch.randn((Hkv, L, d), device=dev).half() for _ in range(S)] for _ in range(n_sets)]
+    q = torch.randn((S, H, d), device=dev)
+    kn = torch.randn((S, Hkv, d), device=dev)
+    vn = torch.randn((S, Hkv, d), device=dev)
+    pos = torch.tensor([L - 2, L - 1], dtype=torch.int32, device=dev)
+    work = pti.attn_workspace(S, H, Hkv, d, L, dev)
+    o = torch.empty_like(q)
+    lib, sp = pti.lib(), pti._stream(stream)
+    ptrs = [((ctypes.c_void_p * S)(*[t.data_ptr() for t in kc[j]]),
+             (ctypes.c_void_p * S)(*[t.data_ptr() for t in vc[j]])) for j in range(n_sets)]
+    for i in range(ISOLATED_CALLS):
+        kp, vp = ptrs[i % n_sets]
+        pti._check(name, lib.pti_attn_decode(q.data_ptr(), kn.data_ptr(), vn.data_ptr(), kp, vp, pos.data_ptr(),
+                                             o.data_ptr(), S, H, Hkv, d, L, work.data_ptr(), work.numel(), sp))
+    torch.cuda.synchronize()
+    log(f"isolated {name}: {ISOLATED_CALLS} calls of {what}, {n_sets} cache sets of {set_bytes} B")
+
+
 def isolated_algo_bytes(name):
     _, _, fmt, n = ISOLATED[name]
+    if fmt == "attn":
+        return attn_algo_bytes(n)
     w = ROWS * (COLS // 32) * (68 if fmt == "ssq" else 34)
     extra = 20 if name == "step" else 0  # guess tokens, argmaxes, accept count
     return w + n * (COLS + ROWS) * 4 + extra
@@ -346,9 +402,11 @@ def isolated_algo_bytes(name):
 def summarize_isolated(name, kt_dir, fetch_dir, write_dir, tcc_dir, sq_dir, out_dir):
     """One call's profile from its --only runs: per-launch kernel time from the
     trace (for the fused step, also the span from the GEMV's start to the
-    verify kernel's end), HBM traffic (FETCH_SIZE, WRITE_SIZE scaled by the
-    counters' reading for torch.neg over 256 MiB in the same run), the L2 hit
-    rate, and SQ counters."""
+    verify kernel's end; for attention, pass 2's time and the span from pass
+    1's start to pass 2's end), HBM traffic (FETCH_SIZE, WRITE_SIZE scaled by
+    the counters' reading for torch.neg over 256 MiB in the same run; for
+    attention both passes), the L2 hit rate, and SQ counters (of the GEMV, or
+    of attention's pass 1)."""
     what, kernel, fmt, n = ISOLATED[name]
     cmds = isolated_cmds(name)
     trace = _csv_rows(kt_dir, "kernel_trace.csv")
@@ -359,16 +417,21 @@ def summarize_isolated(name, kt_dir, fetch_dir, write_dir, tcc_dir, sq_dir, out_
     med = dur[len(dur) // 2]
     avg = sum(dur) / len(dur)
     span = None
-    if name == "step":
-        # the call: the GEMV's start to the verify kernel's end, dispatch by dispatch
+    second = {"step": "verify_keys_kernel"}.get(name, ATTN_COMBINE if fmt == "attn" else None)
+    second_dur = None
+    if second:
+        # the call: the first kernel's start to the second one's end, dispatch by dispatch
         rows = sorted(trace, key=lambda r: int(r["Start_Timestamp"]))
         spans = []
         for i, r in enumerate(rows):
             if _short(r["Kernel_Name"]).endswith(kernel) and i + 1 < len(rows) and \
-                    _short(rows[i + 1]["Kernel_Name"]).endswith("verify_keys_kernel"):
+                    _short(rows[i + 1]["Kernel_Name"]).endswith(second):
                 spans.append((int(rows[i + 1]["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         spans = sorted(spans[10:])
         span = (spans[len(spans) // 2], sum(spans) / len(spans))
+        d2 = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                    for r in trace if _short(r["Kernel_Name"]).endswith(second))[10:]
+        second_dur = d2[len(d2) // 2]
 
     def per_kernel(d, counter):
         acc = {}
@@ -389,6 +452,8 @@ def summarize_isolated(name, kt_dir, fetch_dir, write_dir, tcc_dir, sq_dir, out_
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         acc = per_kernel(d, counter)
         k_kib, k_n = kern_avg(acc, lambda k: k.endswith(kernel))
+        if fmt == "attn":  # the call's traffic: both passes
+            k_kib += kern_avg(acc, lambda k: k.endswith(ATTN_COMBINE))[0]
         c_kib, _ = kern_avg(acc, lambda k: "neg" in k.lower())
         factor = CALIB_BYTES / 1024.0 / c_kib
         traffic[counter] = (k_kib, k_n, factor, int(round(k_kib * 1024 * factor)))
@@ -400,22 +465,28 @@ def summarize_isolated(name, kt_dir, fetch_dir, write_dir, tcc_dir, sq_dir, out_
     for c in SQ_COUNTERS + ("GRBM_GUI_ACTIVE",):
         sq[c] = kern_avg(per_kernel(sq_dir, c), lambda k: k.endswith(kernel))[0]
     fb, wb = traffic["FETCH_SIZE"][3], traffic["WRITE_SIZE"][3]
-    lines = [f"# Isolated profile: {what}, 17408x5120, one MI355X.",
-             f"# {ISOLATED_CALLS} launches, weights rotated over copies past the 256 MB Infinity Cache; durations",
+    where = ("caches rotated over sets past the 256 MB Infinity Cache" if fmt == "attn" else
+             "17408x5120, weights rotated over copies past the 256 MB Infinity Cache")
+    lines = [f"# Isolated profile: {what}, one MI355X.",
+             f"# {ISOLATED_CALLS} launches, {where}; durations",
              "# are per dispatch from the kernel trace (the first 10 dispatches left out); FETCH_SIZE and WRITE_SIZE",
              "# are scaled by their reading for torch.neg over 256 MiB (reads and writes 256 MiB) in the same run.",
              ""] + [f"command_{k}: {v}" for k, v in cmds.items()] + [
-             "kernel_source_sha256: " + kernel_source_hash(), "",
+             "kernel_source_sha256: " + kernel_source_hash(isolated_sources(name)), "",
              f"kernel: {kernel}",
              f"dispatches: {len(disp)}",
              f"duration_us_median: {med:.3f}", f"duration_us_mean: {avg:.3f}",
              f"duration_us_min: {dur[0]:.3f}", f"duration_us_max: {dur[-1]:.3f}"]
     if span:
-        lines += [f"call_span_us_median: {span[0]:.3f}  (GEMV start to verify_keys_kernel end)",
+        if second_dur is not None and fmt == "attn":
+            lines.append(f"second_kernel: {second}  median {second_dur:.3f} us (includes its wait behind pass 1)")
+        lines += [f"call_span_us_median: {span[0]:.3f}  ({kernel} start to {second} end)",
                   f"call_span_us_mean: {span[1]:.3f}"]
     lines += [f"algorithmic_bytes_per_launch: {algo}",
               f"algorithmic_GBps_at_median: {algo / (med * 1e-6) / 1e9:.1f}",
               f"frac_of_8TBps_at_median: {algo / (med * 1e-6) / 1e9 / HBM_PEAK_GBS:.4f}"]
+    if span and fmt == "attn":
+        lines += [f"frac_of_8TBps_at_call_span: {algo / (span[0] * 1e-6) / 1e9 / HBM_PEAK_GBS:.4f}"]
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         k_kib, k_n, factor, b = traffic[counter]
         lines.append(f"{counter.lower()}_kib_per_dispatch: {k_kib:.1f} (x {factor:.4f} calibration = {b} B)")
@@ -427,10 +498,11 @@ def summarize_isolated(name, kt_dir, fetch_dir, write_dir, tcc_dir, sq_dir, out_
     # derived.  A wave64 VALU instruction occupies its SIMD for 4 cycles; the
     # chip has 256 CUs x 4 SIMDs at 2.4 GHz (nominal).  Per weight: lane
     # operations over the weights one launch reads.
-    weights = ROWS * COLS * (2 if fmt == "ssq" else 1)
     simd_cycles = 1024 * med * 1e-6 * 2.4e9
-    lines += [f"valu_lane_ops_per_weight: {sq['SQ_INSTS_VALU'] * 64 / weights:.3f}",
-              f"valu_busy_frac: {sq['SQ_INSTS_VALU'] * 4 / simd_cycles:.4f}  (VALU issue cycles / SIMD cycles at "
+    if fmt != "attn":
+        weights = ROWS * COLS * (2 if fmt == "ssq" else 1)
+        lines.append(f"valu_lane_ops_per_weight: {sq['SQ_INSTS_VALU'] * 64 / weights:.3f}")
+    lines += [f"valu_busy_frac: {sq['SQ_INSTS_VALU'] * 4 / simd_cycles:.4f}  (VALU issue cycles / SIMD cycles at "
               f"the median duration and 2.4 GHz)",
               f"lds_busy_frac: {sq['SQ_INSTS_LDS'] * 64 * 16 / (256 * 128 * med * 1e-6 * 2.4e9):.4f}  (upper bound: "
               f"16 B per lane per LDS instruction at 128 B per CU-cycle)",
@@ -452,7 +524,7 @@ def read_isolated(name):
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
                     kv[k.strip()] = v.strip()
-        if kv.get("kernel_source_sha256") != kernel_source_hash():
+        if kv.get("kernel_source_sha256") != kernel_source_hash(isolated_sources(name)):
             return None
         return kv
     except OSError:
@@ -474,7 +546,10 @@ def isolated_roofline(name, algo_bytes, us):
            "profile": os.path.relpath(isolated_profile_path(name), HERE)}
     if kv:
         out["valu_busy_frac"] = float(kv["valu_busy_frac"].split()[0])
-        out["valu_lane_ops_per_weight"] = float(kv["valu_lane_ops_per_weight"])
+        if "valu_lane_ops_per_weight" in kv:
+            out["valu_lane_ops_per_weight"] = float(kv["valu_lane_ops_per_weight"])
+        if "call_span_us_median" in kv:
+            out["rocprof_call_span_us"] = float(kv["call_span_us_median"].split()[0])
     return out
 
 
@@ -833,6 +908,7 @@ def attention(torch, pti, dev, stream):
         algo = kv_bytes + 2 * S * H * d * 4 + 2 * S * Hkv * d * 4
         out[f"attn_twin_h40_kv8_d128_ctx{L}"] = {
             **st, "kv_bytes": kv_bytes, "algorithmic_bytes": algo, "cache_sets": n_sets,
+            "roofline": isolated_roofline("attn4k" if L == 4096 else "attn32k", algo, st["median_us"]),
             "GBps": round(algo / (st["median_us"] * 1e-6) / 1e9, 1),
             "frac_of_hbm_peak": round(algo / (st["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "graph_frac_of_hbm_peak": round(algo / (st["graph_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}

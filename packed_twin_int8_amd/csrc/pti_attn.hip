@@ -159,9 +159,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     constexpr int IT = KPW / RPI;               // loads per wave per tile
     constexpr int KSTEPS = D / 32;              // MFMA steps over the dimensions (scores)
     constexpr int NB = D / 16;                  // 16-dimension output blocks (weighted V)
-    constexpr int PITCH = 2 * D + 16;           // LDS row pitch of the K and V rows, bytes
+    // LDS row pitch of the K and V rows, bytes: 8 banks (of 64) past a row's
+    // length, so the K operand reads (8 lanes per cycle, 16 B each, one row
+    // apiece) and the transposed V reads (16 lanes, 8 B each, over 4 rows) of a
+    // cycle all fall in different banks
+    constexpr int PITCH = 2 * D + 32;
+    constexpr int OWP = D + 8;                  // park pitch per head, floats: the four k groups' heads
+                                                // (2 apart) land 16 banks apart
     static_assert(KPW == 32, "tile shape");
-    static_assert(G * D * 4 <= KPW * PITCH, "a wave's weighted V fits its own rows' LDS");
+    static_assert(G * OWP * 4 <= KPW * PITCH, "a wave's weighted V fits its own rows' LDS");
     // per wave: its 32 K rows, then its 32 V rows, then its weighted V [G][D]
     __shared__ __attribute__((aligned(16))) uint8_t tile[kChunk * PITCH];
     __shared__ float wred[2][NW][8];  // per wave and head: max, then exp-sum
@@ -357,14 +363,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    float *ow = reinterpret_cast<float *>(rows);  // [G][D]
+    float *ow = reinterpret_cast<float *>(rows);  // [G][OWP]
 #pragma unroll
     for (int j = 0; j < NB; j++)
 #pragma unroll
         for (int u = 0; u < 2; u++) {
             const int h = 2 * kg + u;
             if (h < G)
-                ow[h * D + 16 * j + n] = ov[j][u];
+                ow[h * OWP + 16 * j + n] = ov[j][u];
         }
     __syncthreads();  // (2) every wave's weighted V and exp-sums
 
@@ -376,7 +382,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         float v = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; w++)
-            v += reinterpret_cast<const float *>(tile + w * KPW * PITCH)[o];
+            v += reinterpret_cast<const float *>(tile + w * KPW * PITCH)[h * OWP + dd];
         a.part[(((size_t)s * a.H + (size_t)g * G + h) * a.n_chunks + c) * D + dd] = v;
     }
     if (tid < G) {

@@ -35,23 +35,29 @@ KEYS = "void (anonymous namespace)::verify_keys_kernel(unsigned long long const*
 NEG = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>(int, float*)"
 
 
+COMBINE = "void (anonymous namespace)::attn_combine_kernel<128>((anonymous namespace)::AttnArgs)"
+
+
 def _isolated_dirs(tmp_path, name, kernel, dur_ns, fetch_kib, write_kib, hits, misses, valu):
     kt, fe, wr, sq = (str(tmp_path / name / n) for n in ("kt", "fetch", "write", "sq"))
     tr_hdr = ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+    second = {"step": KEYS}.get(name, COMBINE if name.startswith("attn") else None)
     rows, t = [], 1000
     for _ in range(bench.ISOLATED_CALLS):
         rows.append(["KERNEL_DISPATCH", kernel, t, t + dur_ns])
-        if name == "step":
-            rows.append(["KERNEL_DISPATCH", KEYS, t + dur_ns + 500, t + dur_ns + 2500])
+        if second:
+            rows.append(["KERNEL_DISPATCH", second, t + dur_ns + 500, t + dur_ns + 2500])
         t += 100000
     _write_csv(os.path.join(kt, "box", "kt_kernel_trace.csv"), tr_hdr, rows)
     hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
     calib_kib = bench.CALIB_BYTES / 1024 / 2.0  # the counter reads half the true bytes
+    extra = [[COMBINE, "FETCH_SIZE", 10.0], [COMBINE, "WRITE_SIZE", 4.0]] if name.startswith("attn") else []
     _write_csv(os.path.join(fe, "box", "f_counter_collection.csv"), hdr,
-               [[kernel, "FETCH_SIZE", fetch_kib], [kernel, "FETCH_SIZE", fetch_kib + 2], [NEG, "FETCH_SIZE", calib_kib]])
+               [[kernel, "FETCH_SIZE", fetch_kib], [kernel, "FETCH_SIZE", fetch_kib + 2], [NEG, "FETCH_SIZE", calib_kib]]
+               + extra[:1])
     _write_csv(os.path.join(wr, "box", "w_counter_collection.csv"), hdr,
                [[kernel, "WRITE_SIZE", write_kib], [NEG, "WRITE_SIZE", calib_kib],
-                [kernel, "TCC_HIT_sum", hits], [kernel, "TCC_MISS_sum", misses]])
+                [kernel, "TCC_HIT_sum", hits], [kernel, "TCC_MISS_sum", misses]] + extra[1:])
     _write_csv(os.path.join(sq, "box", "s_counter_collection.csv"), hdr,
                [[kernel, c, valu if c == "SQ_INSTS_VALU" else 1000.0]
                 for c in bench.SQ_COUNTERS + ("GRBM_GUI_ACTIVE",)])
@@ -79,8 +85,30 @@ def test_summarize_isolated(tmp_path, monkeypatch, name):
     r = bench.isolated_roofline(name, bench.isolated_algo_bytes(name), 25.0)
     assert r["traffic"] == int(kv["traffic_bytes_per_launch"]) and r["rocprof_median_us"] == 20.0
     # a profile taken from other kernel sources is not used
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda *a: "0" * 64)
     assert bench.read_isolated(name) is None and bench.isolated_roofline(name, 1, 1.0)["traffic"] is None
+
+
+def test_summarize_isolated_attention(tmp_path, monkeypatch):
+    """Attention: pass 1's time, pass 2's time and the call span, traffic of
+    both passes, no per-weight line, keyed to the attention source."""
+    name = "attn4k"
+    kernel = "void (anonymous namespace)::" + bench.ISOLATED[name][1] + "((anonymous namespace)::AttnArgs)"
+    kt, fe, wr, sq = _isolated_dirs(tmp_path, name, kernel, 10000, 1000.0, 100.0, 25.0, 75.0, 3.2e6)
+    out = str(tmp_path / "out")
+    bench.summarize_isolated(name, kt, fe, wr, wr, sq, out)
+    orig = bench.isolated_profile_path
+    monkeypatch.setattr(bench, "isolated_profile_path", lambda n: os.path.join(out, os.path.basename(orig(n))))
+    kv = bench.read_isolated(name)
+    assert kv is not None and float(kv["duration_us_median"]) == 10.0
+    assert float(kv["call_span_us_median"].split()[0]) == 12.5  # pass 1 start to pass 2 end
+    assert int(kv["fetch_bytes_per_launch"]) == round((1001.0 + 10.0) * 1024 * 2)
+    assert int(kv["write_bytes_per_launch"]) == round((100.0 + 4.0) * 1024 * 2)
+    assert "valu_lane_ops_per_weight" not in kv and "valu_busy_frac" in kv
+    assert kv["kernel_source_sha256"] == bench.kernel_source_hash(bench.ATTN_SOURCES)
+    assert bench.isolated_algo_bytes(name) == bench.attn_algo_bytes(4096) == 33648640
+    r = bench.isolated_roofline(name, bench.attn_algo_bytes(4096), 13.0)
+    assert r["rocprof_call_span_us"] == 12.5 and r["traffic"] == int(kv["traffic_bytes_per_launch"])
 
 
 def test_summarize_isolated_requires_every_dispatch(tmp_path):
@@ -100,7 +128,7 @@ def test_summarize_kt(tmp_path, monkeypatch):
     bench.summarize_kt(kt, out)
     monkeypatch.setattr(bench, "KT_FILE", os.path.join(out, os.path.basename(bench.KT_FILE)))
     assert bench.read_kt_avg(bench.STEP_KERNEL) == 33.6
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda *a: "0" * 64)
     assert bench.read_kt_avg(bench.STEP_KERNEL) is None
 
 
