@@ -1096,31 +1096,28 @@ __global__ __launch_bounds__(64 * BW) void gemv_ssq_split_kernel(SplitArgs sa)
 
 // The rest of the fused verify: argmax of each twin from the workgroups' keys
 // (the largest key is the largest value, the lowest row among equals) and the
-// accept count of twin B's guess.  One workgroup of 256 threads.
-__global__ __launch_bounds__(256) void verify_keys_kernel(const unsigned long long *__restrict__ keys, int n_groups,
-                                                          const int32_t *__restrict__ tokens_in,
-                                                          int32_t *__restrict__ argmax_out,
-                                                          int32_t *__restrict__ accept_out)
+// accept count of twin B's guess.  One wave: each lane takes the maximum of
+// its workgroups' keys (all its loads in flight together), then the wave's.
+__global__ __launch_bounds__(64) void verify_keys_kernel(const unsigned long long *__restrict__ keys, int n_groups,
+                                                         const int32_t *__restrict__ tokens_in,
+                                                         int32_t *__restrict__ argmax_out,
+                                                         int32_t *__restrict__ accept_out)
 {
-    __shared__ unsigned long long part[2][4];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int lane = threadIdx.x;
     unsigned long long k[2] = {0, 0};
-    for (int i = tid; i < n_groups; i += 256) {
-        k[0] = std::max(k[0], keys[2 * i]);
-        k[1] = std::max(k[1], keys[2 * i + 1]);
+#pragma unroll 4
+    for (int i = lane; i < n_groups; i += 64) {
+        const ulonglong2 v = reinterpret_cast<const ulonglong2 *>(keys)[i];
+        k[0] = std::max(k[0], (unsigned long long)v.x);
+        k[1] = std::max(k[1], (unsigned long long)v.y);
     }
     k[0] = wave_umax(k[0]);
     k[1] = wave_umax(k[1]);
-    if (lane == 63)
-        part[0][wv] = k[0], part[1][wv] = k[1];
-    __syncthreads();
-    if (tid == 0) {
+    if (lane == 63) {
         int32_t am[2];
 #pragma unroll
         for (int s = 0; s < 2; s++) {
-            const unsigned long long m =
-                std::max(std::max(part[s][0], part[s][1]), std::max(part[s][2], part[s][3]));
-            am[s] = (int32_t)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
+            am[s] = (int32_t)(0xFFFFFFFFu - (uint32_t)(k[s] & 0xFFFFFFFFull));
             argmax_out[s] = am[s];
         }
         accept_out[0] = 1 + (tokens_in[1] == am[0] ? 1 : 0);
@@ -1189,7 +1186,7 @@ int launch_ssq_split(const GemvArgs &a, const VerifyOut *vo, hipStream_t stream)
         hipLaunchKernelGGL((gemv_ssq_split_kernel<T, NS, VERIFY>), dim3((unsigned)grid),
                            dim3((unsigned)(64 * sa.P * sa.Q)), lds, stream, sa);
     if constexpr (VERIFY)
-        hipLaunchKernelGGL(verify_keys_kernel, dim3(1), dim3(256), 0, stream, vo->keys, (int)grid, vo->tokens_in,
+        hipLaunchKernelGGL(verify_keys_kernel, dim3(1), dim3(64), 0, stream, vo->keys, (int)grid, vo->tokens_in,
                            vo->argmax_out, vo->accept_out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
