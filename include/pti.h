@@ -33,9 +33,13 @@
  *   - Matrices are row-major, little-endian, with no header or padding: row r
  *     holds cols/32 consecutive blocks, block b covering columns 32b..32b+31.
  *     A weight's value is scale * int8 (symmetric, no zero point).
- *   - Ownership: the caller owns every buffer.  The library allocates no memory,
- *     keeps no state other than a thread-local copy of the last HIP error, and
- *     may be called from several threads.
+ *   - Ownership: the caller owns every buffer.  The library makes no
+ *     allocation calls; its only device memory of its own is the 64 KB
+ *     file-scope array of pti_sample_verify_static (one per GPU, from load
+ *     time).  Its other state: a thread-local copy of the last HIP error, a
+ *     thread-local cache of the current device's CU count, per-kernel flags
+ *     of the devices whose launch attributes are set, and that array's
+ *     address per device.  It may be called from several threads.
  *   - Device calls take device pointers and a HIP stream (a hipStream_t passed
  *     as void*, NULL = the default stream).  They enqueue work and return
  *     without synchronising; outputs are overwritten, never accumulated into.
