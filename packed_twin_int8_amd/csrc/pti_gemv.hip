@@ -132,12 +132,16 @@ struct GemvArgs {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Address of row `row` (wave-uniform in every caller, so this is scalar work).
+// A launch of one matrix has seg_end[0] = INT64_MAX and skips the segment
+// search, whose 64-bit compares would otherwise run on the VALU at every pass.
 __device__ __forceinline__ const uint8_t *row_addr(const GemvArgs &a, int64_t row)
 {
     uintptr_t b = a.seg_base[0];
+    if (a.seg_end[0] != INT64_MAX) {  // a grouped launch (uniform)
 #pragma unroll
-    for (int m = 1; m < kMaxSegs; m++)
-        b = row >= a.seg_end[m - 1] ? a.seg_base[m] : b;
+        for (int m = 1; m < kMaxSegs; m++)
+            b = row >= a.seg_end[m - 1] ? a.seg_base[m] : b;
+    }
     return reinterpret_cast<const uint8_t *>(b + (uintptr_t)row * (uintptr_t)a.row_bytes);
 }
 
@@ -364,6 +368,79 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+// Values carried into tree_sums: n rounded up to a power of two.
+constexpr int tree_width(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
+
+// Lane i gets the value of lane i ^ 4: two row shifts by 4, each writing the
+// banks (groups of four lanes) it serves.
+__device__ __forceinline__ float xor4(float v)
+{
+    const int x = __builtin_bit_cast(int, v);
+    int t = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xf, 0x5, false);  // banks 0, 2: row_shl 4
+    t = __builtin_amdgcn_update_dpp(t, x, 0x114, 0xf, 0xa, false);      // banks 1, 3: row_shr 4
+    return __builtin_bit_cast(float, t);
+}
+
+// The sums over the 64 lanes of N values at once (N <= 8), each by the tree
+// of wave_sum: lanes paired by bit 0 of the lane index, then by bit 1, ...,
+// then by bit 5.  Addition being commutative, only that pairing fixes the
+// result, so each sum has the bits wave_sum gives it.  The stages for the
+// bits below log2(V) (V = tree_width(N)) also halve the values a lane
+// carries: of each pair of values (2t, 2t + 1) a lane keeps the one its bit
+// selects and adds its partner's copy of it, so V values cost about as much
+// as two plain trees.  Later stages carry one value: the row shifts of
+// wave_sum (right in the lanes whose bits log2(V)..3 are set), then the row
+// and half-wave swaps for bits 4 and 5.  The total of value k lands in lane
+// 16 - V + k of every row.  Works in place on c (destroyed).
+template <int N>
+__device__ __forceinline__ float tree_sums(float (&c)[N], int lane)
+{
+    constexpr int V = tree_width(N);
+    constexpr int LV = V == 8 ? 3 : V == 4 ? 2 : V == 2 ? 1 : 0;
+    // values past N (three streams) are zeros; pair t writes c[t] after
+    // reading c[2t] and c[2t + 1]
+    auto at = [&](int k) { return k < N ? c[k] : 0.f; };
+    if constexpr (LV > 0) {
+        const bool hi = lane & 1;
+#pragma unroll
+        for (int t = 0; t < V / 2; t++) {
+            const float e0 = at(2 * t), e1 = at(2 * t + 1);
+            const float keep = hi ? e1 : e0, send = hi ? e0 : e1;
+            if (t < N)
+                c[t] = keep + dpp<0xB1, 0xf, false>(send);  // quad_perm [1, 0, 3, 2]
+        }
+    }
+    if constexpr (LV > 1) {
+        const bool hi = lane & 2;
+#pragma unroll
+        for (int t = 0; t < V / 4; t++) {
+            const float keep = hi ? c[2 * t + 1] : c[2 * t], send = hi ? c[2 * t] : c[2 * t + 1];
+            c[t] = keep + dpp<0x4E, 0xf, false>(send);  // quad_perm [2, 3, 0, 1]
+        }
+    }
+    if constexpr (LV > 2) {
+        const bool hi = lane & 4;
+        const float keep = hi ? c[1] : c[0], send = hi ? c[0] : c[1];
+        c[0] = keep + xor4(send);
+    }
+    float x = c[0];
+    if constexpr (LV <= 0)
+        x = x + dpp<0x111, 0xf, true>(x);
+    if constexpr (LV <= 1)
+        x = x + dpp<0x112, 0xf, true>(x);
+    if constexpr (LV <= 2)
+        x = x + dpp<0x114, 0xf, true>(x);
+    x = x + dpp<0x118, 0xf, true>(x);
+    // the swaps return two vectors; each element is cast to a scalar before
+    // its bits are read
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                      false, false);
+    x = __builtin_bit_cast(float, (unsigned)r16[0]) + __builtin_bit_cast(float, (unsigned)r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                      false, false);
+    return __builtin_bit_cast(float, (unsigned)r32[0]) + __builtin_bit_cast(float, (unsigned)r32[1]);
+}
+
 // One step of an unsigned 64-bit max over lanes: DPP moves the low and high
 // words with the same control; lanes DPP does not write see 0 (the identity).
 template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
@@ -562,16 +639,18 @@ struct Wave {
             }
         }
         if (cr == a.rounds - 1) {  // the pass's rows are complete
-            // The sums move to lane (row in group) of outv; they are stored
-            // after the loop, so the loop holds no vector stores (stores share
-            // the counter that the weight-load waits use).
+            // The pass's R x NS sums go through one tree_sums; each moves to
+            // lane (row in group) of outv, stored after the loop, so the loop
+            // holds no vector stores (stores share the counter that the
+            // weight-load waits use).
             const int j0 = (cp - gp0) * R;
+            constexpr int V = tree_width(R * NS);
+            const int tot = __builtin_bit_cast(int, tree_sums<R * NS>(reinterpret_cast<float (&)[R * NS]>(acc), lane));
 #pragma unroll
             for (int r = 0; r < R; r++) {
 #pragma unroll
                 for (int s = 0; s < NS; s++) {
-                    const float v = wave_sum(acc[r][s]);
-                    const float t = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+                    const float t = __builtin_bit_cast(float, __builtin_amdgcn_readlane(tot, 16 - V + r * NS + s));
                     outv[s] = lane == j0 + r ? t : outv[s];
                     acc[r][s] = 0.f;
                 }
