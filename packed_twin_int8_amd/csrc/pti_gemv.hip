@@ -55,9 +55,10 @@
 //   * Signed bytes convert to fp32 with one SDWA v_cvt_f32_i32 each.  Per unit
 //     and stream the products are summed in fp32 in column order, scaled by
 //     the block's f16 scale with one FMA into the lane's accumulator, and the
-//     64 lanes reduce with a fixed DPP tree.  Finished rows park in one lane
-//     each of an output register and are stored after the loop.  No MFMA: this is a matrix-vector
-//     product, one FMA per weight and stream.
+//     64 lanes reduce by a fixed tree (tree_sums: all of a wave's sums in one
+//     pass of DPP and lane swaps).  Finished rows park in one lane each of an
+//     output register and are stored after the loop.  No MFMA: this is a
+//     matrix-vector product, one FMA per weight and stream.
 //   * A row's operation order depends only on (rows, cols) and the format: not
 //     on the stream count, the stream's slot, R or the wave count, so a
 //     stream's output is bitwise independent of those.
@@ -355,19 +356,6 @@ __device__ __forceinline__ float dpp(float v)
                                                                  BOUND_ZERO));
 }
 
-// Sum over the 64 lanes; the total lands in lane 63.  Fixed tree: row_shr 1, 2,
-// 4, 8 within each 16-lane row, then row_bcast15 and row_bcast31 across rows.
-__device__ __forceinline__ float wave_sum(float v)
-{
-    v = v + dpp<0x111, 0xf, true>(v);
-    v = v + dpp<0x112, 0xf, true>(v);
-    v = v + dpp<0x114, 0xf, true>(v);
-    v = v + dpp<0x118, 0xf, true>(v);
-    v = v + dpp<0x142, 0xa, false>(v);
-    v = v + dpp<0x143, 0xc, false>(v);
-    return v;
-}
-
 // Values carried into tree_sums: n rounded up to a power of two.
 constexpr int tree_width(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
 
@@ -381,15 +369,16 @@ __device__ __forceinline__ float xor4(float v)
     return __builtin_bit_cast(float, t);
 }
 
-// The sums over the 64 lanes of N values at once (N <= 8), each by the tree
-// of wave_sum: lanes paired by bit 0 of the lane index, then by bit 1, ...,
-// then by bit 5.  Addition being commutative, only that pairing fixes the
-// result, so each sum has the bits wave_sum gives it.  The stages for the
-// bits below log2(V) (V = tree_width(N)) also halve the values a lane
+// The sums over the 64 lanes of N values at once (N <= 8), each by the fixed
+// lane tree of every GEMV kernel here: the balanced binary tree that pairs
+// lanes by bit 0 of the lane index, then by bit 1, ..., then by bit 5.
+// Addition being commutative, that pairing alone fixes each sum's bits, so
+// every kernel and stream count gives a row the same bits.  The stages for
+// the bits below log2(V) (V = tree_width(N)) also halve the values a lane
 // carries: of each pair of values (2t, 2t + 1) a lane keeps the one its bit
 // selects and adds its partner's copy of it, so V values cost about as much
-// as two plain trees.  Later stages carry one value: the row shifts of
-// wave_sum (right in the lanes whose bits log2(V)..3 are set), then the row
+// as two single-value trees.  Later stages carry one value: row shifts by 1,
+// 2, 4, 8 (right in the lanes whose bits log2(V)..3 are set), then the row
 // and half-wave swaps for bits 4 and 5.  The total of value k lands in lane
 // 16 - V + k of every row.  Works in place on c (destroyed).
 template <int N>
@@ -453,7 +442,8 @@ __device__ __forceinline__ unsigned long long umax_dpp(unsigned long long k)
     return o > k ? o : k;
 }
 
-// Unsigned 64-bit max over the 64 lanes, in lane 63: the tree of wave_sum.
+// Unsigned 64-bit max over the 64 lanes, in lane 63: row shifts by 1, 2, 4, 8
+// within each 16-lane row, then row_bcast15 and row_bcast31 across rows.
 __device__ __forceinline__ unsigned long long wave_umax(unsigned long long k)
 {
     k = umax_dpp<0x111, 0xf, true>(k);
@@ -942,7 +932,7 @@ GemvArgs make_args(const void *w, int64_t rows, int64_t cols)
 // A wave always handles the same column slice, so it loads its T rounds of x
 // (T * 8 columns per lane, every stream) once into registers: no LDS staging,
 // no LDS reads in the loop.  Per step it sums its rounds per lane, reduces
-// over its 64 lanes (the fixed DPP tree) and parks the partial in LDS; every
+// over its 64 lanes (the fixed lane tree) and parks the partial in LDS; every
 // S steps the workgroup sums the Q partials of each finished row in slice
 // order and stores the row.  A row's order of operations depends only on
 // (rows, cols).
@@ -1049,20 +1039,25 @@ __global__ __launch_bounds__(64 * BW) void gemv_ssq_split_kernel(SplitArgs sa)
                 }
             }
             const float da = f16_lo(u.sc), db = f16_hi(u.sc);
+            // fma into +0 at the first round, as the Q8 kernels do: the
+            // product is rounded before it enters the lane tree, so no
+            // contraction of it into the tree's first add can change the bits
 #pragma unroll
             for (int s = 0; s < NS; s++) {
                 const float d = (s & 1) ? db : da;
-                acc[s] = tt == 0 ? d * bs[s] : __builtin_fmaf(d, bs[s], acc[s]);
+                acc[s] = __builtin_fmaf(d, bs[s], tt == 0 ? 0.f : acc[s]);
             }
             __builtin_amdgcn_sched_barrier(0);
             load_round(rs_next, tt, nxt[tt]);
             __builtin_amdgcn_sched_barrier(0);
         }
         const int slot = (half * S + local) * P + p;  // row slot in the double buffer
-#pragma unroll
-        for (int s = 0; s < NS; s++) {
-            const float v = wave_sum(acc[s]);
-            if (lane == 63 && t < steps)
+        {
+            // one tree for every stream; stream s's total lands in lane 64 - V + s
+            constexpr int V = tree_width(NS);
+            const float v = tree_sums<NS>(acc, lane);
+            const int s = lane - (64 - V);
+            if (s >= 0 && s < NS && t < steps)
                 part[(slot * Q + q) * NS + s] = v;
         }
     };
@@ -1298,7 +1293,7 @@ int launch_ssq_split(const GemvArgs &a, const VerifyOut *vo, hipStream_t stream)
 // streams (up to four) keeps its x slice in registers (80 per stream at
 // T = 5), which a bound of four waves per workgroup leaves room for.  A
 // stream's chain (16 products in column order per unit, scaled into the
-// lane's sum per round, the DPP tree, the Q partials in slice order) is the
+// lane's sum per round, the lane tree, the Q partials in slice order) is the
 // same whatever NS is.
 constexpr int kQ8SplitMaxQ = 4;
 constexpr int64_t kQ8SplitMaxRows = 8192;
@@ -1365,10 +1360,12 @@ __global__ __launch_bounds__(64 * 4) void gemv_q8_split_kernel(SplitArgs sa)
             __builtin_amdgcn_sched_barrier(0);
         }
         const int slot = (half * S + local) * P + p;
-#pragma unroll
-        for (int s = 0; s < NS; s++) {
-            const float v = wave_sum(acc[s]);
-            if (lane == 63 && t < steps)
+        {
+            // one tree for every stream; stream s's total lands in lane 64 - V + s
+            constexpr int V = tree_width(NS);
+            const float v = tree_sums<NS>(acc, lane);
+            const int s = lane - (64 - V);
+            if (s >= 0 && s < NS && t < steps)
                 part[(slot * Q + q) * NS + s] = v;
         }
     };
