@@ -77,13 +77,13 @@
 // row and when), so they may differ between stream counts; the values are
 // measured optima and can be overridden at build time.
 #ifndef PTI_Q8_N1_CFG
-#define PTI_Q8_N1_CFG 12, 4, 1
+#define PTI_Q8_N1_CFG 12, 1, 1
 #endif
 #ifndef PTI_Q8_N2_CFG
-#define PTI_Q8_N2_CFG 12, 4, 1
+#define PTI_Q8_N2_CFG 16, 1, 1
 #endif
 #ifndef PTI_Q8_N4_CFG
-#define PTI_Q8_N4_CFG 16, 4, 2
+#define PTI_Q8_N4_CFG 16, 1, 2
 #endif
 #ifndef PTI_SSQ_ROWWISE_CFG
 #define PTI_SSQ_ROWWISE_CFG 16, 3, 1
@@ -384,6 +384,7 @@ __device__ __forceinline__ float xor4(float v)
 template <int N>
 __device__ __forceinline__ float tree_sums(float (&c)[N], int lane)
 {
+    static_assert(N >= 1 && N <= 8, "tree_sums carries at most eight values");
     constexpr int V = tree_width(N);
     constexpr int LV = V == 8 ? 3 : V == 4 ? 2 : V == 2 ? 1 : 0;
     // values past N (three streams) are zeros; pair t writes c[t] after
