@@ -456,7 +456,7 @@ __device__ __forceinline__ unsigned long long wave_umax(unsigned long long k)
     return k;
 }
 
-template <int FMT, int NSP, int NS, int R, bool ROWS4, int kD>
+template <int FMT, int NSP, int NS, int R, bool ROWS4, int kD, bool SEG>
 struct Wave {
     static constexpr int UC = unit_cols<FMT>();
     static constexpr int CG = UC / 4;
@@ -499,6 +499,17 @@ struct Wave {
                 acc[r][s] = 0.f;
     }
 
+    // Address of a row: a launch of one matrix (SEG false) needs no segment
+    // search, whose selects and 64-bit compares would otherwise run at every
+    // pass on the CU's one scalar unit, shared by its 16 waves.
+    __device__ __forceinline__ uintptr_t row_ptr(int64_t row) const
+    {
+        if constexpr (SEG)
+            return reinterpret_cast<uintptr_t>(row_addr(a, row));
+        else
+            return a.seg_base[0] + (uintptr_t)row * (uintptr_t)a.row_bytes;
+    }
+
     __device__ __forceinline__ int rows_in(int pass) const { return min(R, nrow - pass * R); }
 
     // Buffer resources over the rows of pass p (dword-aligned bases).  Rows
@@ -511,7 +522,7 @@ struct Wave {
         const int nr_in = p < p1 ? rows_in(p) : 0;
 #pragma unroll
         for (int r = 0; r < R; r++) {
-            const uintptr_t q = reinterpret_cast<uintptr_t>(row_addr(a, first + ((int64_t)p * R + r) * stride));
+            const uintptr_t q = row_ptr(first + ((int64_t)p * R + r) * stride);
             const uint32_t e0 = (uint32_t)(q & 3);
             icls[r] = ROWS4 ? 0 : (int)(e0 >> 1);
             const uint32_t n = r < nr_in ? e0 + (uint32_t)a.row_bytes : 0u;
@@ -526,7 +537,7 @@ struct Wave {
         if constexpr (!ROWS4) {
 #pragma unroll
             for (int r = 0; r < R; r++)
-                ccls[r] = (int)((reinterpret_cast<uintptr_t>(row_addr(a, first + ((int64_t)p * R + r) * stride)) >> 1) &
+                ccls[r] = (int)((row_ptr(first + ((int64_t)p * R + r) * stride) >> 1) &
                                 1);
         }
     }
@@ -746,7 +757,7 @@ struct Wave {
     }
 };
 
-template <int FMT, int NSP, int NS, int R, bool ROWS4, int W, int D>
+template <int FMT, int NSP, int NS, int R, bool ROWS4, int W, int D, bool SEG>
 __global__ __launch_bounds__(64 * W) void gemv_kernel(GemvArgs a)
 {
     static_assert(W % 4 == 0, "waves per workgroup must fill the four SIMDs evenly");
@@ -772,7 +783,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemvArgs a)
     const int j = wv >> 2;
     const int64_t n_simd_rows = sg < a.rows ? (a.rows - sg + nsimd - 1) / nsimd : 0;
     const int nrow = (int)(n_simd_rows > j ? (n_simd_rows - j + kPerSimd - 1) / kPerSimd : 0);
-    Wave<FMT, NSP, NS, R, ROWS4, D> w(a, xs, lane, sg + (int64_t)j * nsimd, (int64_t)kPerSimd * nsimd, nrow);
+    Wave<FMT, NSP, NS, R, ROWS4, D, SEG> w(a, xs, lane, sg + (int64_t)j * nsimd, (int64_t)kPerSimd * nsimd, nrow);
 
     if (a.chunk_rounds >= a.rounds) {
         // All of x fits: stage it once, then run every pass.  The x loads go
@@ -872,23 +883,25 @@ int launch(const GemvArgs &a0, hipStream_t stream)
     // VALU-bound (four streams), so spreading the rows over more SIMDs is what
     // shortens it; a workgroup without rows only stages x.
     const int64_t grid = std::min<int64_t>(cus, a.rows);
-    auto kern = gemv_kernel<FMT, NSP, NS, R, ROWS4, kWaves, cfg.prefetch>;
-    // The dynamic-LDS limit is a per-device attribute of the kernel: set it once on each device this
+    const bool seg = a.seg_end[0] != INT64_MAX;  // a grouped launch: rows in several matrices
+    auto kern = seg ? gemv_kernel<FMT, NSP, NS, R, ROWS4, kWaves, cfg.prefetch, true>
+                    : gemv_kernel<FMT, NSP, NS, R, ROWS4, kWaves, cfg.prefetch, false>;
+    // The dynamic-LDS limit is a per-device attribute of the kernel: set it once on each device each
     // instance runs on (one bit per device; two threads racing both set it, which is harmless).
-    static std::atomic<uint64_t> attr_devs{0};
+    static std::atomic<uint64_t> attr_devs[2] = {0, 0};
     int dev = 0;
     if (hipError_t e = hipGetDevice(&dev); e != hipSuccess || dev < 0 || dev >= 64) {
         pti::set_hip_error(e != hipSuccess ? e : hipErrorInvalidDevice);
         return PTI_ERR_HIP;
     }
-    if (!(attr_devs.load(std::memory_order_acquire) >> dev & 1)) {
+    if (!(attr_devs[seg].load(std::memory_order_acquire) >> dev & 1)) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, kXLds);
         if (e != hipSuccess) {
             pti::set_hip_error(e);
             return PTI_ERR_HIP;
         }
-        attr_devs.fetch_or(uint64_t{1} << dev, std::memory_order_acq_rel);
+        attr_devs[seg].fetch_or(uint64_t{1} << dev, std::memory_order_acq_rel);
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
     hipError_t e = hipGetLastError();
