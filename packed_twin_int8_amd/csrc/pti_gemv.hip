@@ -70,6 +70,7 @@
 
 #include "pti_internal.h"
 #include "pti_norm.h"
+#include "pti_silu.h"
 
 // Per-wave-row kernel geometry by format and stream count: waves per
 // workgroup (a multiple of 4), steps of loads in flight, rows per wave.  None
@@ -456,8 +457,19 @@ __device__ __forceinline__ unsigned long long wave_umax(unsigned long long k)
     return k;
 }
 
-template <int FMT, int NSP, int NS, int R, bool ROWS4, int kD, bool SEG>
+// Row addressing of the per-wave-row kernel.
+//   kAmFlat: one matrix, row r at seg_base[0] + r * row_bytes.
+//   kAmSeg:  a grouped launch, rows stacked over the segments (row_addr).
+//   kAmPair: the gate and up matrices of an MLP (seg_base[0], seg_base[1]);
+//            a.rows counts row pairs, a wave's pass p takes row u of each
+//            (R = 2: gate in row slot 0, up in slot 1) and the pair leaves
+//            as y[s][u] = silu(gate) * up, so the activation needs no launch
+//            of its own and gate, up are never stored.
+constexpr int kAmFlat = 0, kAmSeg = 1, kAmPair = 2;
+
+template <int FMT, int NSP, int NS, int R, bool ROWS4, int kD, int AM>
 struct Wave {
+    static_assert(AM != kAmPair || R == 2, "a pass takes one gate row and one up row");
     static constexpr int UC = unit_cols<FMT>();
     static constexpr int CG = UC / 4;
 
@@ -469,7 +481,9 @@ struct Wave {
     int nrow, npass;
     LaneOffsets lo;
     float acc[R][NS];
-    float outv[NS];  // finished rows of the current group, row j of the group in lane j
+    // finished rows of the current group, row j of the group in lane j of
+    // outv[0] (pairs: pair j's gate in lane j of outv[0], its up in outv[1])
+    float outv[AM == kAmPair ? 2 : 1][NS];
     int gp0;         // first pass of the current group
     Unit bufs[kD + 1][R];
 
@@ -490,7 +504,7 @@ struct Wave {
                                     int64_t stride_, int nrow_)
         : a(a_), xs(xs_), lane(lane_), first(first_), stride(stride_), nrow(nrow_)
     {
-        npass = (nrow + R - 1) / R;
+        npass = AM == kAmPair ? nrow : (nrow + R - 1) / R;
         lo = lane_offsets(lane_);
 #pragma unroll
         for (int r = 0; r < R; r++)
@@ -504,13 +518,25 @@ struct Wave {
     // pass on the CU's one scalar unit, shared by its 16 waves.
     __device__ __forceinline__ uintptr_t row_ptr(int64_t row) const
     {
-        if constexpr (SEG)
+        if constexpr (AM == kAmSeg)
             return reinterpret_cast<uintptr_t>(row_addr(a, row));
         else
             return a.seg_base[0] + (uintptr_t)row * (uintptr_t)a.row_bytes;
     }
 
-    __device__ __forceinline__ int rows_in(int pass) const { return min(R, nrow - pass * R); }
+    // Address of row slot r of pass p.
+    __device__ __forceinline__ uintptr_t pass_row_ptr(int p, int r) const
+    {
+        if constexpr (AM == kAmPair)
+            return a.seg_base[r] + (uintptr_t)(first + (int64_t)p * stride) * (uintptr_t)a.row_bytes;
+        else
+            return row_ptr(first + ((int64_t)p * R + r) * stride);
+    }
+
+    __device__ __forceinline__ int rows_in(int pass) const
+    {
+        return AM == kAmPair ? R : min(R, nrow - pass * R);
+    }
 
     // Buffer resources over the rows of pass p (dword-aligned bases).  Rows
     // past the pass's last, or a pass past the segment, get empty resources:
@@ -522,7 +548,7 @@ struct Wave {
         const int nr_in = p < p1 ? rows_in(p) : 0;
 #pragma unroll
         for (int r = 0; r < R; r++) {
-            const uintptr_t q = row_ptr(first + ((int64_t)p * R + r) * stride);
+            const uintptr_t q = pass_row_ptr(p, r);
             const uint32_t e0 = (uint32_t)(q & 3);
             icls[r] = ROWS4 ? 0 : (int)(e0 >> 1);
             const uint32_t n = r < nr_in ? e0 + (uint32_t)a.row_bytes : 0u;
@@ -537,8 +563,7 @@ struct Wave {
         if constexpr (!ROWS4) {
 #pragma unroll
             for (int r = 0; r < R; r++)
-                ccls[r] = (int)((row_ptr(first + ((int64_t)p * R + r) * stride) >> 1) &
-                                1);
+                ccls[r] = (int)((pass_row_ptr(p, r) >> 1) & 1);
         }
     }
 
@@ -645,15 +670,17 @@ struct Wave {
             // lane (row in group) of outv, stored after the loop, so the loop
             // holds no vector stores (stores share the counter that the
             // weight-load waits use).
-            const int j0 = (cp - gp0) * R;
             constexpr int V = tree_width(R * NS);
             const int tot = __builtin_bit_cast(int, tree_sums<R * NS>(reinterpret_cast<float (&)[R * NS]>(acc), lane));
 #pragma unroll
             for (int r = 0; r < R; r++) {
+                // the lane and outv slot of row slot r
+                const int j = AM == kAmPair ? cp - gp0 : (cp - gp0) * R + r;
+                float(&o)[NS] = outv[AM == kAmPair ? r : 0];
 #pragma unroll
                 for (int s = 0; s < NS; s++) {
                     const float t = __builtin_bit_cast(float, __builtin_amdgcn_readlane(tot, 16 - V + r * NS + s));
-                    outv[s] = lane == j0 + r ? t : outv[s];
+                    o[s] = lane == j ? t : o[s];
                     acc[r][s] = 0.f;
                 }
             }
@@ -733,31 +760,43 @@ struct Wave {
         }
     }
 
-    // Passes per output group: a group's rows fit one lane each of outv.
-    static constexpr int kGroupPasses = 64 / R;
+    // Passes per output group: a group's rows (pairs) fit one lane each of outv.
+    static constexpr int kGroupPasses = AM == kAmPair ? 64 : 64 / R;
 
     __device__ __forceinline__ void begin_group(int g0)
     {
         gp0 = g0;
 #pragma unroll
-        for (int s = 0; s < NS; s++)
-            outv[s] = 0.f;
-    }
-
-    // Store the finished rows of the group of passes [gp0, g1).
-    __device__ __forceinline__ void store_group(int g1)
-    {
-        const int nj = min(g1 * R, nrow) - gp0 * R;
-        if (lane < nj) {
-            const int64_t row = first + (int64_t)(gp0 * R + lane) * stride;
+        for (auto &o : outv)
 #pragma unroll
             for (int s = 0; s < NS; s++)
-                a.y[s][row] = a.res[s] ? a.res[s][row] + outv[s] : outv[s];
+                o[s] = 0.f;
+    }
+
+    // Store the finished rows (pairs) of the group of passes [gp0, g1).
+    __device__ __forceinline__ void store_group(int g1)
+    {
+        if constexpr (AM == kAmPair) {
+            const int nj = min(g1, nrow) - gp0;
+            if (lane < nj) {
+                const int64_t u = first + (int64_t)(gp0 + lane) * stride;
+#pragma unroll
+                for (int s = 0; s < NS; s++)
+                    a.y[s][u] = pti_silu::silu_mul(outv[0][s], outv[1][s]);
+            }
+        } else {
+            const int nj = min(g1 * R, nrow) - gp0 * R;
+            if (lane < nj) {
+                const int64_t row = first + (int64_t)(gp0 * R + lane) * stride;
+#pragma unroll
+                for (int s = 0; s < NS; s++)
+                    a.y[s][row] = a.res[s] ? a.res[s][row] + outv[0][s] : outv[0][s];
+            }
         }
     }
 };
 
-template <int FMT, int NSP, int NS, int R, bool ROWS4, int W, int D, bool SEG>
+template <int FMT, int NSP, int NS, int R, bool ROWS4, int W, int D, int AM>
 __global__ __launch_bounds__(64 * W) void gemv_kernel(GemvArgs a)
 {
     static_assert(W % 4 == 0, "waves per workgroup must fill the four SIMDs evenly");
@@ -783,9 +822,10 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemvArgs a)
     const int j = wv >> 2;
     const int64_t n_simd_rows = sg < a.rows ? (a.rows - sg + nsimd - 1) / nsimd : 0;
     const int nrow = (int)(n_simd_rows > j ? (n_simd_rows - j + kPerSimd - 1) / kPerSimd : 0);
-    Wave<FMT, NSP, NS, R, ROWS4, D, SEG> w(a, xs, lane, sg + (int64_t)j * nsimd, (int64_t)kPerSimd * nsimd, nrow);
+    Wave<FMT, NSP, NS, R, ROWS4, D, AM> w(a, xs, lane, sg + (int64_t)j * nsimd, (int64_t)kPerSimd * nsimd, nrow);
 
-    if (a.chunk_rounds >= a.rounds) {
+    // (pairs are launched only with all of x in LDS)
+    if (AM == kAmPair || a.chunk_rounds >= a.rounds) {
         // All of x fits: stage it once, then run every pass.  The x loads go
         // out first, then the first weight loads, so the LDS stores wait only
         // for x while the weights are already in flight.
@@ -864,16 +904,20 @@ constexpr RowwiseCfg rowwise_cfg()
         return {PTI_Q8_N4_CFG};
 }
 
-template <int FMT, int NSP, int NS, bool ROWS4>
+// PAIR: a gate|up pair launch (kAmPair; all of x must fit in LDS, which the
+// caller checks); otherwise one matrix or a grouped launch, by a.seg_end.
+template <int FMT, int NSP, int NS, bool ROWS4, bool PAIR = false>
 int launch(const GemvArgs &a0, hipStream_t stream)
 {
     constexpr int UC = unit_cols<FMT>();
     constexpr RowwiseCfg cfg = rowwise_cfg<FMT, NS>();
-    constexpr int R = cfg.rows, kWaves = cfg.waves, kThreads = 64 * kWaves;
+    constexpr int R = PAIR ? 2 : cfg.rows, kWaves = cfg.waves, kThreads = 64 * kWaves;
     GemvArgs a = a0;
     const int per_round = 64 * UC * NSP * 4;  // LDS bytes per round of x
     a.chunk_rounds = max(1, min(a.rounds, kXLds / per_round));
     const size_t lds = (size_t)a.chunk_rounds * per_round;
+    if (PAIR && a.chunk_rounds < a.rounds)
+        return PTI_ERR_SHAPE;  // pairs need all of x in LDS
     const int cus = device_cus();
     if (cus <= 0) {
         pti::set_hip_error(hipGetLastError());
@@ -883,9 +927,13 @@ int launch(const GemvArgs &a0, hipStream_t stream)
     // VALU-bound (four streams), so spreading the rows over more SIMDs is what
     // shortens it; a workgroup without rows only stages x.
     const int64_t grid = std::min<int64_t>(cus, a.rows);
-    const bool seg = a.seg_end[0] != INT64_MAX;  // a grouped launch: rows in several matrices
-    auto kern = seg ? gemv_kernel<FMT, NSP, NS, R, ROWS4, kWaves, cfg.prefetch, true>
-                    : gemv_kernel<FMT, NSP, NS, R, ROWS4, kWaves, cfg.prefetch, false>;
+    const bool seg = !PAIR && a.seg_end[0] != INT64_MAX;  // a grouped launch: rows in several matrices
+    void (*kern)(GemvArgs);
+    if constexpr (PAIR)
+        kern = gemv_kernel<FMT, NSP, NS, R, ROWS4, kWaves, cfg.prefetch, kAmPair>;
+    else
+        kern = seg ? gemv_kernel<FMT, NSP, NS, R, ROWS4, kWaves, cfg.prefetch, kAmSeg>
+                   : gemv_kernel<FMT, NSP, NS, R, ROWS4, kWaves, cfg.prefetch, kAmFlat>;
     // The dynamic-LDS limit is a per-device attribute of the kernel: set it once on each device each
     // instance runs on (one bit per device; two threads racing both set it, which is harmless).
     static std::atomic<uint64_t> attr_devs[2] = {0, 0};
@@ -1596,6 +1644,19 @@ int group_args(const void *const *w, const int64_t *rows, int n, int64_t cols, c
     return PTI_OK;
 }
 
+// Whether the Q8 GEMV of stacked rows a (n streams) takes the per-wave-row
+// kernel with all of x staged at once, the kernel that can normalise x as it
+// stages it (otherwise the shape takes the row-split kernel at every stream
+// count, or x does not fit in LDS).
+bool q8_norm_fusable(const GemvArgs &a, int n)
+{
+    const bool even = (a.cols / PTI_BLOCK) % 2 == 0;
+    if (even && a.rows <= kQ8SplitMaxRows && (a.rounds + split_T(a.rounds) - 1) / split_T(a.rounds) <= kQ8SplitMaxQ)
+        return false;
+    const int nsp = n == 1 ? 1 : n == 2 ? 2 : 4;
+    return a.rounds * 64 * unit_cols<kQ8>() * nsp * 4 <= kXLds;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1782,6 +1843,7 @@ int gemv_q8_res(const void *w, const float *x, float *y, const float *res, int64
     return launch_q8(a, n, static_cast<hipStream_t>(stream));
 }
 
+
 int q8_gemv_rmsnorm(const void *const *w, const int64_t *rows, int n_mats, const float *x, float *y, int64_t cols,
                     int n, float eps, void *stream)
 {
@@ -1789,12 +1851,8 @@ int q8_gemv_rmsnorm(const void *const *w, const int64_t *rows, int n_mats, const
     const int rc = group_args<kQ8>(w, rows, n_mats, cols, nullptr, 0, a);
     if (rc != PTI_OK)
         return rc;
-    // the per-wave-row kernel with all of x staged at once, or no fusion
     const bool even = (a.cols / PTI_BLOCK) % 2 == 0;
-    if (even && a.rows <= kQ8SplitMaxRows && (a.rounds + split_T(a.rounds) - 1) / split_T(a.rounds) <= kQ8SplitMaxQ)
-        return kNormNotFused;
-    const int nsp = n == 1 ? 1 : n == 2 ? 2 : 4;
-    if (a.rounds * 64 * unit_cols<kQ8>() * nsp * 4 > kXLds)
+    if (!q8_norm_fusable(a, n))
         return kNormNotFused;
     for (int s = 0; s < n; s++) {
         a.x[s] = x + (size_t)s * cols;
@@ -1808,6 +1866,38 @@ int q8_gemv_rmsnorm(const void *const *w, const int64_t *rows, int n_mats, const
     case 2: return even ? launch<kQ8, 2, 2, true>(a, st) : launch<kQ8, 2, 2, false>(a, st);
     case 3: return even ? launch<kQ8, 4, 3, true>(a, st) : launch<kQ8, 4, 3, false>(a, st);
     default: return even ? launch<kQ8, 4, 4, true>(a, st) : launch<kQ8, 4, 4, false>(a, st);
+    }
+}
+
+int q8_gate_up_silu(const void *gate, const void *up, int64_t ffn, const float *x, float *y, int64_t cols, int n,
+                    float eps, void *stream)
+{
+    const void *w[2] = {gate, up};
+    const int64_t rows[2] = {ffn, ffn};
+    GemvArgs a;
+    const int rc = group_args<kQ8>(w, rows, 2, cols, nullptr, 0, a);
+    if (rc != PTI_OK)
+        return rc;
+    // the shapes whose gate|up GEMV fuses the norm: the same kernel and rows,
+    // so gate and up keep the bits of that GEMV
+    const bool even = (a.cols / PTI_BLOCK) % 2 == 0;
+    if (!q8_norm_fusable(a, n))
+        return kNormNotFused;
+    a.rows = ffn;  // row pairs
+    a.seg_base[0] = reinterpret_cast<uintptr_t>(gate);
+    a.seg_base[1] = reinterpret_cast<uintptr_t>(up);
+    for (int s = 0; s < n; s++) {
+        a.x[s] = x + (size_t)s * cols;
+        a.y[s] = y + (size_t)s * ffn;
+    }
+    a.norm = 1;
+    a.norm_eps = double(eps);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (n) {
+    case 1: return even ? launch<kQ8, 1, 1, true, true>(a, st) : launch<kQ8, 1, 1, false, true>(a, st);
+    case 2: return even ? launch<kQ8, 2, 2, true, true>(a, st) : launch<kQ8, 2, 2, false, true>(a, st);
+    case 3: return even ? launch<kQ8, 4, 3, true, true>(a, st) : launch<kQ8, 4, 3, false, true>(a, st);
+    default: return even ? launch<kQ8, 4, 4, true, true>(a, st) : launch<kQ8, 4, 4, false, true>(a, st);
     }
 }
 

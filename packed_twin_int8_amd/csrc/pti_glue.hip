@@ -29,6 +29,7 @@
 
 #include "pti_internal.h"
 #include "pti_norm.h"
+#include "pti_silu.h"
 
 namespace {
 
@@ -161,8 +162,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_reg_kernel(const float *
 __global__ void silu_mul_kernel(const float *g, const float *u, float *y, int64_t n)
 {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-        const double gv = g[i];
-        y[i] = float(gv / (1.0 + exp(-gv)) * double(u[i]));
+        y[i] = pti_silu::silu_mul(g[i], u[i]);
     }
 }
 
@@ -174,8 +174,7 @@ __global__ void silu_mul_rows_kernel(const float *gu, float *y, int64_t cols)
     const float *g = gu + s * 2 * cols, *u = g + cols;
     float *ys = y + s * cols;
     for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < cols; j += (int64_t)gridDim.x * blockDim.x) {
-        const double gv = g[j];
-        ys[j] = float(gv / (1.0 + exp(-gv)) * double(u[j]));
+        ys[j] = pti_silu::silu_mul(g[j], u[j]);
     }
 }
 

@@ -43,9 +43,6 @@ int gemv_q8_res(const void *w, const float *x, float *y, const float *res, int64
 int gemv_ssq_res(const void *w, const float *x_a, const float *x_b, float *y_a, float *y_b, const float *res_a,
                  const float *res_b, int64_t rows, int64_t cols, void *stream);
 
-// y[s][j] = silu(gu[s][j]) * gu[s][cols + j] for s < rows, j < cols (rows of
-// 2 cols: the stacked output of a grouped gate|up GEMV), as pti_silu_mul
-// computes it.  Arguments already validated.
 // y[s] = W rmsnorm(x[s]) for the Q8 matrices w[0..n_mats) stacked into one
 // row space (as pti_gemv_q8_multi_grouped stacks them), s < n: the
 // per-wave-row GEMV normalises x while staging it, with the bits pti_rmsnorm
@@ -57,6 +54,19 @@ constexpr int kNormNotFused = 1;
 int q8_gemv_rmsnorm(const void *const *w, const int64_t *rows, int n_mats, const float *x, float *y, int64_t cols,
                     int n, float eps, void *stream);
 
+// y[s][j] = silu(g[s][j]) * u[s][j], j < ffn, s < n, for g = G rmsnorm(x[s])
+// and u = U rmsnorm(x[s]) (Q8 matrices gate and up of ffn rows each, cols
+// columns): one launch of the per-wave-row GEMV in which each wave takes row
+// j of both matrices and applies the activation to the pair, so g and u are
+// never stored.  Each of g, u has the bits q8_gemv_rmsnorm gives for the
+// stacked gate|up, and y those of launch_silu_mul_rows on that output.
+// Returns kNormNotFused, launching nothing, where q8_gemv_rmsnorm would.
+int q8_gate_up_silu(const void *gate, const void *up, int64_t ffn, const float *x, float *y, int64_t cols, int n,
+                    float eps, void *stream);
+
+// y[s][j] = silu(gu[s][j]) * gu[s][cols + j] for s < rows, j < cols (rows of
+// 2 cols: the stacked output of a grouped gate|up GEMV), as pti_silu_mul
+// computes it.  Arguments already validated.
 int launch_silu_mul_rows(const float *gu, float *y, int64_t rows, int64_t cols, void *stream);
 
 // tok[i] = tok_host[i] (i < n_tok) and, when uni_host is set, uni[i] =

@@ -110,8 +110,9 @@ int gemv(const pti_toy_model &m, const void *w, const float *x, float *y, int64_
 // Enqueues one pass; logits may point into the workspace or outside it.
 // Per layer: rmsnorm; gate and up in one grouped launch (outputs stacked per
 // stream); silu(gate) * up; down with the residual added as the rows are
-// stored.  Each step's results are bitwise those of the separate calls
-// (gate, up, silu_mul, down, add).
+// stored.  In Q8 the first three are one launch where the gate|up GEMV takes
+// the per-wave-row kernel.  Each step's results are bitwise those of the
+// separate calls (rmsnorm, gate, up, silu_mul, down, add).
 int forward(const pti_toy_model &m, const Layout &L, char *work, const int32_t *tokens, float *logits, int n,
             void *stream)
 {
@@ -126,9 +127,11 @@ int forward(const pti_toy_model &m, const Layout &L, char *work, const int32_t *
     const int64_t rows2[2] = {F, F};
     for (int l = 0; l < m.n_layers; l++) {
         const void *gate_up[2] = {m.gate[l], m.up[l]};
-        // Q8: the norm inside the gate|up GEMV's staging where that kernel
-        // takes the shape (same bits as the separate norm)
-        const int fused = ssq ? pti::kNormNotFused : pti::q8_gemv_rmsnorm(gate_up, rows2, 2, h, gu, H, n, m.eps, stream);
+        // Q8, where the gate|up GEMV takes the per-wave-row kernel: the norm
+        // inside its staging and silu(gate) * up applied to its row pairs,
+        // one launch (same bits as the separate norm, GEMV and activation)
+        const int fused = ssq ? pti::kNormNotFused
+                              : pti::q8_gate_up_silu(m.gate[l], m.up[l], F, h, x, H, n, m.eps, stream);
         if (fused != pti::kNormNotFused) {
             PTI_TRY(fused);
         } else {
@@ -137,8 +140,8 @@ int forward(const pti_toy_model &m, const Layout &L, char *work, const int32_t *
                 PTI_TRY(pti_gemv_ssq_grouped(gate_up, rows2, 2, r, r + H, gu, gu + 2 * F, H, stream));
             else
                 PTI_TRY(pti_gemv_q8_multi_grouped(gate_up, rows2, 2, r, gu, H, n, stream));
+            PTI_TRY(pti::launch_silu_mul_rows(gu, x, n, F, stream));
         }
-        PTI_TRY(pti::launch_silu_mul_rows(gu, x, n, F, stream));
         if (ssq)
             PTI_TRY(pti::gemv_ssq_res(m.down[l], x, x + F, h, h + H, h, h + H, H, F, stream));
         else
