@@ -269,7 +269,7 @@ ISOLATED = {
              "ssq", 2),
     "q8n1": ("Q8 GEMV, N = 1 (pti_gemv_q8_multi)", "gemv_q8_split_kernel<5, 1>", "q8", 1),
     "q8n2": ("Q8 GEMV, N = 2 (pti_gemv_q8_multi)", "gemv_q8_split_kernel<5, 2>", "q8", 2),
-    "q8n4": ("Q8 GEMV, N = 4 (pti_gemv_q8_multi)", "gemv_kernel<0, 4, 4, 2, true, 16, 1, false>", "q8", 4),
+    "q8n4": ("Q8 GEMV, N = 4 (pti_gemv_q8_multi)", "gemv_kernel<0, 4, 4, 2, true, 16, 1, 0>", "q8", 4),
     # attention: format "attn", the last field the context length
     "attn4k": ("twin-KV decode attention (pti_attn_decode), 2 streams, 40 query heads over 8 kv heads of 128, "
                "4096 positions", "attn_partial_kernel<128, 5>", "attn", 4096),
