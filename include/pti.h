@@ -33,13 +33,15 @@
  *   - Matrices are row-major, little-endian, with no header or padding: row r
  *     holds cols/32 consecutive blocks, block b covering columns 32b..32b+31.
  *     A weight's value is scale * int8 (symmetric, no zero point).
- *   - Ownership: the caller owns every buffer.  The library makes no
+ *   - Ownership: the caller owns every buffer.  The library makes no device
  *     allocation calls; its only device memory of its own is the 64 KB
  *     file-scope array of pti_sample_verify_static (one per GPU, from load
- *     time).  Its other state: a thread-local copy of the last HIP error, a
- *     thread-local cache of the current device's CU count, per-kernel flags
- *     of the devices whose launch attributes are set, and that array's
- *     address per device.  It may be called from several threads.
+ *     time).  Its only host allocation is pti_toy_decode's readback page
+ *     (4 KB of pinned host memory per calling thread, see there).  Its other
+ *     state: a thread-local copy of the last HIP error, a thread-local cache
+ *     of the current device's CU count, per-kernel flags of the devices whose
+ *     launch attributes are set, and that array's address per device.  It
+ *     may be called from several threads.
  *   - Device calls take device pointers and a HIP stream (a hipStream_t passed
  *     as void*, NULL = the default stream).  They enqueue work and return
  *     without synchronising; outputs are overwritten, never accumulated into.
@@ -420,7 +422,11 @@ int pti_graph_destroy(void *graph);
  * [(N - 1) + n_steps * (2N - 1)][5] or NULL; each executed draw appends
  * (step, slot, stream, input token, output token) and *n_passes (host, may be
  * NULL) receives their count.  Synchronises `stream` after every pass (the
- * next inputs depend on the accept count). */
+ * next inputs depend on the accept count).  The pass's verify kernel writes
+ * the draws and the accept count straight into a page of pinned, coherent
+ * host memory (no copy command per pass); the page belongs to the calling
+ * thread, is allocated at its first call (an allocation failure returns
+ * PTI_ERR_HIP) and is kept until the process ends. */
 int pti_toy_decode(const pti_toy_model *m, int32_t first_token, int n_streams, int n_steps, double temperature,
                    const double *uniforms, void *work, size_t work_bytes, int32_t *committed, int32_t *accepts,
                    int32_t *passes, int64_t *n_passes, void *stream);

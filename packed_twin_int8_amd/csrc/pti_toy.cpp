@@ -31,7 +31,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
-    size_t h, r, gu, x, logits, tok, out, acc, uni, sv, total;
+    size_t h, r, gu, x, logits, tok, uni, sv, total;
 };
 
 Layout layout(const pti_toy_model &m, int n)
@@ -50,8 +50,6 @@ Layout layout(const pti_toy_model &m, int n)
     L.x = take(N * size_t(m.ffn) * 4);
     L.logits = take(N * size_t(m.vocab) * 4);
     L.tok = take(PTI_MAX_STREAMS * 4);
-    L.out = take(PTI_MAX_STREAMS * 4 + 4);  // the drawn tokens, then the accept count: read back in one copy
-    L.acc = L.out + PTI_MAX_STREAMS * 4;
     L.uni = take(PTI_MAX_STREAMS * 8);
     L.sv = take(pti_sample_verify_workspace_bytes(m.vocab, n));  // the sampled verify's part sums
     L.total = off;
@@ -179,10 +177,12 @@ struct Decoder {
     int32_t *log;            // host, 5 ints per draw, or null
     int64_t nlog = 0;
     hipStream_t st;
+    // pinned host memory the verify kernels write the draws (ints
+    // 0 .. PTI_MAX_STREAMS - 1) and the accept count (int PTI_MAX_STREAMS)
+    // into, so that a pass's results reach the host without a copy command
+    volatile int32_t *back = nullptr;
 
     int32_t *dev_tok() const { return reinterpret_cast<int32_t *>(work + L.tok); }
-    int32_t *dev_out() const { return reinterpret_cast<int32_t *>(work + L.out); }
-    int32_t *dev_acc() const { return reinterpret_cast<int32_t *>(work + L.acc); }
     double *dev_uni() const { return reinterpret_cast<double *>(work + L.uni); }
     float *dev_logits() const { return reinterpret_cast<float *>(work + L.logits); }
 
@@ -209,18 +209,17 @@ struct Decoder {
     // Draws n tokens from logits rows [row0, row0 + n) with the uniforms set
     // for the pass; the accept count compares them with the pass inputs in
     // dev_tok() (read only when n >= 2, i.e. for row0 == 0).  The draws and
-    // the accept count come back in one copy.
+    // the accept count arrive in the readback page when the stream is synchronised.
     int draw(int row0, int n, int32_t *out, int32_t *accept)
     {
         void *s = st;
         const float *lg = dev_logits() + int64_t(row0) * m.vocab;
+        int32_t *o = const_cast<int32_t *>(back), *a = o + PTI_MAX_STREAMS;
         if (temp == 0.0)
-            PTI_TRY(pti_verify_argmax(lg, dev_tok(), dev_out(), dev_acc(), m.vocab, n, s));
+            PTI_TRY(pti_verify_argmax(lg, dev_tok(), o, a, m.vocab, n, s));
         else
-            PTI_TRY(pti_sample_verify(lg, dev_tok(), dev_uni(), temp, dev_out(), dev_acc(), m.vocab, n, work + L.sv,
+            PTI_TRY(pti_sample_verify(lg, dev_tok(), dev_uni(), temp, o, a, m.vocab, n, work + L.sv,
                                       pti_sample_verify_workspace_bytes(m.vocab, n), s));
-        int32_t back[PTI_MAX_STREAMS + 1];
-        PTI_TRY(hip_status(hipMemcpyAsync(back, dev_out(), sizeof(back), hipMemcpyDeviceToHost, st)));
         PTI_TRY(hip_status(hipStreamSynchronize(st)));
         for (int i = 0; i < n; i++)
             out[i] = back[i];
@@ -255,6 +254,23 @@ struct Decoder {
         return PTI_OK;
     }
 };
+
+// The readback page of the calling thread: pinned, coherent host memory that
+// kernels write into directly (one page per thread that decodes, allocated at
+// its first call and kept until the process ends, so that calls on
+// different threads never share it and nothing is freed while a kernel may
+// still write to it).
+int readback_page(volatile int32_t **out)
+{
+    static thread_local void *page = nullptr;
+    if (!page) {
+        void *p = nullptr;
+        PTI_TRY(hip_status(hipHostMalloc(&p, 4096, hipHostMallocCoherent)));
+        page = p;
+    }
+    *out = static_cast<volatile int32_t *>(page);
+    return PTI_OK;
+}
 
 int check_work(const Layout &L, const void *work, size_t work_bytes)
 {
@@ -367,6 +383,7 @@ extern "C" int pti_toy_decode(const pti_toy_model *m, int32_t first_token, int n
     const int N = n_streams;
     Decoder D{*m, L, static_cast<char *>(work), N, m->format == PTI_FMT_SSQ ? 2 : N, temperature, uniforms, passes,
               0, static_cast<hipStream_t>(stream)};
+    PTI_TRY(readback_page(&D.back));
     int32_t x[PTI_MAX_STREAMS], o[PTI_MAX_STREAMS], nxt[PTI_MAX_STREAMS];
     x[0] = first_token;
     for (int i = 1; i < N; i++)
