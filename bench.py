@@ -172,7 +172,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 KT_FILE = os.path.join(HERE, "profiles", "bench_default_17408x5120_kernel_stats.md")
 # the kernel of the headline step (the fused SSQ twin GEMV; verify_keys_kernel follows it)
 STEP_KERNEL = "gemv_ssq_split_kernel<5, 2, true, 8>"
-KERNEL_SOURCES = ("packed_twin_int8_amd/csrc/pti_gemv.hip", "packed_twin_int8_amd/build.py")
+KERNEL_SOURCES = ("packed_twin_int8_amd/csrc/pti_gemv.hip", "packed_twin_int8_amd/csrc/pti_norm.h",
+                  "packed_twin_int8_amd/csrc/pti_silu.h", "packed_twin_int8_amd/build.py")
 ATTN_SOURCES = ("packed_twin_int8_amd/csrc/pti_attn.hip", "packed_twin_int8_amd/build.py")
 KT_CMDS = {
     "kt": "rocprofv3 --kernel-trace --stats -f csv -d rocprof_out/bench -o bench -- python3 bench.py --no-cpu",
