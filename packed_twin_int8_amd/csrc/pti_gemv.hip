@@ -86,6 +86,11 @@
 #ifndef PTI_Q8_N4_CFG
 #define PTI_Q8_N4_CFG 16, 1, 2
 #endif
+// Stream counts up to which the Q8 row-split kernel takes the paired loads
+// (fewer load instructions, four more VALU ops per 16 quants).
+#ifndef PTI_Q8_PAIRED_MAX_NS
+#define PTI_Q8_PAIRED_MAX_NS 2
+#endif
 #ifndef PTI_SSQ_ROWWISE_CFG
 #define PTI_SSQ_ROWWISE_CFG 16, 3, 1
 #endif
@@ -1359,6 +1364,7 @@ int launch_ssq_split(const GemvArgs &a, const VerifyOut *vo, hipStream_t stream)
 // same whatever NS is.
 constexpr int kQ8SplitMaxQ = 4;
 constexpr int64_t kQ8SplitMaxRows = 8192;
+constexpr uint32_t kPastBuffer = 0x40000000u;  // a load offset past every row's buffer: reads 0, touches nothing
 
 template <int T, int NS>
 __global__ __launch_bounds__(64 * 4) void gemv_q8_split_kernel(SplitArgs sa)
@@ -1377,6 +1383,22 @@ __global__ __launch_bounds__(64 * 4) void gemv_q8_split_kernel(SplitArgs sa)
     float xv[T][UC][NS];  // this lane's x (filled below)
     const LaneOffsets lo = lane_offsets(lane);
     const int soff = q * T * (int)kRoundBytes;
+    // Paired loads (PL): the two lanes of a block read its nine aligned dwords
+    // W0..W8 with one b128 each (its quants' window: W0-3 and W4-7 in an even
+    // block of the round, which starts on a dword; W1-4 and W5-8 in an odd
+    // one, which starts 2 bytes into W0) and one b32 between them (W8 by the
+    // second lane of an even block, W0 by the first lane of an odd one; the
+    // other lane's b32 points past the buffer and reads nothing), then swap
+    // one dword: the first lane's W0 (the scale) and the second lane's first
+    // b128 dword (W4, the first lane's fifth quant dword in an even block).
+    // Each lane then holds the bytes the three loads per lane would give it
+    // (the fifth dword only where its quants start 2 bytes in), so the
+    // arithmetic is unchanged; two load instructions per round instead of
+    // three.
+    constexpr bool PL = NS <= PTI_Q8_PAIRED_MAX_NS;
+    const bool second = lane & 1, odd_block = (lane >> 1) & 1;
+    const bool sends_extra = !second && odd_block;  // the first lane of an odd block holds W0 in its b32
+    const uint32_t xoff = odd_block ? (second ? kPastBuffer : lo.q_sc[0]) : (second ? lo.q_sc[0] + 32 : kPastBuffer);
     auto rsrc_for = [&](int t) {
         const int64_t m = (int64_t)t * P + p;
         const bool in = m < wg_rows;
@@ -1384,13 +1406,15 @@ __global__ __launch_bounds__(64 * 4) void gemv_q8_split_kernel(SplitArgs sa)
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(row_addr(a, in ? g + m * G : 0)), (short)0, n,
                                                  0x00020000);
     };
-    // Loads of round tt: the scale's dword, the 16 quants (4 + 1 dwords).
+    // Loads of round tt: the scale's dword, the 16 quants (4 + 1 dwords);
+    // paired: the b128 and the lane's b32 (in d[4]), sc unused.
     auto load_round = [&](__amdgpu_buffer_rsrc_t rs, int tt, Unit &u) {
         const int so = soff + tt * (int)kRoundBytes;
-        u.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.q_sc[0], so, 0);
+        if constexpr (!PL)
+            u.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.q_sc[0], so, 0);
         const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lo.q_d[0], so, 0);
         u.d[0] = v.x, u.d[1] = v.y, u.d[2] = v.z, u.d[3] = v.w;
-        u.d[4] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lo.q_h[0], so, 0);
+        u.d[4] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(PL ? xoff : lo.q_h[0]), so, 0);
     };
 
     auto step = [&](int t, int half, int local, const Unit (&ut)[T], Unit (&nxt)[T]) {
@@ -1399,10 +1423,17 @@ __global__ __launch_bounds__(64 * 4) void gemv_q8_split_kernel(SplitArgs sa)
 #pragma unroll
         for (int tt = 0; tt < T; tt++) {
             const Unit &u = ut[tt];
+            uint32_t sc = u.sc, d4 = u.d[4];
+            if constexpr (PL) {
+                const uint32_t send = sends_extra ? u.d[4] : u.d[0];
+                const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xf, 0xf, false);
+                sc = second ? got : send;
+                d4 = second ? u.d[4] : got;
+            }
             uint32_t qd[4];
 #pragma unroll
             for (int k = 0; k < 4; k++)
-                qd[k] = __builtin_amdgcn_alignbyte(u.d[k + 1], u.d[k], lo.q_sh[0]);
+                qd[k] = __builtin_amdgcn_alignbyte(k < 3 ? u.d[k + 1] : d4, u.d[k], lo.q_sh[0]);
             float bs[NS];
 #pragma unroll
             for (int c = 0; c < UC; c++) {
@@ -1411,7 +1442,7 @@ __global__ __launch_bounds__(64 * 4) void gemv_q8_split_kernel(SplitArgs sa)
                 for (int s = 0; s < NS; s++)
                     bs[s] = c == 0 ? wq * xv[tt][c][s] : __builtin_fmaf(wq, xv[tt][c][s], bs[s]);
             }
-            const float d = f16_lo(u.sc >> lo.q_ssh[0]);
+            const float d = f16_lo(sc >> lo.q_ssh[0]);
             // fma into +0 at the first round, as the per-wave-row kernel does
             // (d * bs would keep a -0 that it turns into +0)
 #pragma unroll
@@ -1480,8 +1511,9 @@ __global__ __launch_bounds__(64 * 4) void gemv_q8_split_kernel(SplitArgs sa)
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    static_assert(3 * T < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * T));  // vmcnt(3T)
+    constexpr int kLoads = (PL ? 2 : 3) * T;  // weight loads of one step
+    static_assert(kLoads < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kLoads);  // vmcnt(kLoads): the x loads are done
 
     int half = 0;
     for (int t0 = 0; t0 < steps; t0 += S, half ^= 1) {
