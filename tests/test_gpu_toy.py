@@ -371,6 +371,17 @@ def test_forward_full_q8_ops_composition_and_sanity(full_q8, full_oracle):
     assert rel < 1e-3  # sanity (observed ~1e-6), not a parity bar
 
 
+@pytest.mark.parametrize("toks", [[1], [31999, 12345], [7, 7, 500]])
+def test_forward_full_q8_fewer_streams_composition(full_q8, toks):
+    # the gate|up GEMV with the norm and SiLU-up inside it at every stream count
+    # (its one-, two- and three-stream instances), bitwise against the op-by-op
+    # composition, each op checked against the oracle; a stream's logits do not
+    # depend on the other streams of the pass
+    lg = _forward_checks(full_q8, toks)
+    lg4 = host(full_q8.gpu.forward(dev(toks + [0] * (4 - len(toks)), np.int32)))
+    assert np.array_equal(lg, lg4[:len(toks)]), "a stream's logits depend on the stream count"
+
+
 def test_forward_full_ssq_self_twin(full_ssq, full_oracle):
     lg = _forward_checks(full_ssq, [1, 2])
     want = full_oracle.logits([1, 2])
