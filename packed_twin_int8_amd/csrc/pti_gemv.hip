@@ -209,22 +209,42 @@ __device__ __forceinline__ float f16_hi(uint32_t v)
 }
 
 // LDS layout of one chunk of x (float4 elements), UC = unit columns:
-//   xs[((round * (UC/4) + cg) * NSP + p) * 64 + lane]
+//   xs[((round * (UC/4) + cg) * NSP + p) * 64 + (lane ^ swz(cg))]
 // cg = column group (4 columns) of the lane's unit, p = piece.  Piece p of
 // (lane, cg) holds elements 4p..4p+3 of the column-major flattening
 // e = m * NSP + s (m = column within the group, s = stream); NSP = streams
 // rounded up to 1, 2 or 4 (three streams are padded with a zero fourth).
-// Staging items are (round, column group, lane), spread over the threads.
+// The lane slot is XOR-swizzled by the column group, swz(cg) = cg * 16 / CG
+// (CG = UC / 4 groups per unit), so that both the loop's reads of one
+// (round, cg, p) and the staging stores of consecutive column groups spread
+// over all LDS banks.
+template <int UC, int NSP>
+__device__ __forceinline__ int lds_slot(int rd, int cg, int p, int l)
+{
+    constexpr int CG = UC / 4;
+    return ((rd * CG + cg) * NSP + p) * 64 + (l ^ (cg * (16 / CG)));
+}
+
+// Staging item `it` is column group it of the chunk (columns 4 it .. 4 it + 3):
+// unit u = it / CG (round u / 64, lane u % 64), group cg = it % CG of the
+// unit.  Consecutive threads take consecutive 16-byte pieces of each x row,
+// so a wave's staging loads read contiguous memory.
+template <int UC>
+__device__ __forceinline__ void stage_item(int it, int &rd, int &cg, int &l)
+{
+    constexpr int CG = UC / 4;
+    const int u = it / CG;
+    rd = u >> 6, cg = it % CG, l = u & 63;
+}
+
 template <int UC, int NSP, int NS, int BATCH, int THREADS>
 __device__ __forceinline__ void stage_load(const GemvArgs &a, int item0, float4 (&v)[BATCH][NSP], int tid,
                                            int nitems)
 {
-    constexpr int CG = UC / 4;
 #pragma unroll
     for (int i = 0; i < BATCH; i++) {
         const int it = item0 + i * THREADS + tid;
-        const int l = it & 63, cg = (it >> 6) % CG, rd = (it >> 6) / CG;
-        const int col = (rd * 64 + l) * UC + cg * 4;
+        const int col = 4 * it;
 #pragma unroll
         for (int s = 0; s < NSP; s++) {
             v[i][s] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -238,18 +258,18 @@ template <int UC, int NSP, int BATCH, int THREADS>
 __device__ __forceinline__ void stage_store(float4 *xs, int item0, const float4 (&v)[BATCH][NSP], int tid,
                                             int nitems)
 {
-    constexpr int CG = UC / 4;
 #pragma unroll
     for (int i = 0; i < BATCH; i++) {
         const int it = item0 + i * THREADS + tid;
         if (it >= nitems)
             break;
-        const int l = it & 63, cg = (it >> 6) % CG, rd = (it >> 6) / CG;
+        int rd, cg, l;
+        stage_item<UC>(it, rd, cg, l);
         float e[4][4];  // [stream][column]
 #pragma unroll
         for (int s = 0; s < NSP; s++)
             e[s][0] = v[i][s].x, e[s][1] = v[i][s].y, e[s][2] = v[i][s].z, e[s][3] = v[i][s].w;
-        float4 *base = xs + ((rd * CG + cg) * NSP) * 64 + l;
+        float4 *base = xs + lds_slot<UC, NSP>(rd, cg, 0, l);
 #pragma unroll
         for (int p = 0; p < NSP; p++) {
             float o[4];
@@ -267,9 +287,8 @@ __device__ __forceinline__ void stage_store(float4 *xs, int item0, const float4 
 template <int UC, int NSP>
 __device__ __forceinline__ float *staged_elem(float4 *xs, int c, int s)
 {
-    constexpr int CG = UC / 4;
     const int rd = c / (64 * UC), l = (c / UC) % 64, cg = (c % UC) / 4, f = (c % 4) * NSP + s;
-    return reinterpret_cast<float *>(xs + ((rd * CG + cg) * NSP + f / 4) * 64 + l) + f % 4;
+    return reinterpret_cast<float *>(xs + lds_slot<UC, NSP>(rd, cg, f / 4, l)) + f % 4;
 }
 
 // x[s] <- rmsnorm(x[s]) in LDS after all of x was staged and a barrier: the
@@ -316,14 +335,14 @@ __device__ __forceinline__ void norm_staged(const GemvArgs &a, float4 *xs, int t
 #pragma unroll
     for (int s = 0; s < NS; s++)
         r[s] = pti_norm::inv_root(part[s], a.cols, a.norm_eps);
-    constexpr int CG = UC / 4;
 #pragma unroll
     for (int i = 0; i < BATCH; i++) {
         const int it = i * THREADS + tid;
         if (it >= nitems)
             break;
-        const int l = it & 63, cg = (it >> 6) % CG, rd = (it >> 6) / CG;
-        float4 *base = xs + ((rd * CG + cg) * NSP) * 64 + l;
+        int rd, cg, l;
+        stage_item<UC>(it, rd, cg, l);
+        float4 *base = xs + lds_slot<UC, NSP>(rd, cg, 0, l);
 #pragma unroll
         for (int p = 0; p < NSP; p++) {
             float *e = reinterpret_cast<float *>(base + p * 64);
@@ -608,7 +627,7 @@ struct Wave {
     // guarded.
     __device__ __forceinline__ void compute(const Unit (&buf)[R])
     {
-        const float4 *xr = xs + ((cr - i0) * CG * NSP) * 64 + lane;
+        const float4 *xr = xs + ((cr - i0) * CG * NSP) * 64;
         uint32_t q[R][4];
         if constexpr (FMT == kQ8) {
 #pragma unroll
@@ -626,7 +645,7 @@ struct Wave {
             float xv[4][NSP];
 #pragma unroll
             for (int p = 0; p < NSP; p++) {
-                const float4 t = xr[(c * NSP + p) * 64];
+                const float4 t = xr[(c * NSP + p) * 64 + (lane ^ (c * (16 / CG)))];
                 const float e[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
                 for (int qq = 0; qq < 4; qq++) {
