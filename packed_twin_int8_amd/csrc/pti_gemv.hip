@@ -107,6 +107,7 @@ constexpr int kNormLds = 256;
 constexpr int kXLds = PTI_LDS_BUDGET - kNormLds;
 
 constexpr uint32_t kRoundBytes = 1088;  // bytes of a row one round of 64 lanes covers (both formats)
+constexpr uint32_t kPastBuffer = 0x40000000u;  // a buffer load offset past every buffer here: reads 0, touches nothing
 
 enum Fmt { kQ8 = 0, kSSQ = 1 };
 
@@ -211,9 +212,9 @@ __device__ __forceinline__ float f16_hi(uint32_t v)
 // LDS layout of one chunk of x (float4 elements), UC = unit columns:
 //   xs[((round * (UC/4) + cg) * NSP + p) * 64 + (lane ^ swz(cg))]
 // cg = column group (4 columns) of the lane's unit, p = piece.  Piece p of
-// (lane, cg) holds elements 4p..4p+3 of the column-major flattening
-// e = m * NSP + s (m = column within the group, s = stream); NSP = streams
-// rounded up to 1, 2 or 4 (three streams are padded with a zero fourth).
+// (lane, cg) holds stream p's four columns of the group, as x holds them (so
+// staging stores each loaded float4 as it is); NSP = streams rounded up to
+// 1, 2 or 4 (three streams are padded with a zero fourth).
 // The lane slot is XOR-swizzled by the column group, swz(cg) = cg * 16 / CG
 // (CG = UC / 4 groups per unit), so that both the loop's reads of one
 // (round, cg, p) and the staging stores of consecutive column groups spread
@@ -237,19 +238,31 @@ __device__ __forceinline__ void stage_item(int it, int &rd, int &cg, int &l)
     rd = u >> 6, cg = it % CG, l = u & 63;
 }
 
+// A thread loads its items of the chunk (it < nitems) with buffer loads; a
+// column past the row or a padding stream (s >= NS) reads zeros through the
+// buffer bounds.  An item past the chunk leaves v unset (stage_store never
+// reads it), so no load's result is merged with a default, which would make
+// each load wait for the one before.
 template <int UC, int NSP, int NS, int BATCH, int THREADS>
 __device__ __forceinline__ void stage_load(const GemvArgs &a, int item0, float4 (&v)[BATCH][NSP], int tid,
                                            int nitems)
 {
+    __amdgpu_buffer_rsrc_t rs[NSP];
+#pragma unroll
+    for (int s = 0; s < NSP; s++)
+        rs[s] = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(s < NS ? a.x[s] : nullptr), (short)0,
+                                                  s < NS ? (int)(a.cols * 4) : 0, 0x00020000);
 #pragma unroll
     for (int i = 0; i < BATCH; i++) {
         const int it = item0 + i * THREADS + tid;
-        const int col = 4 * it;
+        if (it < nitems) {
 #pragma unroll
-        for (int s = 0; s < NSP; s++) {
-            v[i][s] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (it < nitems && s < NS && col < a.cols)
-                v[i][s] = *reinterpret_cast<const float4 *>(a.x[s] + col);
+            for (int s = 0; s < NSP; s++) {
+                const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rs[s], 16 * it, 0, 0);  // column 4 it
+                v[i][s] = make_float4(
+                    __builtin_bit_cast(float, (uint32_t)t.x), __builtin_bit_cast(float, (uint32_t)t.y),
+                    __builtin_bit_cast(float, (uint32_t)t.z), __builtin_bit_cast(float, (uint32_t)t.w));
+            }
         }
     }
 }
@@ -265,21 +278,10 @@ __device__ __forceinline__ void stage_store(float4 *xs, int item0, const float4 
             break;
         int rd, cg, l;
         stage_item<UC>(it, rd, cg, l);
-        float e[4][4];  // [stream][column]
-#pragma unroll
-        for (int s = 0; s < NSP; s++)
-            e[s][0] = v[i][s].x, e[s][1] = v[i][s].y, e[s][2] = v[i][s].z, e[s][3] = v[i][s].w;
         float4 *base = xs + lds_slot<UC, NSP>(rd, cg, 0, l);
 #pragma unroll
-        for (int p = 0; p < NSP; p++) {
-            float o[4];
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const int f = 4 * p + q;
-                o[q] = e[f % NSP][f / NSP];
-            }
-            base[p * 64] = make_float4(o[0], o[1], o[2], o[3]);
-        }
+        for (int p = 0; p < NSP; p++)
+            base[p * 64] = v[i][p];
     }
 }
 
@@ -287,8 +289,8 @@ __device__ __forceinline__ void stage_store(float4 *xs, int item0, const float4 
 template <int UC, int NSP>
 __device__ __forceinline__ float *staged_elem(float4 *xs, int c, int s)
 {
-    const int rd = c / (64 * UC), l = (c / UC) % 64, cg = (c % UC) / 4, f = (c % 4) * NSP + s;
-    return reinterpret_cast<float *>(xs + lds_slot<UC, NSP>(rd, cg, f / 4, l)) + f % 4;
+    const int rd = c / (64 * UC), l = (c / UC) % 64, cg = (c % UC) / 4;
+    return reinterpret_cast<float *>(xs + lds_slot<UC, NSP>(rd, cg, s, l)) + c % 4;
 }
 
 // x[s] <- rmsnorm(x[s]) in LDS after all of x was staged and a barrier: the
@@ -344,14 +346,11 @@ __device__ __forceinline__ void norm_staged(const GemvArgs &a, float4 *xs, int t
         stage_item<UC>(it, rd, cg, l);
         float4 *base = xs + lds_slot<UC, NSP>(rd, cg, 0, l);
 #pragma unroll
-        for (int p = 0; p < NSP; p++) {
+        for (int p = 0; p < NS; p++) {
             float *e = reinterpret_cast<float *>(base + p * 64);
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const int st = (4 * p + q) % NSP;
-                if (st < NS)
-                    e[q] = pti_norm::apply(e[q], r[st]);
-            }
+            for (int q = 0; q < 4; q++)
+                e[q] = pti_norm::apply(e[q], r[p]);
         }
     }
     __syncthreads();
@@ -642,16 +641,11 @@ struct Wave {
         float bs[R][NS];
 #pragma unroll
         for (int c = 0; c < CG; c++) {
-            float xv[4][NSP];
+            float xv[4][NSP];  // [column of the group][stream]
 #pragma unroll
             for (int p = 0; p < NSP; p++) {
                 const float4 t = xr[(c * NSP + p) * 64 + (lane ^ (c * (16 / CG)))];
-                const float e[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-                for (int qq = 0; qq < 4; qq++) {
-                    const int f = 4 * p + qq;
-                    xv[f / NSP][f % NSP] = e[qq];
-                }
+                xv[0][p] = t.x, xv[1][p] = t.y, xv[2][p] = t.z, xv[3][p] = t.w;
             }
 #pragma unroll
             for (int r = 0; r < R; r++) {
@@ -1383,7 +1377,6 @@ int launch_ssq_split(const GemvArgs &a, const VerifyOut *vo, hipStream_t stream)
 // same whatever NS is.
 constexpr int kQ8SplitMaxQ = 4;
 constexpr int64_t kQ8SplitMaxRows = 8192;
-constexpr uint32_t kPastBuffer = 0x40000000u;  // a load offset past every row's buffer: reads 0, touches nothing
 
 template <int T, int NS>
 __global__ __launch_bounds__(64 * 4) void gemv_q8_split_kernel(SplitArgs sa)
