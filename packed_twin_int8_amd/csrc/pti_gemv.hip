@@ -806,9 +806,19 @@ struct Wave {
             const int nj = min(g1 * R, nrow) - gp0 * R;
             if (lane < nj) {
                 const int64_t row = first + (int64_t)(gp0 * R + lane) * stride;
+                if (a.res[0]) {  // uniform: a residual launch sets every stream's
+                    float r[NS];  // all loads first, then the sums
 #pragma unroll
-                for (int s = 0; s < NS; s++)
-                    a.y[s][row] = a.res[s] ? a.res[s][row] + outv[0][s] : outv[0][s];
+                    for (int s = 0; s < NS; s++)
+                        r[s] = a.res[s][row];
+#pragma unroll
+                    for (int s = 0; s < NS; s++)
+                        a.y[s][row] = r[s] + outv[0][s];
+                } else {
+#pragma unroll
+                    for (int s = 0; s < NS; s++)
+                        a.y[s][row] = outv[0][s];
+                }
             }
         }
     }
@@ -1149,25 +1159,34 @@ __global__ __launch_bounds__(64 * BW) void gemv_ssq_split_kernel(SplitArgs sa)
     auto flush = [&](int t0, int t1, int half) {
         __syncthreads();
         const int n = (t1 - t0) * P;
-        // streams outermost with a compile-time index: a lane-varying index
+        // streams by a compile-time index (unrolled): a lane-varying index
         // into the argument array would load the output pointer from memory,
-        // and that wait would also drain the weight loads in flight
+        // and that wait would also drain the weight loads in flight; a
+        // residual launch's loads of every stream go out before any is used
+        for (int r = tid; r < n; r += 64 * P * Q) {  // r: row slot relative to step t0
+            const int64_t m = (int64_t)t0 * P + r;
+            if (m >= wg_rows)
+                continue;
+            const int slot = half * S * P + r;
+            const int64_t row = g + m * G;
+            float rv[NS];
+            if (a.res[0]) {  // uniform: a residual launch sets every stream's
 #pragma unroll
-        for (int s = 0; s < NS; s++)
-            for (int r = tid; r < n; r += 64 * P * Q) {  // r: row slot relative to step t0
-                const int64_t m = (int64_t)t0 * P + r;
-                if (m >= wg_rows)
-                    continue;
-                const int slot = half * S * P + r;
+                for (int s = 0; s < NS; s++)
+                    rv[s] = a.res[s][row];
+            }
+#pragma unroll
+            for (int s = 0; s < NS; s++) {
                 float acc = part[(slot * Q) * NS + s];
                 for (int j = 1; j < Q; j++)
                     acc += part[((slot * Q) + j) * NS + s];
-                if (a.res[s])
-                    acc = a.res[s][g + m * G] + acc;
-                a.y[s][g + m * G] = acc;
+                if (a.res[0])
+                    acc = rv[s] + acc;
+                a.y[s][row] = acc;
                 if constexpr (VERIFY)
-                    vkey[s & 1] = std::max(vkey[s & 1], verify_key(acc, g + m * G));
+                    vkey[s & 1] = std::max(vkey[s & 1], verify_key(acc, row));
             }
+        }
         // Stores count on the same counter as the weight loads.  Without this
         // wait the compiler cannot tell how many operations follow the
         // prefetched loads when the loop is re-entered, and it would make the
@@ -1478,20 +1497,28 @@ __global__ __launch_bounds__(64 * 4) void gemv_q8_split_kernel(SplitArgs sa)
     auto flush = [&](int t0, int t1, int half) {
         __syncthreads();
         const int n = (t1 - t0) * P;
+        for (int r = tid; r < n; r += 64 * P * Q) {  // as in the SSQ kernel
+            const int64_t m = (int64_t)t0 * P + r;
+            if (m >= wg_rows)
+                continue;
+            const int slot = half * S * P + r;
+            const int64_t row = g + m * G;
+            float rv[NS];
+            if (a.res[0]) {  // uniform: a residual launch sets every stream's
 #pragma unroll
-        for (int s = 0; s < NS; s++)
-            for (int r = tid; r < n; r += 64 * P * Q) {
-                const int64_t m = (int64_t)t0 * P + r;
-                if (m >= wg_rows)
-                    continue;
-                const int slot = half * S * P + r;
+                for (int s = 0; s < NS; s++)
+                    rv[s] = a.res[s][row];
+            }
+#pragma unroll
+            for (int s = 0; s < NS; s++) {
                 float acc = part[(slot * Q) * NS + s];
                 for (int j = 1; j < Q; j++)
                     acc += part[((slot * Q) + j) * NS + s];
-                if (a.res[s])
-                    acc = a.res[s][g + m * G] + acc;
-                a.y[s][g + m * G] = acc;
+                if (a.res[0])
+                    acc = rv[s] + acc;
+                a.y[s][row] = acc;
             }
+        }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): see the SSQ kernel
     };
 

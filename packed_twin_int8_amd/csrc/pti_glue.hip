@@ -130,12 +130,14 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_reg_kernel(const float *
     const int tid = threadIdx.x;
     const float *xs = x + blockIdx.x * dim;
     float *ys = y + blockIdx.x * dim;
+    // buffer loads bounded by the row: past dim they read zeros, with no
+    // branch, so all PER loads are in flight at once
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(xs), (short)0, (int)(dim * 4), 0x00020000);
     float v[PER];
 #pragma unroll
-    for (int i = 0; i < PER; i++) {
-        const int64_t c = tid + (int64_t)i * kNormThreads;
-        v[i] = c < dim ? xs[c] : 0.f;
-    }
+    for (int i = 0; i < PER; i++)
+        v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (tid + i * kNormThreads) * 4, 0, 0));
     double acc = 0.0;
 #pragma unroll
     for (int i = 0; i < PER; i++)
