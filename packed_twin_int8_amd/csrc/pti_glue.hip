@@ -219,10 +219,19 @@ __global__ __launch_bounds__(kSvThreads) void sv_part_kernel(const float *__rest
     const int64_t b = blockIdx.x, s = blockIdx.y;
     const int64_t j0 = b * kSvPart;
     const int n = (int)min<int64_t>(kSvPart, vocab - j0);
-    const float *v = logits + s * vocab + j0;
+    // the thread's kSvRun strided logits, all loads in flight at once
+    // (buffer loads bounded by the part; entries past it are masked below)
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(logits + s * vocab + j0), (short)0, n * 4, 0x00020000);
+    float x[kSvRun];
+#pragma unroll
+    for (int k = 0; k < kSvRun; k++)
+        x[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (tid + k * kSvThreads) * 4, 0, 0));
     float m = -__builtin_inff();
-    for (int i = tid; i < n; i += kSvThreads)
-        m = fmaxf(m, v[i]);
+#pragma unroll
+    for (int k = 0; k < kSvRun; k++)
+        if (tid + k * kSvThreads < n)
+            m = fmaxf(m, x[k]);
     m = wave_max_f32(m);
     if (lane == 0)
         wmax[wv] = m;
@@ -233,8 +242,10 @@ __global__ __launch_bounds__(kSvThreads) void sv_part_kernel(const float *__rest
     const double md = m;
     double acc = 0.0;
     if (m > -__builtin_inff())
-        for (int i = tid; i < n; i += kSvThreads)
-            acc += exp((double(v[i]) - md) / temperature);
+#pragma unroll
+        for (int k = 0; k < kSvRun; k++)
+            if (tid + k * kSvThreads < n)
+                acc += exp((double(x[k]) - md) / temperature);
     acc = pti_norm::wave_sum_f64(acc);
     if (lane == 0)
         wsum[wv] = acc;
@@ -364,15 +375,21 @@ __global__ __launch_bounds__(kSvThreads) void sv_draw_kernel(const float *__rest
     const int64_t b = own_part;
     const int64_t j0 = b * kSvPart;
     const int n = (int)min<int64_t>(kSvPart, vocab - j0);
-    const float *v = logits + s * vocab + j0;
     const double mb = ps[b].m, fb = factor(mb);
     const int cq = (n + kSvThreads - 1) / kSvThreads;  // at most kSvRun
     const int q0 = min(n, tid * cq), q1 = min(n, q0 + cq);
+    // the run's logits, all loads in flight at once (bounded by the part)
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(logits + s * vocab + j0), (short)0, n * 4, 0x00020000);
+    float x[kSvRun];
+#pragma unroll
+    for (int k = 0; k < kSvRun; k++)
+        x[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (q0 + k) * 4, 0, 0));
     double e[kSvRun];  // this thread's weights, kept for the owner's scan
     double loc2 = 0.0;
 #pragma unroll
     for (int k = 0; k < kSvRun; k++) {
-        e[k] = q0 + k < q1 ? exp((double(v[q0 + k]) - mb) / temperature) * fb : 0.0;
+        e[k] = q0 + k < q1 ? exp((double(x[k]) - mb) / temperature) * fb : 0.0;
         loc2 += e[k];
     }
     if (tid == 0)
