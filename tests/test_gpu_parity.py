@@ -178,8 +178,12 @@ def test_ssq_vs_oracle_and_split(env, rows, cols):
 # the row-split form (one and four waves per row); (8193, 1024): above the
 # row-split form's row limit; (8200, 5120): above it with rows of one wave of
 # five rounds, which one and two streams run in the row-split kernel and three
-# and four in the per-wave-row kernel
-@pytest.mark.parametrize("rows,cols", [(129, 1056), (300, 5120), (40, 17408), (8193, 1024), (8200, 5120)])
+# and four in the per-wave-row kernel; (5, 20544) and (8200, 12288): the
+# per-wave-row kernel with x staged in LDS chunks at some stream counts and
+# whole at others (20544 columns: chunked from two streams on; 12288: from
+# three on)
+@pytest.mark.parametrize("rows,cols", [(129, 1056), (300, 5120), (40, 17408), (8193, 1024), (8200, 5120), (5, 20544),
+                                       (8200, 12288)])
 def test_stream_slot_invariance(env, rows, cols):
     d = synth.q8(rows, cols, 4, seed=33)
     single = [run_q8(env, d["Q"], d["S"], d["X"][s:s + 1])[0] for s in range(4)]
