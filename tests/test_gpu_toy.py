@@ -540,6 +540,38 @@ def test_decode_greedy_small_q8_all_stream_counts(small_raw):
         check_draws(st, p)
 
 
+def test_decode_threads_at_once(small_raw):
+    """Decode loops run at once from three host threads, each on its own
+    stream and workspace (each thread has its own readback page, which the
+    verify kernels write into): every loop returns what it returns alone."""
+    import threading
+    pti, torch = _pti(), _torch()
+    st = Stack(small_raw, pti.FMT_Q8)
+    jobs = [(0, 4, 40), (7, 2, 40), (999, 3, 40)]
+    alone = [st.gpu.decode(f, n, k) for f, n, k in jobs]
+    out, err = [None] * len(jobs), []
+
+    def run(i):
+        try:
+            f, n, k = jobs[i]
+            s = torch.cuda.Stream()
+            w = st.gpu.workspace(n)
+            torch.cuda.synchronize()
+            out[i] = st.gpu.decode(f, n, k, work=w, stream=s)
+        except Exception as e:  # reported below
+            err.append(e)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(len(jobs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not err, err
+    for i, (a, b) in enumerate(zip(alone, out)):
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y), jobs[i]
+
+
 def sampled_statistics(raw, steps, what):
     """T = 0.7, four Q8 streams: the loop's control is replayed through the
     oracle's loop, every draw equals the oracle's inverse-CDF draw on the
