@@ -135,6 +135,9 @@ struct GemvArgs {
     int32_t chunk_rounds;  // rounds of x held in LDS at once
     int32_t norm;          // per-wave-row kernel, x staged at once: x[s] <- rmsnorm(x[s]) as it is staged
     double norm_eps;
+    // per-wave-row kernel, greedy verify of the outputs (null: none): per
+    // workgroup g the largest verify key of stream s at keys[kKeyStride g + s]
+    unsigned long long *keys;
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -480,6 +483,18 @@ __device__ __forceinline__ unsigned long long wave_umax(unsigned long long k)
     return k;
 }
 
+// Key ordering (value, then lower row) as one unsigned 64-bit number: the
+// float's bits made monotonic (-0 counted as +0), then the row inverted.  The
+// largest key is the argmax with the lowest row among equals; no key is 0.
+__device__ __forceinline__ unsigned long long verify_key(float v, int64_t row)
+{
+    uint32_t u = __builtin_bit_cast(uint32_t, v == 0.f ? 0.f : v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)u << 32) | (0xFFFFFFFFu - (uint32_t)row);
+}
+
+constexpr int kKeyStride = pti::kVerifyKeyStride;  // keys per workgroup in a per-wave-row verify (streams, padded)
+
 // Row addressing of the per-wave-row kernel.
 //   kAmFlat: one matrix, row r at seg_base[0] + r * row_bytes.
 //   kAmSeg:  a grouped launch, rows stacked over the segments (row_addr).
@@ -508,6 +523,7 @@ struct Wave {
     // outv[0] (pairs: pair j's gate in lane j of outv[0], its up in outv[1])
     float outv[AM == kAmPair ? 2 : 1][NS];
     int gp0;         // first pass of the current group
+    unsigned long long vkey[NS];  // a.keys: this lane's largest verify key of each stream
     Unit bufs[kD + 1][R];
 
     // Cursors over the steps (pass, round) of the current segment: passes
@@ -529,6 +545,9 @@ struct Wave {
     {
         npass = AM == kAmPair ? nrow : (nrow + R - 1) / R;
         lo = lane_offsets(lane_);
+#pragma unroll
+        for (int s = 0; s < NS; s++)
+            vkey[s] = 0;
 #pragma unroll
         for (int r = 0; r < R; r++)
 #pragma unroll
@@ -804,6 +823,12 @@ struct Wave {
             }
         } else {
             const int nj = min(g1 * R, nrow) - gp0 * R;
+            if (a.keys && lane < nj) {  // the launch's greedy verify (uniform test first)
+                const int64_t row = first + (int64_t)(gp0 * R + lane) * stride;
+#pragma unroll
+                for (int s = 0; s < NS; s++)
+                    vkey[s] = std::max(vkey[s], verify_key(outv[0][s], row));
+            }
             if (lane < nj) {
                 const int64_t row = first + (int64_t)(gp0 * R + lane) * stride;
                 if (a.res[0]) {  // uniform: a residual launch sets every stream's
@@ -898,6 +923,26 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemvArgs a)
                         w.store_group(p + 1);
                 }
             }
+    }
+    if (a.keys) {  // uniform: the workgroup's largest key of each stream
+        // The waves' keys go to the x area (at least one round of x, whatever
+        // the chunking) once every wave is done reading x.
+        static_assert(NS * W * 8 <= 64 * UC * NSP * 4, "the verify keys must fit one round of x");
+        unsigned long long *wk = reinterpret_cast<unsigned long long *>(xs);  // [NS][W]
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+            const unsigned long long k = wave_umax(w.vkey[s]);  // in lane 63
+            if (lane == 63)
+                wk[s * W + wv] = k;
+        }
+        __syncthreads();
+        if (tid < NS) {
+            unsigned long long k = wk[tid * W];
+            for (int i = 1; i < W; i++)
+                k = std::max(k, wk[tid * W + i]);
+            a.keys[kKeyStride * blockIdx.x + tid] = k;
+        }
     }
 }
 
@@ -1048,15 +1093,6 @@ struct SplitArgs {
     unsigned long long *keys;
 };
 
-// Key ordering (value, then lower row) as one unsigned 64-bit number: the
-// float's bits made monotonic (-0 counted as +0), then the row inverted.  The
-// largest key is the argmax with the lowest row among equals; no key is 0.
-__device__ __forceinline__ unsigned long long verify_key(float v, int64_t row)
-{
-    uint32_t u = __builtin_bit_cast(uint32_t, v == 0.f ? 0.f : v);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((unsigned long long)u << 32) | (0xFFFFFFFFu - (uint32_t)row);
-}
 
 // VERIFY: also the first half of the greedy verify of the two twins' outputs
 // -- each thread keeps the largest key of the rows it stores and each
@@ -1294,6 +1330,46 @@ __global__ __launch_bounds__(64) void verify_keys_kernel(const unsigned long lon
             argmax_out[s] = am[s];
         }
         accept_out[0] = 1 + (tokens_in[1] == am[0] ? 1 : 0);
+    }
+}
+
+// The same for a per-wave-row launch's keys of n streams (keys[kKeyStride g +
+// s]): each stream's argmax and the accept count of the staggered streams, 1
+// + the leading run of tokens_in[i] == argmax[i - 1], as pti_verify_argmax
+// gives them.
+__global__ __launch_bounds__(64) void verify_keys_n_kernel(const unsigned long long *__restrict__ keys, int n_groups,
+                                                           int n, const int32_t *__restrict__ tokens_in,
+                                                           int32_t *__restrict__ argmax_out,
+                                                           int32_t *__restrict__ accept_out)
+{
+    const int lane = threadIdx.x;
+    unsigned long long k[kKeyStride] = {0, 0, 0, 0};
+#pragma unroll 4
+    for (int i = lane; i < n_groups; i += 64) {
+        const ulonglong2 *g = reinterpret_cast<const ulonglong2 *>(keys + (size_t)kKeyStride * i);
+        const ulonglong2 v0 = g[0], v1 = g[1];
+        k[0] = std::max(k[0], (unsigned long long)v0.x);
+        k[1] = std::max(k[1], (unsigned long long)v0.y);
+        k[2] = std::max(k[2], (unsigned long long)v1.x);
+        k[3] = std::max(k[3], (unsigned long long)v1.y);
+    }
+#pragma unroll
+    for (int s = 0; s < kKeyStride; s++)
+        k[s] = wave_umax(k[s]);
+    if (lane == 63) {
+        int32_t am[kKeyStride];
+#pragma unroll
+        for (int s = 0; s < kKeyStride; s++) {
+            am[s] = (int32_t)(0xFFFFFFFFu - (uint32_t)(k[s] & 0xFFFFFFFFull));
+            if (s < n)
+                argmax_out[s] = am[s];
+        }
+        int acc = 1;
+#pragma unroll
+        for (int s = 1; s < kKeyStride; s++)
+            if (s < n && acc == s && tokens_in[s] == am[s - 1])
+                acc++;
+        accept_out[0] = acc;
     }
 }
 
@@ -1916,12 +1992,13 @@ int gemv_q8_res(const void *w, const float *x, float *y, const float *res, int64
 
 
 int q8_gemv_rmsnorm(const void *const *w, const int64_t *rows, int n_mats, const float *x, float *y, int64_t cols,
-                    int n, float eps, void *stream)
+                    int n, float eps, void *stream, unsigned long long *keys)
 {
     GemvArgs a;
     const int rc = group_args<kQ8>(w, rows, n_mats, cols, nullptr, 0, a);
     if (rc != PTI_OK)
         return rc;
+    a.keys = keys;
     const bool even = (a.cols / PTI_BLOCK) % 2 == 0;
     if (!q8_norm_fusable(a, n))
         return kNormNotFused;
@@ -1938,6 +2015,25 @@ int q8_gemv_rmsnorm(const void *const *w, const int64_t *rows, int n_mats, const
     case 3: return even ? launch<kQ8, 4, 3, true>(a, st) : launch<kQ8, 4, 3, false>(a, st);
     default: return even ? launch<kQ8, 4, 4, true>(a, st) : launch<kQ8, 4, 4, false>(a, st);
     }
+}
+
+int64_t rowwise_groups(int64_t rows)
+{
+    const int cus = device_cus();
+    return cus > 0 ? std::min<int64_t>(cus, rows) : 0;
+}
+
+int launch_verify_keys_n(const unsigned long long *keys, int n_groups, int n, const int32_t *tokens_in,
+                         int32_t *argmax_out, int32_t *accept_out, void *stream)
+{
+    hipLaunchKernelGGL(verify_keys_n_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), keys, n_groups, n,
+                       tokens_in, argmax_out, accept_out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        pti::set_hip_error(e);
+        return PTI_ERR_HIP;
+    }
+    return PTI_OK;
 }
 
 int q8_gate_up_silu(const void *gate, const void *up, int64_t ffn, const float *x, float *y, int64_t cols, int n,

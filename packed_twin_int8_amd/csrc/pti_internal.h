@@ -51,8 +51,21 @@ int gemv_ssq_res(const void *w, const float *x_a, const float *x_b, float *y_a, 
 // caller then runs pti_rmsnorm and the plain GEMV).  Arguments already validated, except that
 // the matrices are checked as a grouped launch checks them.
 constexpr int kNormNotFused = 1;
+// keys (optional): the launch also writes, per workgroup, the largest greedy
+// verify key of each stream (kVerifyKeyStride per workgroup, stream s at s;
+// rowwise_groups(sum of rows) workgroups), for launch_verify_keys_n.
+constexpr int kVerifyKeyStride = 4;
 int q8_gemv_rmsnorm(const void *const *w, const int64_t *rows, int n_mats, const float *x, float *y, int64_t cols,
-                    int n, float eps, void *stream);
+                    int n, float eps, void *stream, unsigned long long *keys = nullptr);
+
+// Workgroups of a per-wave-row launch over `rows` rows (0 if the device
+// cannot be queried).
+int64_t rowwise_groups(int64_t rows);
+
+// argmax_out[s] (s < n) and accept_out[0] from the keys of a q8_gemv_rmsnorm
+// launch, the results pti_verify_argmax gives on that launch's outputs.
+int launch_verify_keys_n(const unsigned long long *keys, int n_groups, int n, const int32_t *tokens_in,
+                         int32_t *argmax_out, int32_t *accept_out, void *stream);
 
 // y[s][j] = silu(g[s][j]) * u[s][j], j < ffn, s < n, for g = G rmsnorm(x[s])
 // and u = U rmsnorm(x[s]) (Q8 matrices gate and up of ffn rows each, cols

@@ -31,8 +31,12 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
-    size_t h, r, gu, x, logits, tok, uni, sv, total;
+    size_t h, r, gu, x, logits, tok, uni, sv, keys, total;
 };
+
+// Workgroups of the LM head whose greedy-verify keys the workspace holds (a
+// head launch over more takes the separate verify).
+constexpr int64_t kMaxKeyGroups = 1024;
 
 Layout layout(const pti_toy_model &m, int n)
 {
@@ -52,6 +56,7 @@ Layout layout(const pti_toy_model &m, int n)
     L.tok = take(PTI_MAX_STREAMS * 4);
     L.uni = take(PTI_MAX_STREAMS * 8);
     L.sv = take(pti_sample_verify_workspace_bytes(m.vocab, n));  // the sampled verify's part sums
+    L.keys = take(size_t(kMaxKeyGroups) * pti::kVerifyKeyStride * 8);  // the head's greedy-verify keys
     L.total = off;
     return L;
 }
@@ -111,9 +116,15 @@ int gemv(const pti_toy_model &m, const void *w, const float *x, float *y, int64_
 // stored.  In Q8 the first three are one launch where the gate|up GEMV takes
 // the per-wave-row kernel.  Each step's results are bitwise those of the
 // separate calls (rmsnorm, gate, up, silu_mul, down, add).
+//
+// keyed (optional): ask the Q8 head for greedy-verify keys in the workspace;
+// *keyed is set to whether it wrote them (the head took the per-wave-row
+// kernel with the norm fused and its workgroups fit the key region).
 int forward(const pti_toy_model &m, const Layout &L, char *work, const int32_t *tokens, float *logits, int n,
-            void *stream)
+            void *stream, bool *keyed = nullptr)
 {
+    if (keyed)
+        *keyed = false;
     float *h = reinterpret_cast<float *>(work + L.h), *r = reinterpret_cast<float *>(work + L.r);
     float *gu = reinterpret_cast<float *>(work + L.gu), *x = reinterpret_cast<float *>(work + L.x);
     const int64_t H = m.hidden, F = m.ffn;
@@ -148,9 +159,16 @@ int forward(const pti_toy_model &m, const Layout &L, char *work, const int32_t *
     if (!ssq) {
         const void *head[1] = {m.head};
         const int64_t vrows[1] = {m.vocab};
-        const int fused = pti::q8_gemv_rmsnorm(head, vrows, 1, h, logits, H, n, m.eps, stream);
-        if (fused != pti::kNormNotFused)
+        const int64_t groups = pti::rowwise_groups(m.vocab);
+        unsigned long long *keys = keyed && groups > 0 && groups <= kMaxKeyGroups
+                                       ? reinterpret_cast<unsigned long long *>(work + L.keys)
+                                       : nullptr;
+        const int fused = pti::q8_gemv_rmsnorm(head, vrows, 1, h, logits, H, n, m.eps, stream, keys);
+        if (fused != pti::kNormNotFused) {
+            if (keyed)
+                *keyed = fused == PTI_OK && keys != nullptr;
             return fused;
+        }
     }
     PTI_TRY(pti_rmsnorm(h, r, H, n, m.eps, stream));
     return gemv(m, m.head, r, logits, m.vocab, H, n, stream);
@@ -210,12 +228,17 @@ struct Decoder {
     // for the pass; the accept count compares them with the pass inputs in
     // dev_tok() (read only when n >= 2, i.e. for row0 == 0).  The draws and
     // the accept count arrive in the readback page when the stream is synchronised.
-    int draw(int row0, int n, int32_t *out, int32_t *accept)
+    // keyed: the pass's head left greedy-verify keys (row0 is then 0), which
+    // one wave reduces instead of a pass over the logits.
+    int draw(int row0, int n, int32_t *out, int32_t *accept, bool keyed)
     {
         void *s = st;
         const float *lg = dev_logits() + int64_t(row0) * m.vocab;
         int32_t *o = const_cast<int32_t *>(back), *a = o + PTI_MAX_STREAMS;
-        if (temp == 0.0)
+        if (temp == 0.0 && keyed)
+            PTI_TRY(pti::launch_verify_keys_n(reinterpret_cast<const unsigned long long *>(work + L.keys),
+                                              (int)pti::rowwise_groups(m.vocab), n, dev_tok(), o, a, s));
+        else if (temp == 0.0)
             PTI_TRY(pti_verify_argmax(lg, dev_tok(), o, a, m.vocab, n, s));
         else
             PTI_TRY(pti_sample_verify(lg, dev_tok(), dev_uni(), temp, o, a, m.vocab, n, work + L.sv,
@@ -231,8 +254,9 @@ struct Decoder {
     int multi(int step, const int32_t *x, int32_t *o, int32_t *a)
     {
         PTI_TRY(set_inputs(x, N, step, 0, N));
-        PTI_TRY(forward(m, L, work, dev_tok(), dev_logits(), npass, st));
-        PTI_TRY(draw(0, N, o, a));
+        bool keyed = false;
+        PTI_TRY(forward(m, L, work, dev_tok(), dev_logits(), npass, st, temp == 0.0 ? &keyed : nullptr));
+        PTI_TRY(draw(0, N, o, a, keyed));
         for (int s = 0; s < N; s++)
             record(step, s, s, x[s], o[s]);
         return PTI_OK;
@@ -247,9 +271,10 @@ struct Decoder {
         const int n = m.format == PTI_FMT_SSQ ? 2 : 1;
         int32_t a;
         PTI_TRY(set_inputs(in, n, step, slot, 1));
-        PTI_TRY(forward(m, L, work, dev_tok(), dev_logits(), n, st));
+        bool keyed = false;
+        PTI_TRY(forward(m, L, work, dev_tok(), dev_logits(), n, st, temp == 0.0 ? &keyed : nullptr));
         const int row = (m.format == PTI_FMT_SSQ && stream >= 1) ? 1 : 0;
-        PTI_TRY(draw(row, 1, o, &a));
+        PTI_TRY(draw(row, 1, o, &a, keyed && row == 0));
         record(step, slot, stream, t, *o);
         return PTI_OK;
     }

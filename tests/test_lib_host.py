@@ -377,8 +377,8 @@ def test_toy_errors():
     n = ws(ctypes.byref(m), 4)
     # h, r: 4*64*4 = 1024 each; stacked gate|up 4*2*96*4 = 3072; silu*up 4*96*4 = 1536;
     # logits 1600 (-> 1792); two small regions (tokens, uniforms) and the sampled verify's part
-    # sums (4 x 16 -> 256)
-    assert n == 2 * 1024 + 3072 + 1536 + 1792 + 3 * 256
+    # sums (4 x 16 -> 256); the LM head's greedy-verify keys (1024 workgroups x 4 streams x 8)
+    assert n == 2 * 1024 + 3072 + 1536 + 1792 + 3 * 256 + 1024 * 4 * 8
     assert ws(ctypes.byref(m), 0) == 0 and ws(ctypes.byref(m), 5) == 0
     assert ws(ctypes.byref(_toy(fmt=pti.FMT_SSQ)), 4) == 0 and ws(ctypes.byref(_toy(fmt=pti.FMT_SSQ)), 2) > 0
     for bad in (_toy(fmt=2), _toy(layers=0), _toy(layers=65), _toy(hidden=48), _toy(ffn=0), _toy(vocab=0),
