@@ -415,7 +415,11 @@ int pti_graph_destroy(void *graph);
  *     next inputs are drawn again by single-stream passes starting from
  *     o_{a-1} (slots N .. 2N-1-a).
  * A draw is the argmax of the logits (temperature == 0) or the sampled-verify
- * draw at that temperature with uniform uniforms[k * 2N + slot].  A
+ * draw at that temperature with uniform uniforms[k * 2N + slot].  A greedy
+ * pass whose Q8 LM head runs the per-wave-row kernel with the norm fused
+ * takes the argmaxes from per-workgroup keys that the head writes into
+ * `work` (the same argmax, lowest index among equals, without a second pass
+ * over the logits); any other pass runs pti_verify_argmax.  A
  * single-stream pass of stream i >= 1 runs twin B in the SSQ format.
  * uniforms: host fp64 [(n_steps + 1) * 2 * N], may be NULL when temperature
  * is 0.  committed, accepts: host int32 [n_steps].  passes: host int32
