@@ -499,6 +499,26 @@ def test_decode_greedy_q8_four_streams(full_q8, full_oracle):
     greedy_chain_checks(c4.tolist(), 1, full_oracle, "q8 greedy chain")
 
 
+def test_decode_greedy_q8_tied_head_takes_lowest_row(full_raw):
+    """Every LM-head row a copy of one row: all 32000 logits of a pass carry the
+    same bits (a row's arithmetic does not depend on its index), so ties span
+    every workgroup of the head's GEMV.  The greedy draw is the lowest index
+    among the largest values [README, how acceptance works], token 0, for every
+    stream of every pass, and each staggered step accepts all N guesses."""
+    head = full_raw["head"]
+    tied = dict(full_raw)
+    tied["head"] = {"Q": np.ascontiguousarray(np.broadcast_to(head["Q"][7], head["Q"].shape)),
+                    "S": np.ascontiguousarray(np.broadcast_to(head["S"][7], head["S"].shape))}
+    st = Stack(tied, _pti().FMT_Q8)
+    lg = st.logits_for([1, 0])
+    assert (lg == lg[:, :1]).all()  # the premise: every logit of a row equal
+    steps = 6
+    for n in (1, 2, 4):
+        c, a, p = st.gpu.decode(1, n, steps)
+        assert c.tolist() == [0] * steps and a.tolist() == [n] * steps, n
+        assert all(int(out) == 0 for *_, out in p), n
+
+
 def test_decode_greedy_ssq_self_twin(full_ssq, full_oracle):
     st = full_ssq
     steps = 64
